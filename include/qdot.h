@@ -1,0 +1,128 @@
+/*
+ * qdot.h -- C ABI of the integer-dot block-quantized matmul for AMD MI355X
+ * (gfx950).  Library: libqdot.so.
+ *
+ * The operation.  Decode in GGUF-quantized LLM inference multiplies raw
+ * block-quantized weights (Q4_K, Q6_K, IQ4_XS superblocks of 256 weights)
+ * against activations quantized to Q8_1 blocks of 32, using integer dot
+ * products on the raw quantized values, and only then produces fp32; the
+ * weights are never dequantized to fp32 (xLLM v0.7 dev log,
+ * developer.cloud.tencent.com.cn/article/2739032, section 1 "background" and
+ * section B1.3).  Each activation quantization is shared by every row of the
+ * batch (same page, section C, the shared d_xn_q8 buffer).  Inside each block
+ * the dot is an exact int32 sum; the scales are applied afterwards (Kestrel
+ * page, wsisp.com posts/117433, section 5).
+ *
+ * Formats (byte layouts; the pages name the formats, the layouts are the plain
+ * GGUF reading):
+ *   Q8_1   36 B per 32 activations: fp16 d, fp16 s, int8 q[32].
+ *   Q4_K  144 B per 256 weights: fp16 d, fp16 dmin, 12 B of 6-bit scales and
+ *         mins for 8 sub-blocks of 32, 128 B of 4-bit codes;
+ *         w = d*sc*q - dmin*m.
+ *   Q6_K  210 B per 256 weights: 128 B low 4 bits, 64 B high 2 bits, 16 int8
+ *         sub-scales (sub-blocks of 16), fp16 d; w = d*sc*(q-32).
+ *   IQ4_XS 136 B per 256 weights: fp16 d, u16 scales_h, 4 B scales_l (eight
+ *         6-bit scales ls), 128 B of 4-bit codebook indices; each 32-element
+ *         sub-block has low nibbles = elements 0-15 and high nibbles = 16-31
+ *         (V100TPS log, agent-report.daedalus.work, 2026-08-12 "batch kernel
+ *         locked to Q4_0"); w = d*(ls-32)*codebook[idx].  The 16-entry
+ *         codebook is a placeholder (the pages do not print kvalues_iq4nl):
+ *         round_half_away(-127 + 240*(i/15)^1.4), i = 0..15.
+ *
+ * Layouts.  Every buffer is contiguous and row-major: x is fp32 [M][K];
+ * x_q8 is [M][K/32] Q8_1 blocks; W is [N][K/256] superblocks (GGUF row
+ * order, row n at W + n*row_bytes, so a row subset is W + n0*row_bytes with a
+ * smaller N); y is fp32 [M][N].
+ *
+ * Ownership and threading.  The caller owns and allocates every buffer;
+ * device pointers must be device memory of the current HIP device.  The
+ * library never allocates, frees or synchronizes, keeps no mutable global
+ * state, and enqueues its kernels on the caller's stream (0 = the null
+ * stream).  Calls are asynchronous and thread-safe.
+ *
+ * Errors.  Arguments are validated before any HIP call; on failure nothing is
+ * launched and a negative status is returned:
+ *   QDOT_E_ARG   null pointer, M < 1, N < 1, K < 256 or K % 256 != 0 (K % 32
+ *                != 0 for the quantizer), unknown type, or a size overflow;
+ *   QDOT_E_ALIGN W not 16-byte aligned, or x, x_q8, y, isums not 4-byte
+ *                aligned;
+ *   QDOT_E_HIP   the launch failed (hipGetLastError after the launch).
+ * There is no fallback path and no environment variable.  Inputs must be
+ * finite and each Q8_1 block's fp16 d and s finite; otherwise results are
+ * undefined (but every launch stays in bounds).
+ */
+#ifndef QDOT_H
+#define QDOT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { QDOT_Q4_K = 1, QDOT_Q6_K = 2, QDOT_IQ4_XS = 3 } qdot_type;
+
+enum { QDOT_OK = 0, QDOT_E_ARG = -1, QDOT_E_ALIGN = -2, QDOT_E_HIP = -3 };
+
+/* Bytes per 256-weight superblock: 144 (Q4_K), 210 (Q6_K), 136 (IQ4_XS);
+ * 0 for an unknown type. */
+size_t qdot_block_bytes(int type);
+
+/* Bytes of an N x K weight matrix: N * (K/256) * qdot_block_bytes(type);
+ * 0 if the arguments are invalid. */
+size_t qdot_weight_bytes(int type, int64_t N, int64_t K);
+
+/* Bytes of M x K activations in Q8_1: M * (K/32) * 36; 0 if invalid. */
+size_t qdot_q8_1_bytes(int64_t M, int64_t K);
+
+/* Number of int32 sub-block sums written by qdot_qmatmul_dump_isums:
+ * M * N * (K/S), S = 32 (Q4_K, IQ4_XS) or 16 (Q6_K); 0 if invalid. */
+size_t qdot_isum_count(int type, int64_t N, int64_t K, int64_t M);
+
+/* Quantize fp32 activations x [M][K] (device) to Q8_1 blocks x_q8 (device,
+ * qdot_q8_1_bytes(M, K) bytes).  Per block of 32: amax = max|x_i|;
+ * d32 = amax/127 (IEEE fp32 division); q_i = roundf(x_i/d32) (fp32 division,
+ * ties away from zero) clamped to [-127, 127], all zero when amax == 0;
+ * stored d = fp16(d32), stored s = fp16(d * sum q_i), both round to nearest
+ * even.  The pages launch this quantizer once ahead of the matmul and share
+ * it across the batch (V100TPS log, 2026-08-12, on ggml_mul_mat_a8; xLLM
+ * page, section C).  K % 32 == 0 is required. */
+int qdot_quantize_q8_1(const float *x, int64_t M, int64_t K, void *x_q8,
+                       void *stream);
+
+/* y [M][N] = x_q8 [M][K] (Q8_1) times W^T, W = [N][K] raw superblocks of
+ * `type`.  Per output: sum over superblocks and sub-blocks of
+ *   Q4_K   d*sc*D*I - dmin*m*S
+ *   Q6_K   d*sc*D*I            (sub-blocks of 16)
+ *   IQ4_XS d*(ls-32)*D*I
+ * where I is the exact integer dot of the sub-block's weight codes with the
+ * int8 activations and D, S are the activation block's fp16 d and s.  Every
+ * scale product is exact and accumulated in fp64; y is rounded once to fp32.
+ * M <= 8 runs the decode kernel (v_dot4_i32_i8, M-row register tile); M > 8
+ * runs the MFMA i8 prefill kernel.  K % 256 == 0 is required. */
+int qdot_qmatmul(const void *W, int type, int64_t N, int64_t K,
+                 const void *x_q8, int64_t M, float *y, void *stream);
+
+/* Same as qdot_qmatmul (same kernel template, same y) and also writes every
+ * integer sub-block sum I to isums [M][N][K/S] (int32, device,
+ * qdot_isum_count elements): a debug dump for bit-exact checks. */
+int qdot_qmatmul_dump_isums(const void *W, int type, int64_t N, int64_t K,
+                            const void *x_q8, int64_t M, float *y,
+                            int32_t *isums, void *stream);
+
+/* Static text for a status code. */
+const char *qdot_status_str(int status);
+
+/* Name of the kernel qdot_qmatmul runs for (type, M), e.g. "qmv_dot4<Q4_K,8>"
+ * or "qmm_mfma<Q6_K>"; "invalid" for bad arguments.  Static text. */
+const char *qdot_kernel_name(int type, int64_t M);
+
+/* Build identifier of the library (compile date and time).  Static text. */
+const char *qdot_build_id(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QDOT_H */

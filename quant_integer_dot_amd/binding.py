@@ -1,0 +1,137 @@
+"""Thin ctypes binding over libqdot.so (declared in include/qdot.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library.  Arguments may be torch tensors (their data_ptr is
+passed) or plain integer addresses.  The stream defaults to torch's current
+stream on the tensor's device.  There is no fallback: if the library is
+missing, every call raises.
+"""
+import ctypes
+import os
+
+QDOT_Q4_K, QDOT_Q6_K, QDOT_IQ4_XS = 1, 2, 3
+QDOT_OK, QDOT_E_ARG, QDOT_E_ALIGN, QDOT_E_HIP = 0, -1, -2, -3
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libqdot.so"
+_lib = None
+
+
+class QdotError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {qdot_status_str(status)} ({status})")
+
+
+def library_path():
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load():
+    """Load libqdot.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: the HIP library has not been built "
+            "(run __graft_entry__.build()); there is no fallback path")
+    L = ctypes.CDLL(path)
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.qdot_block_bytes.argtypes = [i32]
+    L.qdot_block_bytes.restype = ctypes.c_size_t
+    L.qdot_weight_bytes.argtypes = [i32, i64, i64]
+    L.qdot_weight_bytes.restype = ctypes.c_size_t
+    L.qdot_q8_1_bytes.argtypes = [i64, i64]
+    L.qdot_q8_1_bytes.restype = ctypes.c_size_t
+    L.qdot_isum_count.argtypes = [i32, i64, i64, i64]
+    L.qdot_isum_count.restype = ctypes.c_size_t
+    L.qdot_quantize_q8_1.argtypes = [P, i64, i64, P, P]
+    L.qdot_quantize_q8_1.restype = i32
+    L.qdot_qmatmul.argtypes = [P, i32, i64, i64, P, i64, P, P]
+    L.qdot_qmatmul.restype = i32
+    L.qdot_qmatmul_dump_isums.argtypes = [P, i32, i64, i64, P, i64, P, P, P]
+    L.qdot_qmatmul_dump_isums.restype = i32
+    L.qdot_status_str.argtypes = [i32]
+    L.qdot_status_str.restype = ctypes.c_char_p
+    L.qdot_kernel_name.argtypes = [i32, i64]
+    L.qdot_kernel_name.restype = ctypes.c_char_p
+    L.qdot_build_id.argtypes = []
+    L.qdot_build_id.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _addr(a):
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    return a.data_ptr()
+
+
+def _stream(stream, *tensors):
+    """Raw hipStream_t: explicit int/None-as-default, else torch's current."""
+    if stream is not None:
+        if isinstance(stream, int):
+            return stream
+        return stream.cuda_stream
+    for t in tensors:
+        if hasattr(t, "device") and getattr(t.device, "type", None) == "cuda":
+            import torch
+            return torch.cuda.current_stream(t.device).cuda_stream
+    return 0
+
+
+def _check(status, where):
+    if status != QDOT_OK:
+        raise QdotError(status, where)
+
+
+def qdot_block_bytes(wtype):
+    return load().qdot_block_bytes(wtype)
+
+
+def qdot_weight_bytes(wtype, N, K):
+    return load().qdot_weight_bytes(wtype, N, K)
+
+
+def qdot_q8_1_bytes(M, K):
+    return load().qdot_q8_1_bytes(M, K)
+
+
+def qdot_isum_count(wtype, N, K, M):
+    return load().qdot_isum_count(wtype, N, K, M)
+
+
+def qdot_quantize_q8_1(x, M, K, x_q8, stream=None):
+    s = _stream(stream, x, x_q8)
+    _check(load().qdot_quantize_q8_1(_addr(x), M, K, _addr(x_q8), s), "qdot_quantize_q8_1")
+
+
+def qdot_qmatmul(W, wtype, N, K, x_q8, M, y, stream=None):
+    s = _stream(stream, W, x_q8, y)
+    _check(load().qdot_qmatmul(_addr(W), wtype, N, K, _addr(x_q8), M, _addr(y), s),
+           "qdot_qmatmul")
+
+
+def qdot_qmatmul_dump_isums(W, wtype, N, K, x_q8, M, y, isums, stream=None):
+    s = _stream(stream, W, x_q8, y, isums)
+    _check(load().qdot_qmatmul_dump_isums(_addr(W), wtype, N, K, _addr(x_q8), M, _addr(y),
+                                          _addr(isums), s), "qdot_qmatmul_dump_isums")
+
+
+def qdot_status_str(status):
+    try:
+        return load().qdot_status_str(status).decode()
+    except RuntimeError:
+        return "library not loaded"
+
+
+def qdot_kernel_name(wtype, M):
+    return load().qdot_kernel_name(wtype, M).decode()
+
+
+def qdot_build_id():
+    return load().qdot_build_id().decode()

@@ -1,0 +1,99 @@
+"""Seeded synthetic inputs: raw weight superblocks and fp32 activations.
+
+This module is shared by the tests, the benchmark and the smoke check.  It holds
+none of the matmul's arithmetic: it only draws random bytes and writes the
+stated value distributions into the fields of each superblock.
+
+Distributions (the workloads of the xLLM and V100TPS pages are GGUF checkpoints
+of Qwen2.5-1.5B, Qwen3-8B and a hidden-5120 IQ4_XS model; their trained
+weights are not available, so seeded inputs of the same shapes stand in):
+  * Q4_K  : quant and scale bytes uniform random (nibbles uniform 0..15, 6-bit
+            scales and mins uniform 0..63); d, dmin ~ |N(0, 1e-3)| as binary16.
+  * Q6_K  : ql, qh bytes uniform random; 16 int8 sub-scales round(N(0, 30))
+            clipped to [-128, 127]; d ~ |N(0, 1e-3)| as binary16.
+  * IQ4_XS: index, scales_h and scales_l bytes uniform random (indices 0..15,
+            6-bit scales 0..63); d ~ |N(0, 1e-3)| as binary16.
+  * activations: fp32 N(0, 1).
+Seeds: numpy SeedSequence([2026, config, layer, projection]) for weights and
+SeedSequence([2026, config, K, M, 7]) for activations.
+"""
+import numpy as np
+
+Q4_K, Q6_K, IQ4_XS = 1, 2, 3
+TYPE_NAMES = {Q4_K: "Q4_K", Q6_K: "Q6_K", IQ4_XS: "IQ4_XS"}
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, IQ4_XS: 136}
+
+# (name, N, K, type) per projection; N = output rows, K = input width.
+QWEN25_1P5B = [
+    ("q", 1536, 1536, Q4_K), ("k", 256, 1536, Q4_K), ("v", 256, 1536, Q4_K),
+    ("o", 1536, 1536, Q4_K), ("gate", 8960, 1536, Q4_K), ("up", 8960, 1536, Q4_K),
+    ("down", 1536, 8960, Q4_K),
+]
+QWEN3_8B = [
+    ("q", 4096, 4096, Q4_K), ("k", 1024, 4096, Q4_K), ("v", 1024, 4096, Q6_K),
+    ("o", 4096, 4096, Q4_K), ("gate", 12288, 4096, Q4_K), ("up", 12288, 4096, Q4_K),
+    ("down", 4096, 12288, Q6_K),
+]
+IQ4XS_H5120 = [
+    ("qkv", 7168, 5120, IQ4_XS), ("o", 5120, 5120, IQ4_XS),
+    ("gate", 17408, 5120, IQ4_XS), ("up", 17408, 5120, IQ4_XS),
+    ("down", 5120, 17408, IQ4_XS),
+]
+
+# Workloads: index -> description.  Index 4 reuses the Qwen3-8B shapes at M=512.
+WORKLOADS = {
+    0: dict(name="q4k-matvec-1536", shapes=[("w", 1536, 1536, Q4_K)], layers=1, Ms=[1]),
+    1: dict(name="qwen2.5-1.5b-decode", shapes=QWEN25_1P5B, layers=28, Ms=[1, 2, 4, 8]),
+    2: dict(name="qwen3-8b-decode", shapes=QWEN3_8B, layers=36, Ms=list(range(1, 9))),
+    3: dict(name="iq4xs-h5120-decode", shapes=IQ4XS_H5120, layers=64, Ms=list(range(1, 9))),
+    4: dict(name="qwen3-8b-prefill-512", shapes=QWEN3_8B, layers=36, Ms=[512]),
+}
+
+
+def rng_for(*seed):
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(s) for s in seed])))
+
+
+def _half_bytes(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32).astype(np.float16)).view(np.uint8)
+
+
+def weight_bytes(wtype, N, K):
+    return N * (K // 256) * BLOCK_BYTES[wtype]
+
+
+def weights(wtype, N, K, seed):
+    """Raw superblocks, uint8 [N][K/256 * block_bytes] (GGUF row order)."""
+    assert K % 256 == 0 and N >= 1
+    rng = rng_for(*seed)
+    nb = K // 256
+    B = BLOCK_BYTES[wtype]
+    raw = np.frombuffer(rng.bytes(N * nb * B), dtype=np.uint8).reshape(N, nb, B).copy()
+    d = np.abs(rng.standard_normal((N, nb)) * 1e-3)
+    if wtype == Q4_K:
+        dmin = np.abs(rng.standard_normal((N, nb)) * 1e-3)
+        raw[:, :, 0:2] = _half_bytes(d).reshape(N, nb, 2)
+        raw[:, :, 2:4] = _half_bytes(dmin).reshape(N, nb, 2)
+    elif wtype == Q6_K:
+        sc = np.clip(np.rint(rng.standard_normal((N, nb, 16)) * 30.0), -128, 127).astype(np.int8)
+        raw[:, :, 192:208] = sc.view(np.uint8)
+        raw[:, :, 208:210] = _half_bytes(d).reshape(N, nb, 2)
+    elif wtype == IQ4_XS:
+        raw[:, :, 0:2] = _half_bytes(d).reshape(N, nb, 2)
+    else:
+        raise ValueError(f"unknown weight type {wtype}")
+    return raw.reshape(N, nb * B)
+
+
+def activations(M, K, seed):
+    """fp32 [M][K] ~ N(0, 1)."""
+    rng = rng_for(*seed)
+    return rng.standard_normal((M, K), dtype=np.float32)
+
+
+def weight_seed(config, layer, proj):
+    return (2026, config, layer, proj)
+
+
+def act_seed(config, K, M):
+    return (2026, config, K, M, 7)
