@@ -1,0 +1,126 @@
+// api.cpp -- the C ABI of libqdot (declared in include/qdot.h): argument
+// validation (before any HIP call), kernel selection and launch on the
+// caller's stream.  No allocation, no synchronization, no mutable globals,
+// no environment variables, no fallback path: the caller states M and the
+// weight type, and a bad argument fails loudly (the xLLM v0.7 log, section
+// B1.2, gives the reason: a silently degraded path cost a 100x cliff).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qdot.h"
+
+namespace qdot {
+int launch_quantize_q8_1(const float* x, int64_t M, int64_t K, void* xq, hipStream_t s);
+int launch_qmv(const void* W, int type, int N, int K, const void* xq, int M, float* y,
+               int32_t* isums, hipStream_t s);
+int launch_qmm(const void* W, int type, int N, int K, const void* xq, int M, float* y,
+               int32_t* isums, hipStream_t s);
+}  // namespace qdot
+
+namespace {
+
+constexpr int64_t kMaxDim = 0x7FFFFFFF;  // kernels index N, K with int
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int sub_len(int type) { return type == QDOT_Q6_K ? 16 : 32; }
+
+// Validates everything but pointers; 0 or a status.
+int check_dims(int type, int64_t N, int64_t K, int64_t M) {
+  if (qdot_block_bytes(type) == 0) return QDOT_E_ARG;
+  if (N < 1 || M < 1 || K < 256 || K % 256 != 0) return QDOT_E_ARG;
+  if (N > kMaxDim || K > kMaxDim || M > kMaxDim) return QDOT_E_ARG;
+  // products that index memory must fit in 63 bits
+  if ((double)N * (double)(K / 256) * 210.0 > 9.0e18) return QDOT_E_ARG;
+  if ((double)M * (double)N * (double)(K / 16) > 9.0e18) return QDOT_E_ARG;
+  return QDOT_OK;
+}
+
+int run_qmatmul(const void* W, int type, int64_t N, int64_t K, const void* x_q8, int64_t M,
+                float* y, int32_t* isums, void* stream, bool dump) {
+  int st = check_dims(type, N, K, M);
+  if (st) return st;
+  if (!W || !x_q8 || !y || (dump && !isums)) return QDOT_E_ARG;
+  if (!aligned4(x_q8) || !aligned4(y) || (dump && !aligned4(isums))) return QDOT_E_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc;
+  if (M <= 8)
+    rc = qdot::launch_qmv(W, type, (int)N, (int)K, x_q8, (int)M, y, dump ? isums : nullptr, s);
+  else
+    rc = qdot::launch_qmm(W, type, (int)N, (int)K, x_q8, (int)M, y, dump ? isums : nullptr, s);
+  return rc == 0 ? QDOT_OK : QDOT_E_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qdot_block_bytes(int type) {
+  switch (type) {
+    case QDOT_Q4_K: return 144;
+    case QDOT_Q6_K: return 210;
+    case QDOT_IQ4_XS: return 136;
+    default: return 0;
+  }
+}
+
+size_t qdot_weight_bytes(int type, int64_t N, int64_t K) {
+  if (check_dims(type, N, K, 1)) return 0;
+  return (size_t)N * (size_t)(K / 256) * qdot_block_bytes(type);
+}
+
+size_t qdot_q8_1_bytes(int64_t M, int64_t K) {
+  if (M < 1 || K < 32 || K % 32 != 0 || M > kMaxDim || K > kMaxDim) return 0;
+  return (size_t)M * (size_t)(K / 32) * 36;
+}
+
+size_t qdot_isum_count(int type, int64_t N, int64_t K, int64_t M) {
+  if (check_dims(type, N, K, M)) return 0;
+  return (size_t)M * (size_t)N * (size_t)(K / sub_len(type));
+}
+
+int qdot_quantize_q8_1(const float* x, int64_t M, int64_t K, void* x_q8, void* stream) {
+  if (!x || !x_q8) return QDOT_E_ARG;
+  if (M < 1 || K < 32 || K % 32 != 0 || M > kMaxDim || K > kMaxDim) return QDOT_E_ARG;
+  if ((double)M * (double)K > 4.0e18) return QDOT_E_ARG;
+  if (!aligned4(x) || !aligned4(x_q8)) return QDOT_E_ALIGN;
+  int rc = qdot::launch_quantize_q8_1(x, M, K, x_q8, static_cast<hipStream_t>(stream));
+  return rc == 0 ? QDOT_OK : QDOT_E_HIP;
+}
+
+int qdot_qmatmul(const void* W, int type, int64_t N, int64_t K, const void* x_q8, int64_t M,
+                 float* y, void* stream) {
+  return run_qmatmul(W, type, N, K, x_q8, M, y, nullptr, stream, false);
+}
+
+int qdot_qmatmul_dump_isums(const void* W, int type, int64_t N, int64_t K, const void* x_q8,
+                            int64_t M, float* y, int32_t* isums, void* stream) {
+  return run_qmatmul(W, type, N, K, x_q8, M, y, isums, stream, true);
+}
+
+const char* qdot_status_str(int status) {
+  switch (status) {
+    case QDOT_OK: return "ok";
+    case QDOT_E_ARG: return "invalid argument";
+    case QDOT_E_ALIGN: return "misaligned pointer";
+    case QDOT_E_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+const char* qdot_kernel_name(int type, int64_t M) {
+  static const char* const dec[3][8] = {
+      {"qmv_dot4<Q4_K,1>", "qmv_dot4<Q4_K,2>", "qmv_dot4<Q4_K,3>", "qmv_dot4<Q4_K,4>",
+       "qmv_dot4<Q4_K,5>", "qmv_dot4<Q4_K,6>", "qmv_dot4<Q4_K,7>", "qmv_dot4<Q4_K,8>"},
+      {"qmv_dot4<Q6_K,1>", "qmv_dot4<Q6_K,2>", "qmv_dot4<Q6_K,3>", "qmv_dot4<Q6_K,4>",
+       "qmv_dot4<Q6_K,5>", "qmv_dot4<Q6_K,6>", "qmv_dot4<Q6_K,7>", "qmv_dot4<Q6_K,8>"},
+      {"qmv_dot4<IQ4_XS,1>", "qmv_dot4<IQ4_XS,2>", "qmv_dot4<IQ4_XS,3>", "qmv_dot4<IQ4_XS,4>",
+       "qmv_dot4<IQ4_XS,5>", "qmv_dot4<IQ4_XS,6>", "qmv_dot4<IQ4_XS,7>", "qmv_dot4<IQ4_XS,8>"}};
+  static const char* const pre[3] = {"qmm_mfma<Q4_K>", "qmm_mfma<Q6_K>", "qmm_mfma<IQ4_XS>"};
+  if (type < QDOT_Q4_K || type > QDOT_IQ4_XS || M < 1 || M > kMaxDim) return "invalid";
+  return M <= 8 ? dec[type - 1][M - 1] : pre[type - 1];
+}
+
+const char* qdot_build_id(void) { return "libqdot gfx950 " __DATE__ " " __TIME__; }
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/qdot.h declares, computes sizes, and rejects bad arguments before any
+HIP call (so nothing is launched and no device is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quant_integer_dot_amd import binding as qd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qdot.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return qd.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qdot_\w+)\s*\(", text)))
+
+
+def test_header_symbols_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 9, names
+    for n in names:
+        assert hasattr(lib, n), f"libqdot.so does not export {n}"
+
+
+def test_sizes(lib):
+    assert qd.qdot_block_bytes(qd.QDOT_Q4_K) == 144
+    assert qd.qdot_block_bytes(qd.QDOT_Q6_K) == 210
+    assert qd.qdot_block_bytes(qd.QDOT_IQ4_XS) == 136
+    assert qd.qdot_block_bytes(0) == 0 and qd.qdot_block_bytes(4) == 0
+    assert qd.qdot_weight_bytes(qd.QDOT_Q4_K, 12288, 4096) == 12288 * 16 * 144
+    assert qd.qdot_weight_bytes(qd.QDOT_Q6_K, 4096, 12288) == 4096 * 48 * 210
+    assert qd.qdot_weight_bytes(qd.QDOT_Q4_K, 10, 100) == 0
+    assert qd.qdot_q8_1_bytes(8, 17408) == 156672
+    assert qd.qdot_q8_1_bytes(1, 33) == 0
+    assert qd.qdot_isum_count(qd.QDOT_Q6_K, 3, 512, 2) == 2 * 3 * 32
+    assert qd.qdot_isum_count(qd.QDOT_Q4_K, 3, 512, 2) == 2 * 3 * 16
+
+
+def test_names_and_status(lib):
+    assert qd.qdot_kernel_name(qd.QDOT_Q4_K, 8) == "qmv_dot4<Q4_K,8>"
+    assert qd.qdot_kernel_name(qd.QDOT_IQ4_XS, 1) == "qmv_dot4<IQ4_XS,1>"
+    assert qd.qdot_kernel_name(qd.QDOT_Q6_K, 512) == "qmm_mfma<Q6_K>"
+    assert qd.qdot_kernel_name(9, 1) == "invalid"
+    assert qd.qdot_status_str(qd.QDOT_E_ALIGN) == "misaligned pointer"
+    assert "gfx950" in qd.qdot_build_id()
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 7, 16, 256, FAKE, 1, FAKE), qd.QDOT_E_ARG),        # unknown type
+    ((FAKE, 1, 0, 256, FAKE, 1, FAKE), qd.QDOT_E_ARG),         # N < 1
+    ((FAKE, 1, 16, 255, FAKE, 1, FAKE), qd.QDOT_E_ARG),        # K % 256
+    ((FAKE, 1, 16, 0, FAKE, 1, FAKE), qd.QDOT_E_ARG),          # K = 0
+    ((FAKE, 1, 16, 256, FAKE, 0, FAKE), qd.QDOT_E_ARG),        # M < 1
+    ((0, 1, 16, 256, FAKE, 1, FAKE), qd.QDOT_E_ARG),           # null W
+    ((FAKE, 1, 16, 256, 0, 1, FAKE), qd.QDOT_E_ARG),           # null x_q8
+    ((FAKE, 1, 16, 256, FAKE, 1, 0), qd.QDOT_E_ARG),           # null y
+    ((FAKE, 1, 16, 256, FAKE + 2, 1, FAKE), qd.QDOT_E_ALIGN),  # x_q8 misaligned
+    ((FAKE, 1, 16, 256, FAKE, 1, FAKE + 1), qd.QDOT_E_ALIGN),  # y misaligned
+    ((FAKE, 1, 2**31, 256, FAKE, 1, FAKE), qd.QDOT_E_ARG),     # N too large
+])
+def test_qmatmul_validation(lib, args, status):
+    W, t, N, K, X, M, Y = args
+    assert lib.qdot_qmatmul(W, t, N, K, X, M, Y, None) == status
+    assert lib.qdot_qmatmul_dump_isums(W, t, N, K, X, M, Y, FAKE, None) == status
+
+
+def test_dump_needs_isums(lib):
+    assert lib.qdot_qmatmul_dump_isums(FAKE, 1, 16, 256, FAKE, 1, FAKE, 0, None) == qd.QDOT_E_ARG
+    assert lib.qdot_qmatmul_dump_isums(FAKE, 1, 16, 256, FAKE, 1, FAKE, FAKE + 2, None) == qd.QDOT_E_ALIGN
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 1, 32, FAKE), qd.QDOT_E_ARG),
+    ((FAKE, 1, 32, 0), qd.QDOT_E_ARG),
+    ((FAKE, 0, 32, FAKE), qd.QDOT_E_ARG),
+    ((FAKE, 1, 48, FAKE), qd.QDOT_E_ARG),
+    ((FAKE + 2, 1, 32, FAKE), qd.QDOT_E_ALIGN),
+    ((FAKE, 1, 32, FAKE + 1), qd.QDOT_E_ALIGN),
+])
+def test_quantize_validation(lib, args, status):
+    x, M, K, xq = args
+    assert lib.qdot_quantize_q8_1(x, M, K, xq, None) == status
+
+
+def test_binding_raises_on_error(lib):
+    with pytest.raises(qd.QdotError):
+        qd.qdot_qmatmul(FAKE, 7, 16, 256, FAKE, 1, FAKE, stream=0)
+
+
+def test_product_path_does_not_import_oracle():
+    """The HIP path never imports or loads the oracle (test infrastructure)."""
+    pkg = os.path.join(ROOT, "quant_integer_dot_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in txt and "liboracle" not in txt, f

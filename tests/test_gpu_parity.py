@@ -1,0 +1,194 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: Q8_1 bytes bit-exact; integer sub-block sums bit-exact (debug dump);
+fp32 y within relative 1e-5 of the oracle's fp64 result on every output;
+y fully written (NaN-poisoned before each call); bitwise determinism and
+batch invariance (row m of y is identical for every M in 1..8).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from quant_integer_dot_amd import binding as qd
+from quant_integer_dot_amd import synth
+
+from gpu_util import assert_close, qmatmul, quantize, to_dev
+
+pytestmark = pytest.mark.gpu
+TYPES = [synth.Q4_K, synth.Q6_K, synth.IQ4_XS]
+TN = synth.TYPE_NAMES
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qd.load()
+
+
+# ------------------------------------------------------------- quantizer
+@pytest.mark.parametrize("M,K", [(1, 32), (1, 1536), (3, 4096), (8, 12288), (8, 17408),
+                                 (5, 8960), (512, 4096), (512, 12288)])
+def test_quantizer_bytes_exact(M, K):
+    x = synth.activations(M, K, (2026, 77, K, M, 7))
+    _, got = quantize(x)
+    assert np.array_equal(got, oracle.quantize_q8_1(x).reshape(-1)), (M, K)
+
+
+def test_quantizer_edge_values():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((4, 1024)).astype(np.float32)
+    x[0, 0:32] = 0.0                                      # amax = 0
+    x[1, 32:64] *= np.float32(3e-5)                       # subnormal fp16 d
+    x[2, 64:96] = np.float32(127.0)
+    x[2, 65:73] = [0.5, -0.5, 1.5, -1.5, 2.5, -2.5, 126.5, -126.5]  # exact ties
+    x[3, 96:128] = -np.abs(x[3, 96:128])                  # all negative
+    x[3, 128:160] = np.float32(1e-38)                     # fp32-subnormal-ish inputs
+    x[3, 160:192] = np.float32(200.0) * np.sign(x[3, 160:192])
+    _, got = quantize(x)
+    assert np.array_equal(got, oracle.quantize_q8_1(x).reshape(-1))
+
+
+# ---------------------------------------------------------------- matmul
+CASES = [
+    # (N, K): several 32-row workgroup tiles plus ragged tails, one superblock
+    # up to multi-chunk K
+    (1, 256), (37, 256), (100, 512), (257, 1536), (64, 4096), (129, 5120), (50, 8960),
+]
+
+
+@pytest.mark.parametrize("wtype", TYPES)
+@pytest.mark.parametrize("N,K", CASES)
+def test_qmatmul_parity_all_M(wtype, N, K):
+    W = synth.weights(wtype, N, K, (2026, 50, N, K + wtype))
+    Wd = to_dev(W)
+    x = synth.activations(8, K, (2026, 50, K, 8, 7))
+    xqd, xq = quantize(x)
+    y64_all, _, _ = oracle.qmatmul(W, wtype, N, K, xq, 8)
+    is_all = oracle.isums(W, wtype, N, K, xq, 8)
+    ref_rows = None
+    for M in range(1, 9):
+        y, isums = qmatmul(Wd, wtype, N, K, xqd, M, dump=True)
+        assert np.array_equal(isums, is_all[:M]), f"{TN[wtype]} N={N} K={K} M={M}: isums differ"
+        assert_close(y, y64_all[:M], f"{TN[wtype]} N={N} K={K} M={M}")
+        y_plain, _ = qmatmul(Wd, wtype, N, K, xqd, M)
+        assert np.array_equal(y_plain.view(np.uint32), y.view(np.uint32)), "dump changes y"
+        # batch invariance: rows are bitwise identical for every M
+        if ref_rows is None:
+            ref_rows = y_plain
+        assert np.array_equal(y_plain[:1].view(np.uint32), ref_rows[:1].view(np.uint32))
+        if M == 8:
+            for Mp in range(1, 8):
+                yp, _ = qmatmul(Wd, wtype, N, K, xqd, Mp)
+                assert np.array_equal(yp.view(np.uint32), y_plain[:Mp].view(np.uint32)), \
+                    f"batch invariance broken at M={Mp}"
+
+
+@pytest.mark.parametrize("wtype", TYPES)
+def test_deterministic(wtype):
+    N, K, M = 300, 4096, 8
+    W = synth.weights(wtype, N, K, (3, wtype))
+    Wd = to_dev(W)
+    xqd, _ = quantize(synth.activations(M, K, (4, K, M)))
+    y1, _ = qmatmul(Wd, wtype, N, K, xqd, M)
+    y2, _ = qmatmul(Wd, wtype, N, K, xqd, M)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+@pytest.mark.parametrize("wtype", TYPES)
+def test_one_hot_probes_rebuild_dequant(wtype):
+    """x = (127/64) e_k gives y[n] = (127/64) w[n, k] exactly: sweeping k
+    through every position of two superblocks rebuilds the dequantized
+    matrix through the GPU path, pinning every element-to-bit mapping."""
+    N, K = 40, 512
+    W = synth.weights(wtype, N, K, (5, wtype))
+    Wd = to_dev(W)
+    wdeq = oracle.dequant(W, wtype, N, K)
+    for k0 in range(0, K, 8):
+        x = np.zeros((8, K), np.float32)
+        for i in range(8):
+            x[i, k0 + i] = np.float32(127 * 2.0 ** -6)
+        xqd, _ = quantize(x)
+        y, _ = qmatmul(Wd, wtype, N, K, xqd, 8)
+        exp = (127 / 64) * wdeq[:, k0:k0 + 8].T
+        assert np.array_equal(y, exp.astype(np.float32)), f"{TN[wtype]} k0={k0}"
+
+
+@pytest.mark.parametrize("wtype", TYPES)
+def test_row_subset(wtype):
+    N, K, M = 200, 1536, 3
+    W = synth.weights(wtype, N, K, (6, wtype))
+    Wd = to_dev(W)
+    xqd, _ = quantize(synth.activations(M, K, (7, K, M)))
+    y, _ = qmatmul(Wd, wtype, N, K, xqd, M)
+    n0, n1 = 33, 171
+    Wsub = Wd.reshape(-1)[n0 * qd.qdot_weight_bytes(wtype, 1, K):]   # W + n0*row_bytes
+    ys, _ = qmatmul(Wsub, wtype, n1 - n0, K, xqd, M)
+    assert np.array_equal(ys.view(np.uint32), y[:, n0:n1].view(np.uint32))
+
+
+def test_zero_activations_give_zero():
+    for wtype in TYPES:
+        N, K = 64, 1024
+        Wd = to_dev(synth.weights(wtype, N, K, (8, wtype)))
+        xqd, _ = quantize(np.zeros((4, K), np.float32))
+        y, _ = qmatmul(Wd, wtype, N, K, xqd, 4)
+        assert not y.any()
+
+
+@pytest.mark.parametrize("wtype", TYPES)
+@pytest.mark.parametrize("M", [9, 16, 33])
+def test_qmatmul_m_above_8(wtype, M):
+    N, K = 70, 1536
+    W = synth.weights(wtype, N, K, (9, wtype, M))
+    Wd = to_dev(W)
+    x = synth.activations(M, K, (10, K, M))
+    xqd, xq = quantize(x)
+    y, isums = qmatmul(Wd, wtype, N, K, xqd, M, dump=True)
+    y64, _, _ = oracle.qmatmul(W, wtype, N, K, xq, M)
+    assert np.array_equal(isums, oracle.isums(W, wtype, N, K, xq, M))
+    assert_close(y, y64, f"{TN[wtype]} M={M}")
+
+
+# ------------------------------------------- full-size shapes, sampled rows
+FULL = [(name, N, K, t) for (name, N, K, t) in synth.QWEN3_8B] + \
+       [(name, N, K, t) for (name, N, K, t) in synth.IQ4XS_H5120] + \
+       [("c1-down", 1536, 8960, synth.Q4_K), ("c0", 1536, 1536, synth.Q4_K)]
+
+
+@pytest.mark.parametrize("name,N,K,wtype", FULL)
+def test_full_size_sampled(name, N, K, wtype):
+    M = 8
+    W = synth.weights(wtype, N, K, (2026, 60, N, K))
+    Wd = to_dev(W)
+    x = synth.activations(M, K, (2026, 60, K, M, 7))
+    xqd, xq = quantize(x)
+    y, _ = qmatmul(Wd, wtype, N, K, xqd, M)
+    rng = np.random.default_rng(N + K)
+    rows = np.unique(np.concatenate([rng.integers(0, N, 48), [0, N - 1]]))
+    y64, _ = oracle.qmatmul_rows(W, wtype, N, K, xq, M, rows)
+    assert_close(y[:, rows], y64, f"{name} {N}x{K}")
+    y1, _ = qmatmul(Wd, wtype, N, K, xqd, 1)
+    assert np.array_equal(y1.view(np.uint32), y[:1].view(np.uint32)), "batch invariance"
+
+
+# ------------------------------------------------- the pages' noise anchor
+def test_noise_against_fp32_sgemv():
+    """About 0.5 % RMS against unquantized fp32 SGEMV, argmax kept (xLLM B1.3)."""
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "q8_activation_noise.json")))
+    N, K, M = 2048, 4096, 4
+    for wtype in TYPES:
+        W = synth.weights(wtype, N, K, (2026, 61, wtype, 0))
+        x = synth.activations(M, K, (2026, 61, K, M, 7))
+        xqd, _ = quantize(x)
+        y, _ = qmatmul(to_dev(W), wtype, N, K, xqd, M)
+        ref = (x @ oracle.dequant(W, wtype, N, K).astype(np.float32).T).astype(np.float64)
+        rel = np.sqrt(np.mean((y - ref) ** 2) / np.mean(ref ** 2))
+        lo, hi = g["test_band"]
+        assert lo <= rel <= hi, (TN[wtype], rel)
+        for m in range(M):
+            top = np.argsort(ref[m])[::-1]
+            if ref[m, top[0]] - ref[m, top[1]] > 6 * rel * np.sqrt(np.mean(ref[m] ** 2)):
+                assert int(np.argmax(y[m])) == int(top[0])
