@@ -1,0 +1,351 @@
+#!/usr/bin/env python3
+"""Benchmark of the integer-dot block-quantized matmul on one MI355X.
+
+Default workload: Qwen3-8B-shaped decode (hidden 4096, 36 layers; Q 4096x4096,
+K/V 1024x4096, O 4096x4096, gate/up 12288x4096, down 4096x12288; V and down in
+Q6_K, the rest Q4_K), seeded synthetic weights resident in HBM.  One step is one
+pass of the whole path for M = 1, 2, 4 and 8 token rows: per layer, four
+activation quantizations (qkv input, o input, gate/up input, down input) and the
+seven qmatmuls.  Every matrix is cold in the 256 MB Infinity Cache because a
+36-layer sweep streams 4.4 GB.
+
+Timing: each M's 36-layer sweep is captured once in a HIP graph; the timed
+region replays the step graphs between HIP events (no host launch overhead in
+the measurement).  Per-kernel durations come from graphs holding one
+projection's 36 launches, replayed between HIP events on the same stream
+(ROCm does not allow timing events inside a captured graph); they include the
+graph's sub-microsecond dispatch gaps, so they are slightly conservative
+against the rocprofv3 kernel trace.
+
+Output: one JSON line (metric, value = whole-step weight GB/s, roofline of the
+dominant kernel, the CPU oracle's rate on a bounded sample, per-M details).
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_I8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, published (TOP/s)
+METRIC = "weight GB/s (% HBM peak) and µs per qmatmul at M=1,2,4,8; Qwen3-8B shapes"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="qwen3-8b-decode",
+                   choices=["qwen3-8b-decode", "qwen3-8b-prefill-512", "iq4xs-h5120-decode",
+                            "qwen2.5-1.5b-decode"])
+    p.add_argument("--ms", default=None, help="comma-separated M values (default per workload)")
+    p.add_argument("--layers", type=int, default=None, help="override the layer count")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-check", action="store_true", help="skip the sampled oracle check")
+    p.add_argument("--kernel-reps", type=int, default=None,
+                   help="replays of each per-projection graph (default: steps)")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="run only a plain device copy of this size (PMC calibration) and exit")
+    return p.parse_args()
+
+
+def workload_def(name):
+    from quant_integer_dot_amd import synth
+    if name == "qwen3-8b-decode":
+        return 2, synth.QWEN3_8B, 36, [1, 2, 4, 8]
+    if name == "qwen3-8b-prefill-512":
+        return 4, synth.QWEN3_8B, 36, [512]
+    if name == "iq4xs-h5120-decode":
+        return 3, synth.IQ4XS_H5120, 64, [1, 2, 4, 8]
+    if name == "qwen2.5-1.5b-decode":
+        return 1, synth.QWEN25_1P5B, 28, [1, 2, 4, 8]
+    raise ValueError(name)
+
+
+# The input each projection reads: projections sharing an input share one
+# activation quantization (xLLM v0.7 log, section C: one d_xn_q8 per step).
+INPUT_OF = {"q": "attn", "k": "attn", "v": "attn", "qkv": "attn", "o": "o",
+            "gate": "ffn", "up": "ffn", "down": "down", "w": "attn"}
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib * 1024 * 1024
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+def cpu_baseline(shapes, cfg_idx, Ms, budget_s=20.0):
+    """The CPU oracle (plain scalar C, fp64, one thread) on a bounded sample:
+    the first layer's projections at each M, stopping once the budget is spent."""
+    import numpy as np
+    import oracle
+    from quant_integer_dot_amd import synth
+    done_bytes = 0
+    t_used = 0.0
+    parts = []
+    for M in Ms:
+        for pi, (name, N, K, t) in enumerate(shapes):
+            if t_used > budget_s:
+                break
+            W = synth.weights(t, N, K, synth.weight_seed(cfg_idx, 0, pi))
+            x = synth.activations(M, K, synth.act_seed(cfg_idx, K, M))
+            t0 = time.perf_counter()
+            xq = oracle.quantize_q8_1(x)
+            oracle.qmatmul(W, t, N, K, xq, M)
+            t_used += time.perf_counter() - t0
+            done_bytes += W.nbytes
+            parts.append(f"{name}@M={M}")
+    return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"layer 0 of the same workload: {', '.join(parts)} "
+                      f"({done_bytes / 1e6:.1f} MB of weights, {t_used:.1f} s, single thread, "
+                      f"quantize + qmatmul per projection; CPU: {platform.processor() or platform.machine()})"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        log(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding "
+            "of this path is a design note, not a measured configuration.")
+        sys.exit(2)
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return
+
+    import numpy as np
+    import torch
+    from quant_integer_dot_amd import binding as qd
+    from quant_integer_dot_amd import synth
+
+    qd.load()
+    dev = torch.device("cuda:0")
+    cfg_idx, shapes, layers, Ms = workload_def(args.workload)
+    if args.layers:
+        layers = args.layers
+    if args.ms:
+        Ms = [int(v) for v in args.ms.split(",")]
+    log(f"[bench] workload {args.workload}: {len(shapes)} projections x {layers} layers, M={Ms}; "
+        f"library {qd.qdot_build_id()}")
+
+    # ---------------------------------------------------------- weights
+    t0 = time.time()
+    Wdev = []   # [layer][proj] device tensors
+    for layer in range(layers):
+        row = []
+        for pi, (name, N, K, t) in enumerate(shapes):
+            row.append(torch.from_numpy(synth.weights(t, N, K, synth.weight_seed(cfg_idx, layer, pi))).to(dev))
+        Wdev.append(row)
+    torch.cuda.synchronize()
+    wbytes_sweep = sum(int(w.numel()) for row in Wdev for w in row)
+    log(f"[bench] weights resident: {wbytes_sweep / 1e9:.3f} GB in {time.time() - t0:.1f} s")
+
+    # ------------------------------------------------ activations, buffers
+    inputs = sorted({INPUT_OF[name] for name, *_ in shapes})
+    in_K = {INPUT_OF[name]: K for name, N, K, t in shapes}
+    bufs = {}
+    for M in Ms:
+        b = {"x": {}, "xq": {}, "y": {}}
+        for inp in inputs:
+            K = in_K[inp]
+            b["x"][inp] = torch.from_numpy(synth.activations(M, K, synth.act_seed(cfg_idx, K, M))).to(dev)
+            b["xq"][inp] = torch.empty(qd.qdot_q8_1_bytes(M, K), dtype=torch.uint8, device=dev)
+        for name, N, K, t in shapes:
+            b["y"][name] = torch.empty((M, N), dtype=torch.float32, device=dev)
+        bufs[M] = b
+
+    lib = qd.load()
+    stream = torch.cuda.current_stream(dev)
+
+    def sweep(M, only=None):
+        """Launch one M's sweep on the current stream (all layers)."""
+        b = bufs[M]
+        s = torch.cuda.current_stream(dev).cuda_stream
+        for layer in range(layers):
+            done_inputs = set()
+            for pi, (name, N, K, t) in enumerate(shapes):
+                inp = INPUT_OF[name]
+                if only is None and inp not in done_inputs:
+                    rc = lib.qdot_quantize_q8_1(b["x"][inp].data_ptr(), M, K, b["xq"][inp].data_ptr(), s)
+                    assert rc == 0, rc
+                    done_inputs.add(inp)
+                if only == "quantize" and inp not in done_inputs:
+                    rc = lib.qdot_quantize_q8_1(b["x"][inp].data_ptr(), M, K, b["xq"][inp].data_ptr(), s)
+                    assert rc == 0, rc
+                    done_inputs.add(inp)
+                if only is None or only == name:
+                    rc = lib.qdot_qmatmul(Wdev[layer][pi].data_ptr(), t, N, K, b["xq"][inp].data_ptr(), M,
+                                          b["y"][name].data_ptr(), s)
+                    assert rc == 0, rc
+
+    # eager run once (also fills every xq buffer)
+    for M in Ms:
+        sweep(M)
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------------- step graphs
+    graphs = {}
+    for M in Ms:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            sweep(M)
+        graphs[M] = g
+    for _ in range(args.warmup):
+        for M in Ms:
+            graphs[M].replay()
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    per_m_ms = {M: [] for M in Ms}
+    t_start, t_end = ev(), ev()
+    marks = [[ev() for _ in range(len(Ms) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start.record()
+    for k in range(args.steps):
+        marks[k][0].record()
+        for i, M in enumerate(Ms):
+            graphs[M].replay()
+            marks[k][i + 1].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    for k in range(args.steps):
+        for i, M in enumerate(Ms):
+            per_m_ms[M].append(marks[k][i].elapsed_time(marks[k][i + 1]))
+    value = len(Ms) * wbytes_sweep / (ms_per_step * 1e-3) / 1e9
+    log(f"[bench] step {ms_per_step:.3f} ms -> {value:.1f} GB/s of weights")
+
+    # ------------------------------------- per-projection kernel timing
+    reps = args.kernel_reps or args.steps
+    kern = {}      # kernel name -> [bytes, ms, launches]
+    per_m = {}
+    for M in Ms:
+        rows = {}
+        for pi, (name, N, K, t) in enumerate(shapes):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                sweep(M, only=name)
+            g.replay()
+            torch.cuda.synchronize()
+            a, bb = ev(), ev()
+            a.record()
+            for _ in range(reps):
+                g.replay()
+            bb.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(bb) * 1e3 / (reps * layers)
+            wb = qd.qdot_weight_bytes(t, N, K)
+            alg = wb + qd.qdot_q8_1_bytes(M, K) + 4 * M * N
+            rows[name] = {"N": N, "K": K, "type": synth.TYPE_NAMES[t], "us": round(us, 3),
+                          "weight_GBps": round(wb / us / 1e3, 1),
+                          "pct_hbm_peak": round(100 * wb / us / 1e3 / HBM_PEAK_GBS, 1)}
+            kn = qd.qdot_kernel_name(t, M)
+            e = kern.setdefault(kn, [0, 0.0, 0])
+            e[0] += alg * layers
+            e[1] += us * layers * 1e-3
+            e[2] += layers
+        # quantizer
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            sweep(M, only="quantize")
+        g.replay()
+        torch.cuda.synchronize()
+        a, bb = ev(), ev()
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        bb.record()
+        torch.cuda.synchronize()
+        nq = layers * len(inputs)
+        qus = a.elapsed_time(bb) * 1e3 / (reps * nq)
+        qbytes = sum(M * in_K[i] * 4 + qd.qdot_q8_1_bytes(M, in_K[i]) for i in inputs) * layers
+        e = kern.setdefault("quantize_q8_1", [0, 0.0, 0])
+        e[0] += qbytes
+        e[1] += qus * nq * 1e-3
+        e[2] += nq
+        wb_m = wbytes_sweep
+        per_m[str(M)] = {"sweep_ms": round(float(np.median(per_m_ms[M])), 4),
+                         "sweep_weight_GBps": round(wb_m / (np.median(per_m_ms[M]) * 1e-3) / 1e9, 1),
+                         "quantize_us": round(qus, 3), "qmatmul": rows}
+
+    dom = max(kern.items(), key=lambda kv: kv[1][1])
+    dname, (dbytes, dms, dn) = dom
+    achieved = dbytes / (dms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": dname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "launches": dn, "avg_launch_us": round(dms * 1e3 / dn, 3),
+                "algorithmic_bytes_per_launch": round(dbytes / dn)}
+    kernels = {k: {"launches_per_step": v[2], "ms_per_step": round(v[1], 4),
+                   "GBps": round(v[0] / (v[1] * 1e-3) / 1e9, 1)} for k, v in kern.items()}
+
+    # ------------------------------------------- sampled oracle check
+    check = None
+    if not args.no_check:
+        import oracle
+        bad = 0
+        nchk = 0
+        for M in Ms:
+            graphs[M].replay()
+            torch.cuda.synchronize()
+            b = bufs[M]
+            layer = layers - 1   # the buffers hold the last layer's outputs
+            for pi, (name, N, K, t) in enumerate(shapes):
+                W = synth.weights(t, N, K, synth.weight_seed(cfg_idx, layer, pi))
+                xq = b["xq"][INPUT_OF[name]].cpu().numpy()
+                rows = np.random.default_rng(M * 100 + pi).integers(0, N, 8)
+                y64, _ = oracle.qmatmul_rows(W, t, N, K, xq, M, rows)
+                yg = b["y"][name].cpu().numpy()[:, rows].astype(np.float64)
+                bad += int((np.abs(yg - y64) > 1e-5 * np.abs(y64)).sum())
+                nchk += y64.size
+        check = {"outputs_checked": nchk, "outside_1e-5_rel": bad}
+        if bad:
+            log(f"[bench] SAMPLED CHECK FAILED: {bad} of {nchk} outputs")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(shapes, cfg_idx, Ms)
+
+    out = {
+        "metric": METRIC if args.workload == "qwen3-8b-decode" else f"weight GB/s, {args.workload}",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "layers": layers, "M": Ms,
+                   "projections": [f"{n} {N}x{K} {synth.TYPE_NAMES[t]}" for n, N, K, t in shapes],
+                   "weight_bytes_per_sweep": wbytes_sweep,
+                   "launches_per_step": len(Ms) * layers * (len(shapes) + len(inputs))},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_M": per_m,
+        "kernels": kernels,
+        "sampled_check": check,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -7,7 +7,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/qdot.h"
+#include "qdot.h"
 
 namespace qdot {
 int launch_quantize_q8_1(const float* x, int64_t M, int64_t K, void* xq, hipStream_t s);

@@ -13,27 +13,19 @@
 //  * exact int32 sums inside each sub-block, scales applied afterwards
 //    (Kestrel section 5).
 // What differs from the pages' V100 design: the M=8 V100 kernel was L1-bound
-// (xLLM section B2 ncu table).  Here the activations of a K-chunk are staged
-// once per workgroup into LDS (int8 codes plus fp64 scales), each lane keeps
-// the activation dwords of its current block in VGPRs and reuses them for R
-// weight rows, and the scale drains are exact fp64 terms (every product exact,
-// one rounding per accumulate), so y is the fp32 rounding of a value within a
-// few fp64 ulps of the exact sum.
-//
-// Mapping (256 threads = 4 waves of 64):
-//  * lane = (slot s = lane/4, quarter q = lane%4).  A quarter is 64 weights of
-//    a superblock = two Q8_1 activation blocks, in all three formats;
-//  * the workgroup owns rows n0 + s + 16*r (r < R): 16*R rows;
-//  * wave w takes superblocks b = w, w+4, ... of the current K-chunk;
-//  * the partial sums are reduced over the 4 quarter lanes (xor shuffles), then
-//    over the 4 waves through LDS in a fixed order (deterministic, and the same
-//    for every M: row m of y does not depend on M).
+// (xLLM section B2 ncu table).  Here, for small M each lane reads its two
+// activation blocks straight from L1/L2 (one cache line per quarter serves
+// the 16 rows of a wave); for larger M a workgroup stages the activations
+// once into LDS (int8 codes plus fp64 scales) and each lane reuses every
+// activation dword it reads for R weight rows.  The scale drains are exact
+// fp64 terms (every product exact, one rounding per accumulate), so y is the
+// fp32 rounding of a value within a few fp64 ulps of the exact sum.
+
 #include "qdot_common.hpp"
 
 namespace qdot {
 
-constexpr int QMV_THREADS = 256;
-constexpr int QMV_WAVES = 4;
+constexpr int QMV_MAX_THREADS = 512;  // up to 8 waves per workgroup
 constexpr int QMV_SLOTS = 16;  // row slots per wave (64 lanes / 4 quarters)
 
 // One LDS entry per Q8_1 block and row m: the fp64 scale D and a second field
@@ -123,193 +115,142 @@ __device__ __forceinline__ uint32_t cb_lookup(uint32_t idx, uint32_t t0, uint32_
   return perm(hi, lo, pick);
 }
 
-// ---------------------------------------------------------------- kernel
+// ---------------------------------------------------------------- kernels
+//
+// One lane handles quarter q of superblock b for R weight rows (slot s, rows
+// n0 + s + 16*r).  The P waves of a workgroup split the superblocks of each
+// row: wave w takes b = w, w+P, ...  P is a function of K only, and every
+// kernel below walks a lane's superblocks, halves and rows in the same order
+// with the same fp64 operations, so each output is computed by the same
+// sequence of roundings whatever M is (row m of y does not depend on M).
+//
+// The workgroup stages the activations of a K-chunk once into LDS (int8
+// codes and fp64 scales); each lane reads the activation dwords of its
+// current block from LDS and reuses them for its R weight rows.
+
+// Per-row, per-half-quarter weight data: the 8 code dwords (32 int8 codes in
+// activation order) and what the drain needs.
+template <int T> struct Sub;
+template <> struct Sub<Q4_K> { uint32_t cw[8]; double wsc, wmn; };
+template <> struct Sub<IQ4_XS> { uint32_t cw[8]; double wsc; };
+template <> struct Sub<Q6_K> { uint32_t cw[8]; int s0, s1; double d; };
+
+template <int T>
+__device__ __forceinline__ void decode_sub(const typename Fmt<T>::Regs& g, int q, int half,
+                                           Sub<T>& o) {
+  if constexpr (T == Q4_K) {
+    // sub-block j = 2q + half: 6-bit scale and min (plain GGUF packing); q < 2
+    // reads scales[j], scales[j+4]; q >= 2 splices the nibbles of scales[j+4]
+    // with the top two bits of scales[j-4] (scale) and scales[j] (min).
+    const int sh = 8 * (((2 * q) & 3) + half);
+    const bool lo = q < 2;
+    const uint32_t Ys = g.h.y >> sh, Zs = g.h.z >> sh, Ws = g.h.w >> sh;
+    const uint32_t sc = lo ? (Ys & 63u) : ((Ws & 15u) | ((Ys >> 2) & 0x30u));
+    const uint32_t mn = lo ? (Zs & 63u) : (((Ws >> 4) & 15u) | ((Zs >> 2) & 0x30u));
+    o.wsc = (double)(h2f(g.h.x) * (float)sc);          // d*sc, exact in fp32
+    o.wmn = -(double)(h2f(g.h.x >> 16) * (float)mn);   // -dmin*m, exact in fp32
+    const uint32_t pk[8] = {g.a.x, g.a.y, g.a.z, g.a.w, g.b.x, g.b.y, g.b.z, g.b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o.cw[i] = (half ? (pk[i] >> 4) : pk[i]) & 0x0F0F0F0Fu;
+  } else if constexpr (T == IQ4_XS) {
+    const int j = 2 * q + half;
+    const uint32_t sl = (g.h.y >> (4 * j)) & 15u;
+    const uint32_t shb = ((g.h.x >> 16) >> (2 * j)) & 3u;
+    const int ls = (int)(sl | (shb << 4));
+    o.wsc = (double)(h2f(g.h.x) * (float)(ls - 32));  // d*(ls-32), exact in fp32
+    const u32x4 pq = half ? g.b : g.a;
+    const uint32_t pk[4] = {pq.x, pq.y, pq.z, pq.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o.cw[i] = cb_lookup(pk[i], CB0, CB1, CB2, CB3);           // elements 4i..4i+3
+      o.cw[i + 4] = cb_lookup(pk[i] >> 4, CB0, CB1, CB2, CB3);  // elements 16+4i..
+    }
+  } else {  // Q6_K
+    const int h = q >> 1, gp = q & 1;
+    // codes of Q8 block 4h+gp (half 0: g = gp, low nibbles) or 4h+gp+2 (half
+    // 1: g = gp+2, high nibbles): values 0..63; the -32 offset is applied
+    // through the activation half-sums.
+    const uint32_t pl[8] = {g.a.x, g.a.y, g.a.z, g.a.w, g.b.x, g.b.y, g.b.z, g.b.w};
+    const uint32_t ph[8] = {g.c.x, g.c.y, g.c.z, g.c.w, g.e.x, g.e.y, g.e.z, g.e.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (half == 0)
+        o.cw[i] = (pl[i] & 0x0F0F0F0Fu) | ((ph[i] << (4 - 2 * gp)) & 0x30303030u);
+      else
+        o.cw[i] = ((pl[i] >> 4) & 0x0F0F0F0Fu) | ((ph[i] >> (2 * gp)) & 0x30303030u);
+    }
+    // int8 sub-scales of sub-blocks t0 = 8h + 2gp + 4*half and t0 + 1
+    const uint32_t scw = h ? (half ? g.sc.w : g.sc.z) : (half ? g.sc.y : g.sc.x);
+    o.s0 = (int)(int8_t)(scw >> (16 * gp));
+    o.s1 = (int)(int8_t)(scw >> (16 * gp + 8));
+    o.d = (double)h2f(g.d);
+  }
+}
+
+// Index of the first sub-block (of length SUB) that (q, half) covers inside
+// its superblock; Q6_K covers two consecutive 16-element sub-blocks.
+template <int T> __device__ __forceinline__ int sub_index(int q, int half) {
+  if constexpr (T == Q6_K) return 8 * (q >> 1) + 2 * (q & 1) + 4 * half;
+  else return 2 * q + half;
+}
+
+// fp64 view of one Q8_1 block's scales: D and (Q4_K) S, or (Q6_K) 32 times
+// the integer sum of each 16-element half of q (for the -32 code offset).
+__device__ __forceinline__ DsEntry ds_entry(int T, uint32_t ds, const u32x4& q0, const u32x4& q1) {
+  DsEntry e;
+  e.d = (double)h2f(ds & 0xFFFFu);
+  if (T == Q6_K) {
+    const uint32_t ones = 0x01010101u;
+    const int lo = dot4(q0.w, ones, dot4(q0.z, ones, dot4(q0.y, ones, dot4(q0.x, ones, 0))));
+    const int hi = dot4(q1.w, ones, dot4(q1.z, ones, dot4(q1.y, ones, dot4(q1.x, ones, 0))));
+    e.xs32[0] = 32 * lo;
+    e.xs32[1] = 32 * hi;
+  } else {
+    e.s = (double)h2f(ds >> 16);
+  }
+  return e;
+}
+
+// The integer dots of one (row, activation row, half quarter) and their
+// exact-term fp64 drain into acc.  Optionally stores the int32 sums.
+template <int T, bool DUMP>
+__device__ __forceinline__ void dot_drain(const Sub<T>& sw, const uint32_t (&xa)[8],
+                                          const DsEntry& de, double& acc, int32_t* isp) {
+  if constexpr (T == Q6_K) {
+    int I0 = 0, I1 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) I0 = dot4(sw.cw[i], xa[i], I0);
+#pragma unroll
+    for (int i = 4; i < 8; ++i) I1 = dot4(sw.cw[i], xa[i], I1);
+    I0 -= de.xs32[0];
+    I1 -= de.xs32[1];
+    const int Pq = sw.s0 * I0 + sw.s1 * I1;               // exact int
+    acc = fma(sw.d * de.d, (double)Pq, acc);              // exact product, one rounding
+    if (DUMP && isp) { isp[0] = I0; isp[1] = I1; }
+  } else {
+    int I = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) I = dot4(sw.cw[i], xa[i], I);
+    acc = fma(sw.wsc * de.d, (double)I, acc);             // exact product, one rounding
+    if constexpr (T == Q4_K) acc = fma(sw.wmn, de.s, acc);
+    if (DUMP && isp) isp[0] = I;
+  }
+}
+
 template <int T, int M, int R, bool DUMP>
-__global__ __launch_bounds__(QMV_THREADS) void qmv_dot4_kernel(
-    const uint8_t* __restrict__ W, int N, int K, const uint8_t* __restrict__ xq,
-    float* __restrict__ y, int32_t* __restrict__ isums, int kc) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr int BYTES = Geom<T>::BYTES;
+__device__ __forceinline__ int32_t* isum_ptr(int32_t* isums, int N, int K, int m, int n, int b, int q,
+                                             int half) {
   constexpr int SUB = Geom<T>::SUB;
-  const int nsb = K / QK;                  // superblocks per row
-  const size_t row_bytes = (size_t)nsb * BYTES;
-  const int nq8 = K / Q8_BLOCK;            // Q8_1 blocks per activation row
+  if (!DUMP || n >= N) return nullptr;
+  return isums + ((size_t)m * N + n) * (K / SUB) + (size_t)b * (QK / SUB) + sub_index<T>(q, half);
+}
 
-  uint8_t* lds_x = smem;                                   // int8 [M][kc]
-  DsEntry* lds_ds = reinterpret_cast<DsEntry*>(smem + (size_t)M * kc);  // [M][kc/32]
-  double* lds_red = reinterpret_cast<double*>(smem + (size_t)M * kc + (size_t)M * (kc / 32) * sizeof(DsEntry));
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int slot = lane >> 2;
-  const int q = lane & 3;
-  const int n0 = blockIdx.x * (QMV_SLOTS * R);
-
-  // Rows of this lane; rows past N re-read row N-1 and are never stored.
-  const uint8_t* wrow[R];
-  int nrow[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    nrow[r] = n0 + slot + QMV_SLOTS * r;
-    const int nc = nrow[r] < N ? nrow[r] : N - 1;
-    wrow[r] = W + (size_t)nc * row_bytes;
-  }
-
-  double acc[R][M];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int m = 0; m < M; ++m) acc[r][m] = 0.0;
-
-  for (int c0 = 0; c0 < K; c0 += kc) {
-    const int kcc = (K - c0) < kc ? (K - c0) : kc;
-    const int nblk = kcc / Q8_BLOCK;
-    __syncthreads();
-    // ---- stage the chunk's activations: int8 codes and fp64 scales
-    for (int it = tid; it < M * nblk; it += QMV_THREADS) {
-      const int m = it / nblk, kb = it - m * nblk;
-      const uint8_t* src = xq + ((size_t)m * nq8 + c0 / Q8_BLOCK + kb) * Q8_BYTES;
-      const uint32_t ds = ld4(src);
-      const u32x4 q0 = ld16(src + 4), q1 = ld16(src + 20);
-      *reinterpret_cast<u32x4*>(lds_x + (size_t)m * kc + Q8_BLOCK * kb) = q0;
-      *reinterpret_cast<u32x4*>(lds_x + (size_t)m * kc + Q8_BLOCK * kb + 16) = q1;
-      DsEntry e;
-      e.d = (double)h2f(ds & 0xFFFFu);
-      if (T == Q6_K) {
-        const uint32_t ones = 0x01010101u;
-        const int lo = dot4(q0.w, ones, dot4(q0.z, ones, dot4(q0.y, ones, dot4(q0.x, ones, 0))));
-        const int hi = dot4(q1.w, ones, dot4(q1.z, ones, dot4(q1.y, ones, dot4(q1.x, ones, 0))));
-        e.xs32[0] = 32 * lo;
-        e.xs32[1] = 32 * hi;
-      } else {
-        e.s = (double)h2f(ds >> 16);
-      }
-      lds_ds[(size_t)m * (kc / 32) + kb] = e;
-    }
-    __syncthreads();
-
-    const int nsb_c = kcc / QK;
-    const int sb0 = c0 / QK;
-    for (int bl = wave; bl < nsb_c; bl += QMV_WAVES) {
-      const int b = sb0 + bl;
-      typename Fmt<T>::Regs rg[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) rg[r] = Fmt<T>::load(wrow[r] + (size_t)b * BYTES, q);
-
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int kb = bl * (QK / Q8_BLOCK) + Fmt<T>::blk(q, half);  // chunk-local Q8 block
-        uint32_t xa[M][8];
-        DsEntry de[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const u32x4 v0 = *reinterpret_cast<const u32x4*>(lds_x + (size_t)m * kc + Q8_BLOCK * kb);
-          const u32x4 v1 = *reinterpret_cast<const u32x4*>(lds_x + (size_t)m * kc + Q8_BLOCK * kb + 16);
-          xa[m][0] = v0.x; xa[m][1] = v0.y; xa[m][2] = v0.z; xa[m][3] = v0.w;
-          xa[m][4] = v1.x; xa[m][5] = v1.y; xa[m][6] = v1.z; xa[m][7] = v1.w;
-          de[m] = lds_ds[(size_t)m * (kc / 32) + kb];
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const typename Fmt<T>::Regs& g = rg[r];
-          if constexpr (T == Q4_K) {
-            // sub-block j = 2q + half: 6-bit scale and min (plain GGUF packing)
-            const int p = (2 * q) & 3;
-            const uint32_t Ys = g.h.y >> (8 * p), Zs = g.h.z >> (8 * p), Ws = g.h.w >> (8 * p);
-            const int sh = 8 * half;
-            uint32_t sc, mn;
-            if (q < 2) {
-              sc = (Ys >> sh) & 63u;
-              mn = (Zs >> sh) & 63u;
-            } else {
-              sc = ((Ws >> sh) & 15u) | ((Ys >> (sh + 2)) & 0x30u);
-              mn = ((Ws >> (sh + 4)) & 15u) | ((Zs >> (sh + 2)) & 0x30u);
-            }
-            const double wsc = (double)(h2f(g.h.x) * (float)sc);          // d*sc, exact
-            const double wmn = -(double)(h2f(g.h.x >> 16) * (float)mn);   // -dmin*m, exact
-            const uint32_t pk[8] = {g.a.x, g.a.y, g.a.z, g.a.w, g.b.x, g.b.y, g.b.z, g.b.w};
-            uint32_t cw[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) cw[i] = (half ? (pk[i] >> 4) : pk[i]) & 0x0F0F0F0Fu;
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-              int I = 0;
-#pragma unroll
-              for (int i = 0; i < 8; ++i) I = dot4(cw[i], xa[m][i], I);
-              acc[r][m] = fma(wsc * de[m].d, (double)I, acc[r][m]);
-              acc[r][m] = fma(wmn, de[m].s, acc[r][m]);
-              if (DUMP && nrow[r] < N)
-                isums[((size_t)m * N + nrow[r]) * (K / SUB) + (size_t)b * (QK / SUB) + 2 * q + half] = I;
-            }
-          } else if constexpr (T == IQ4_XS) {
-            const int j = 2 * q + half;
-            const uint32_t sl = (g.h.y >> (4 * j)) & 15u;
-            const uint32_t shb = ((g.h.x >> 16) >> (2 * j)) & 3u;
-            const int ls = (int)(sl | (shb << 4));
-            const double wsc = (double)(h2f(g.h.x) * (float)(ls - 32));  // d*(ls-32), exact
-            const u32x4 pq = half ? g.b : g.a;
-            const uint32_t pk[4] = {pq.x, pq.y, pq.z, pq.w};
-            uint32_t cw[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              cw[i] = cb_lookup(pk[i], CB0, CB1, CB2, CB3);              // elements 4i..4i+3
-              cw[i + 4] = cb_lookup(pk[i] >> 4, CB0, CB1, CB2, CB3);     // elements 16+4i..
-            }
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-              int I = 0;
-#pragma unroll
-              for (int i = 0; i < 8; ++i) I = dot4(cw[i], xa[m][i], I);
-              acc[r][m] = fma(wsc * de[m].d, (double)I, acc[r][m]);
-              if (DUMP && nrow[r] < N)
-                isums[((size_t)m * N + nrow[r]) * (K / SUB) + (size_t)b * (QK / SUB) + j] = I;
-            }
-          } else {  // Q6_K
-            const int h = q >> 1, gp = q & 1;
-            // codes for Q8 block (half 0: g = gp from low nibbles; half 1:
-            // g = gp+2 from high nibbles); values 0..63, the -32 offset is
-            // applied through the activation sums.
-            const uint32_t pl[8] = {g.a.x, g.a.y, g.a.z, g.a.w, g.b.x, g.b.y, g.b.z, g.b.w};
-            const uint32_t ph[8] = {g.c.x, g.c.y, g.c.z, g.c.w, g.e.x, g.e.y, g.e.z, g.e.w};
-            uint32_t cw[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              if (half == 0)
-                cw[i] = (pl[i] & 0x0F0F0F0Fu) | ((ph[i] << (4 - 2 * gp)) & 0x30303030u);
-              else
-                cw[i] = ((pl[i] >> 4) & 0x0F0F0F0Fu) | ((ph[i] >> (2 * gp)) & 0x30303030u);
-            }
-            // int8 sub-scales of sub-blocks t0 = 8h + 2gp + 4*half and t0 + 1
-            const uint32_t scw = h ? (half ? g.sc.w : g.sc.z) : (half ? g.sc.y : g.sc.x);
-            const int s0 = (int)(int8_t)(scw >> (16 * gp));
-            const int s1 = (int)(int8_t)(scw >> (16 * gp + 8));
-            const float d = h2f(g.d);
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-              int I0 = 0, I1 = 0;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) I0 = dot4(cw[i], xa[m][i], I0);
-#pragma unroll
-              for (int i = 4; i < 8; ++i) I1 = dot4(cw[i], xa[m][i], I1);
-              I0 -= de[m].xs32[0];
-              I1 -= de[m].xs32[1];
-              const int P = s0 * I0 + s1 * I1;
-              acc[r][m] = fma((double)d * de[m].d, (double)P, acc[r][m]);
-              if (DUMP && nrow[r] < N) {
-                const size_t base = ((size_t)m * N + nrow[r]) * (K / SUB) + (size_t)b * (QK / SUB) +
-                                    8 * h + 2 * gp + 4 * half;
-                isums[base] = I0;
-                isums[base + 1] = I1;
-              }
-            }
-          }
-        }
-      }
-    }
-  }
-
-  // ---- reduce over the 4 quarter lanes, then over the 4 waves
+// Quad reduction (the 4 quarter lanes of a slot), then over the P waves in
+// order through LDS, then the fp32 store.  lds_red holds P*16*R*M doubles.
+template <int M, int R>
+__device__ __forceinline__ void reduce_store(double (&acc)[R][M], double* lds_red, int P, int wave,
+                                             int slot, int q, int tid, int n0, int N,
+                                             float* __restrict__ y) {
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -319,7 +260,7 @@ __global__ __launch_bounds__(QMV_THREADS) void qmv_dot4_kernel(
       v += __shfl_xor(v, 2);
       acc[r][m] = v;
     }
-  __syncthreads();
+  __syncthreads();  // the staging area is reused for the reduction
   if (q == 0) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -328,57 +269,197 @@ __global__ __launch_bounds__(QMV_THREADS) void qmv_dot4_kernel(
         lds_red[((wave * QMV_SLOTS + slot) * R + r) * M + m] = acc[r][m];
   }
   __syncthreads();
-  for (int o = tid; o < QMV_SLOTS * R * M; o += QMV_THREADS) {
+  for (int o = tid; o < QMV_SLOTS * R * M; o += 64 * P) {
     const int m = o % M;
     const int r = (o / M) % R;
     const int s = o / (M * R);
     const int n = n0 + s + QMV_SLOTS * r;
-    double v = lds_red[((0 * QMV_SLOTS + s) * R + r) * M + m];
-#pragma unroll
-    for (int w = 1; w < QMV_WAVES; ++w) v += lds_red[((w * QMV_SLOTS + s) * R + r) * M + m];
+    double v = lds_red[(s * R + r) * M + m];
+    for (int w = 1; w < P; ++w) v += lds_red[((w * QMV_SLOTS + s) * R + r) * M + m];
     if (n < N) y[(size_t)m * N + n] = (float)v;
   }
 }
 
-// ------------------------------------------------------------- launcher
-template <int M> struct QmvCfg { static constexpr int R = 2; };
+// ------------------------------------------------------ the decode kernel
+constexpr int QMV_MGROUP = 4;  // activation rows held in registers at once
 
-// LDS budget per workgroup for the activation chunk.
-constexpr int QMV_LDS_BUDGET = 64 * 1024;
-
-template <int T, int M, bool DUMP>
-static int launch_qmv_t(const uint8_t* W, int N, int K, const uint8_t* xq, float* y,
-                        int32_t* isums, hipStream_t s) {
-  constexpr int R = QmvCfg<M>::R;
-  // K-chunk: multiple of 256 that fits the LDS budget, chunks of equal size.
-  const int per_k = M + M * 16 / Q8_BLOCK;  // bytes of LDS per activation column
-  const int red_bytes = QMV_WAVES * QMV_SLOTS * R * M * (int)sizeof(double);
-  int kcmax = ((QMV_LDS_BUDGET - red_bytes) / per_k) / QK * QK;
-  if (kcmax < QK) kcmax = QK;
+template <int T, int M, int R, int DEPTH, bool DUMP>
+__global__ __launch_bounds__(QMV_MAX_THREADS) void qmv_lds_kernel(
+    const uint8_t* __restrict__ W, int N, int K, const uint8_t* __restrict__ xq,
+    float* __restrict__ y, int32_t* __restrict__ isums, int kc) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int BYTES = Geom<T>::BYTES;
+  const int P = blockDim.x >> 6;
   const int nsb = K / QK;
-  const int nchunk = (K + kcmax - 1) / kcmax;
-  const int kc = ((nsb + nchunk - 1) / nchunk) * QK;
-  const size_t lds = (size_t)M * kc + (size_t)M * (kc / Q8_BLOCK) * sizeof(DsEntry) + red_bytes;
+  const size_t row_bytes = (size_t)nsb * BYTES;
+  const int nq8 = K / Q8_BLOCK;
+  const int kc_sb = kc / QK;  // superblocks per chunk (a multiple of P)
+  uint8_t* lds_x = smem;                                                  // int8 [M][kc]
+  DsEntry* lds_ds = reinterpret_cast<DsEntry*>(smem + (size_t)M * kc);  // [M][kc/32]
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, slot = lane >> 2, q = lane & 3;
+  const int n0 = blockIdx.x * (QMV_SLOTS * R);
+
+  const uint8_t* wrow[R];
+  int nrow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    nrow[r] = n0 + slot + QMV_SLOTS * r;
+    const int nc = nrow[r] < N ? nrow[r] : N - 1;
+    wrow[r] = W + (size_t)nc * row_bytes;
+  }
+  double acc[R][M];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.0;
+
+  // DEPTH weight stages in flight (a ring of register sets).  The prefetch
+  // loads are unconditional (superblock clamped to the row) so the compiler
+  // waits for exactly the stage a compute step uses.
+  typename Fmt<T>::Regs S[DEPTH][R];
+  auto prefetch = [&](typename Fmt<T>::Regs (&X)[R], int bsb) {
+    const int bc = bsb < nsb ? bsb : nsb - 1;
+#pragma unroll
+    for (int r = 0; r < R; ++r) X[r] = Fmt<T>::load(wrow[r] + (size_t)bc * BYTES, q);
+  };
+  // Stage activations [c0, c0 + kc) into LDS: int8 codes and fp64 scales.
+  auto stage = [&](int chunk) {
+    const int c0 = chunk * kc;
+    const int kcc = (K - c0) < kc ? (K - c0) : kc;
+    const int nblk = kcc / Q8_BLOCK;
+    for (int it = tid; it < M * nblk; it += blockDim.x) {
+      const int m = it / nblk, kb = it - m * nblk;
+      const uint8_t* src = xq + ((size_t)m * nq8 + c0 / Q8_BLOCK + kb) * Q8_BYTES;
+      const uint32_t ds = ld4(src);
+      const u32x4 q0 = ld16(src + 4), q1 = ld16(src + 20);
+      *reinterpret_cast<u32x4*>(lds_x + (size_t)m * kc + Q8_BLOCK * kb) = q0;
+      *reinterpret_cast<u32x4*>(lds_x + (size_t)m * kc + Q8_BLOCK * kb + 16) = q1;
+      lds_ds[(size_t)m * (kc / Q8_BLOCK) + kb] = ds_entry(T, ds, q0, q1);
+    }
+  };
+  auto compute = [&](const typename Fmt<T>::Regs (&rg)[R], int b, int bl) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int kb = bl * (QK / Q8_BLOCK) + Fmt<T>::blk(q, half);  // chunk-local Q8 block
+      Sub<T> sw[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) decode_sub<T>(rg[r], q, half, sw[r]);
+#pragma unroll
+      for (int m0 = 0; m0 < M; m0 += QMV_MGROUP) {
+        const int mg = (M - m0) < QMV_MGROUP ? (M - m0) : QMV_MGROUP;
+        uint32_t xa[QMV_MGROUP][8];
+        DsEntry de[QMV_MGROUP];
+#pragma unroll
+        for (int mm = 0; mm < QMV_MGROUP; ++mm) {
+          if (mm < mg) {
+            const int m = m0 + mm;
+            const u32x4 v0 = *reinterpret_cast<const u32x4*>(lds_x + (size_t)m * kc + Q8_BLOCK * kb);
+            const u32x4 v1 = *reinterpret_cast<const u32x4*>(lds_x + (size_t)m * kc + Q8_BLOCK * kb + 16);
+            xa[mm][0] = v0.x; xa[mm][1] = v0.y; xa[mm][2] = v0.z; xa[mm][3] = v0.w;
+            xa[mm][4] = v1.x; xa[mm][5] = v1.y; xa[mm][6] = v1.z; xa[mm][7] = v1.w;
+            de[mm] = lds_ds[(size_t)m * (kc / Q8_BLOCK) + kb];
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int mm = 0; mm < QMV_MGROUP; ++mm)
+            if (mm < mg)
+              dot_drain<T, DUMP>(sw[r], xa[mm], de[mm], acc[r][m0 + mm],
+                                 isum_ptr<T, M, R, DUMP>(isums, N, K, m0 + mm, nrow[r], b, q, half));
+      }
+    }
+  };
+
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) prefetch(S[d], wave + d * P);
+  stage(0);
+  __syncthreads();
+  const int ipc = kc_sb / P;  // iterations per chunk (a multiple of DEPTH)
+  const int niter = (((nsb + P - 1) / P) + DEPTH - 1) / DEPTH * DEPTH;
+  auto step = [&](typename Fmt<T>::Regs (&X)[R], int ii, bool refill) {
+    if (ii > 0 && ii % ipc == 0) {  // next chunk (only when K does not fit one chunk)
+      __syncthreads();
+      stage(ii / ipc);
+      __syncthreads();
+    }
+    const int b = wave + ii * P;
+    if (b < nsb) compute(X, b, b - (ii / ipc) * kc_sb);
+    if (refill) prefetch(X, b + DEPTH * P);
+  };
+  // The last DEPTH iterations are peeled so that no prefetch runs past the
+  // row (a redundant load would still have to land before the wave retires).
+  int i = 0;
+  for (; i + DEPTH < niter; i += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) step(S[d], i + d, true);
+  }
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) step(S[d], i + d, false);
+  reduce_store<M, R>(acc, reinterpret_cast<double*>(smem), P, wave, slot, q, tid, n0, N, y);
+}
+
+// ------------------------------------------------------------- launcher
+constexpr int QMV_LDS_BUDGET = 64 * 1024;
+// Tuning constants, chosen by measurement on MI355X (Qwen3-8B shapes, M = 1..8):
+// one weight row per lane beat two at every M (more workgroups matter more
+// than reusing each LDS activation read twice), and two prefetch stages beat
+// four.  Lanes reading their activations straight from L1/L2 instead of LDS
+// was slower at M = 1 and 2 (each lane pulls more activation than weight
+// bytes through the vector memory return path).
+constexpr int QMV_ROWS = 1;   // weight rows per lane (R)
+constexpr int QMV_DEPTH = 2;  // weight prefetch stages in flight
+
+// Waves per workgroup: a function of K only (the K split fixes the fp64
+// summation order, which must not depend on M): about four superblocks per
+// wave, at most eight waves.
+static int qmv_waves(int nsb) {
+  const int p = (nsb + 3) / 4;
+  return p < 1 ? 1 : (p > 8 ? 8 : p);
+}
+
+template <int T, int M, int R, int DEPTH, bool DUMP>
+static int launch_lds(const uint8_t* W, int N, int K, const uint8_t* xq, float* y, int32_t* isums,
+                      hipStream_t s) {
+  const int nsb = K / QK;
+  const int P = qmv_waves(nsb);
+  const int per_k = M + M * (int)sizeof(DsEntry) / Q8_BLOCK;  // LDS bytes per activation column
+  // chunk = multiple of P*DEPTH superblocks that fits the budget (the last
+  // chunk may be short), so every wave changes chunk at the same iteration
+  const int unit = P * DEPTH;
+  int kc_sb = (QMV_LDS_BUDGET / per_k) / QK / unit * unit;
+  if (kc_sb < unit) return -1;
+  if (kc_sb >= nsb) kc_sb = ((nsb + unit - 1) / unit) * unit;
+  const int kc = kc_sb * QK;
+  const size_t stage = (size_t)M * kc + (size_t)M * (kc / Q8_BLOCK) * sizeof(DsEntry);
+  const size_t red = (size_t)P * QMV_SLOTS * R * M * sizeof(double);
+  const size_t lds = stage > red ? stage : red;
   if (lds > (size_t)QMV_LDS_BUDGET) return -1;
   const int rows_per_wg = QMV_SLOTS * R;
   const int grid = (N + rows_per_wg - 1) / rows_per_wg;
-  hipLaunchKernelGGL((qmv_dot4_kernel<T, M, R, DUMP>), dim3(grid), dim3(QMV_THREADS), lds, s, W, N,
+  hipLaunchKernelGGL((qmv_lds_kernel<T, M, R, DEPTH, DUMP>), dim3(grid), dim3(64 * P), lds, s, W, N,
                      K, xq, y, isums, kc);
   return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <int T, int M, bool DUMP>
+static int launch_qmv_r(const uint8_t* W, int N, int K, const uint8_t* xq, float* y,
+                        int32_t* isums, hipStream_t s) {
+  return launch_lds<T, M, QMV_ROWS, QMV_DEPTH, DUMP>(W, N, K, xq, y, isums, s);
 }
 
 template <int T, bool DUMP>
 static int launch_qmv_m(const uint8_t* W, int N, int K, const uint8_t* xq, int M, float* y,
                         int32_t* isums, hipStream_t s) {
   switch (M) {
-    case 1: return launch_qmv_t<T, 1, DUMP>(W, N, K, xq, y, isums, s);
-    case 2: return launch_qmv_t<T, 2, DUMP>(W, N, K, xq, y, isums, s);
-    case 3: return launch_qmv_t<T, 3, DUMP>(W, N, K, xq, y, isums, s);
-    case 4: return launch_qmv_t<T, 4, DUMP>(W, N, K, xq, y, isums, s);
-    case 5: return launch_qmv_t<T, 5, DUMP>(W, N, K, xq, y, isums, s);
-    case 6: return launch_qmv_t<T, 6, DUMP>(W, N, K, xq, y, isums, s);
-    case 7: return launch_qmv_t<T, 7, DUMP>(W, N, K, xq, y, isums, s);
-    case 8: return launch_qmv_t<T, 8, DUMP>(W, N, K, xq, y, isums, s);
+    case 1: return launch_qmv_r<T, 1, DUMP>(W, N, K, xq, y, isums, s);
+    case 2: return launch_qmv_r<T, 2, DUMP>(W, N, K, xq, y, isums, s);
+    case 3: return launch_qmv_r<T, 3, DUMP>(W, N, K, xq, y, isums, s);
+    case 4: return launch_qmv_r<T, 4, DUMP>(W, N, K, xq, y, isums, s);
+    case 5: return launch_qmv_r<T, 5, DUMP>(W, N, K, xq, y, isums, s);
+    case 6: return launch_qmv_r<T, 6, DUMP>(W, N, K, xq, y, isums, s);
+    case 7: return launch_qmv_r<T, 7, DUMP>(W, N, K, xq, y, isums, s);
+    case 8: return launch_qmv_r<T, 8, DUMP>(W, N, K, xq, y, isums, s);
     default: return -2;
   }
 }
