@@ -24,6 +24,12 @@ COMMON = [
 ]
 
 
+# Per-source extra flags.  qmm.hip: keep MFMA results in VGPRs (the VALU
+# drains read every result register; accumulation registers would cost one
+# v_accvgpr_read per result).
+EXTRA = {"qmm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith((".hip", ".cpp")))
@@ -31,9 +37,10 @@ def sources():
 
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + COMMON + ["-c", src, "-o", obj]
+    extra = EXTRA.get(os.path.basename(src), [])
+    cmd = [HIPCC] + COMMON + extra + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
-        cmd = [HIPCC] + COMMON + ["-x", "hip", "-c", src, "-o", obj]
+        cmd = [HIPCC] + COMMON + extra + ["-x", "hip", "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,21 +1,24 @@
-// qmm.hip -- M > 8 (prefill) entry.  Placeholder until the MFMA i8 kernel:
-// runs the decode kernel over 8-row chunks of the activations.
-#include "qdot_common.hpp"
+// qmm.hip -- launches of the prefill kernel (M > 8).  The kernel itself is
+// in qmm_kernel.hpp; this file is built with MFMA results in VGPRs, the
+// sub-block-sum dump variant in qmm_dump.hip without that option.
+#include "qmm_kernel.hpp"
 
 namespace qdot {
-int launch_qmv(const void* W, int type, int N, int K, const void* xq, int M, float* y,
-               int32_t* isums, hipStream_t s);
+
+int launch_qmm_dump(const uint8_t* W, int type, int N, int K, const uint8_t* xq, int M, float* y,
+                    int32_t* isums, hipStream_t s);
 
 int launch_qmm(const void* W, int type, int N, int K, const void* xq, int M, float* y,
                int32_t* isums, hipStream_t s) {
-  const int sub = type == Q6_K ? 16 : 32;
-  for (int m0 = 0; m0 < M; m0 += 8) {
-    const int mc = M - m0 < 8 ? M - m0 : 8;
-    const uint8_t* x = static_cast<const uint8_t*>(xq) + (size_t)m0 * (K / Q8_BLOCK) * Q8_BYTES;
-    int32_t* is = isums ? isums + (size_t)m0 * N * (K / sub) : nullptr;
-    int rc = launch_qmv(W, type, N, K, x, mc, y + (size_t)m0 * N, is, s);
-    if (rc) return rc;
+  const uint8_t* w8 = static_cast<const uint8_t*>(W);
+  const uint8_t* x8 = static_cast<const uint8_t*>(xq);
+  if (isums != nullptr) return launch_qmm_dump(w8, type, N, K, x8, M, y, isums, s);
+  switch (type) {
+    case Q4_K: return launch_qmm_t<Q4_K, false>(w8, N, K, x8, M, y, nullptr, s);
+    case Q6_K: return launch_qmm_t<Q6_K, false>(w8, N, K, x8, M, y, nullptr, s);
+    case IQ4_XS: return launch_qmm_t<IQ4_XS, false>(w8, N, K, x8, M, y, nullptr, s);
+    default: return -2;
   }
-  return 0;
 }
+
 }  // namespace qdot

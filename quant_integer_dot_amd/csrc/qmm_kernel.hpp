@@ -1,0 +1,363 @@
+// qmm_kernel.hpp -- prefill matmul for M > 8 activation rows (row a6 of the hot
+// path), on the int8 matrix cores of gfx950.
+//
+// Same arithmetic as the decode kernel -- exact int32 block dots of the raw
+// weight codes with the Q8_1 activations, then exact-term fp64 scale drains
+// (Kestrel section 5: exact int32 inside the block, scales after) -- but the
+// block dots of a 32 x 32 output tile come from one MFMA per 32-element
+// block: v_mfma_i32_32x32x32_i8 for Q4_K and IQ4_XS (one MFMA = one
+// sub-block), two v_mfma_i32_32x32x16_i8 for Q6_K (16-element sub-blocks).
+// The V100 pages found dequantize + dense GEMM faster than their dp4a kernel
+// above M ~ 32-64 and their fused WMMA attempts slower than dp4a because the
+// dequantized tile went through shared memory (V100TPS, "fp16 vs Q4
+// crossover" and the fused-WMMA entry).  Here the int8 codes go straight from
+// VGPRs into the MFMA and only the per-block scales are applied on the VALU.
+//
+// MFMA lane layout (measured on gfx950): operand lane l supplies row
+// (A) / column (B) l%32 and K-slice l/32 (16 bytes for K=32, 8 for K=16); the
+// bytes of A and B lanes pair by position.  Result register r of lane l holds
+// D[8*(r/4) + 4*(l/32) + r%4][l%32].  A = activations (rows m), B = weight
+// codes (columns n), so a lane's 16 outputs share one weight row and need 16
+// activation scales, which the wave stages in LDS as fp64.
+//
+// Tiles: a workgroup has QMM_WAVES waves; wave w owns activation rows
+// m0 + 32w .. +31 and all QMM_BN weight rows of the workgroup (QMM_NT MFMA
+// tiles).  Each output is one lane's sequential sum over all of K, so its
+// value does not depend on M or on the tiling.
+#pragma once
+#include <type_traits>
+
+#include "qdot_common.hpp"
+
+namespace qdot {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int QMM_WAVES = 4;             // waves per workgroup
+constexpr int QMM_NT = 2;                // 32-row weight tiles per wave
+constexpr int QMM_BM = 32 * QMM_WAVES;   // activation rows per workgroup
+constexpr int QMM_BN = 32 * QMM_NT;      // weight rows per workgroup
+constexpr int QMM_XCDS = 8;              // MI355X: 8 XCDs, workgroups dealt round-robin
+
+struct QmmDs { double d, s; };  // one Q8_1 block's scales, fp64 (Q6_K uses d only)
+
+// Result register r of lane l -> row of the 32 x 32 tile.
+__device__ __forceinline__ int mfma_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
+
+// IQ4_NL-style codebook as four little-endian dwords, placeholder values
+// round_half_away(-127 + 240*(i/15)^1.4) (the pages do not print the table).
+constexpr uint32_t QMM_CB0 = 0x9A8F8681u, QMM_CB1 = 0xD4C4B5A7u, QMM_CB2 = 0x1C09F6E5u,
+                   QMM_CB3 = 0x715B4531u;
+__device__ __forceinline__ uint32_t qmm_cb(uint32_t idx) {
+  const uint32_t sel = idx & 0x07070707u;
+  const uint32_t lo = perm(QMM_CB1, QMM_CB0, sel);
+  const uint32_t hi = perm(QMM_CB3, QMM_CB2, sel);
+  return perm(hi, lo, ((idx >> 1) & 0x04040404u) | 0x03020100u);
+}
+
+// Q6_K: 6-bit codes (one per byte, 0..63) -> int8 code - 32.
+__device__ __forceinline__ uint32_t q6_signed(uint32_t u) {
+  const uint32_t v = u ^ 0x20202020u;        // bit 5 flipped: 6-bit two's complement
+  const uint32_t t = v & 0x20202020u;        // its sign bit, per byte
+  return v | (t << 1) | (t << 2);            // sign-extended to 8 bits
+}
+
+// -------------------------------------------------------------- per format
+// Per weight row and superblock: the scale fields.  Per weight row and
+// 32-element block: the B operand data of this lane's K-slice g.
+template <int T> struct QmmFmt;
+
+template <> struct QmmFmt<Q4_K> {
+  static constexpr int BYTES = 144;
+  struct Hdr { u32x4 h; };
+  struct Blk { u32x4 qs; };  // qs[32c + 16g .. +16], c = j/2: sub-blocks 2c (low), 2c+1 (high)
+  __device__ static Hdr hdr(const uint8_t* sb) { return Hdr{ld16(sb)}; }
+  __device__ static Blk blk(const uint8_t* sb, int j, int g) { return Blk{ld16(sb + 16 + 32 * (j >> 1) + 16 * g)}; }
+  // 6-bit scale and min of sub-block j (plain GGUF packing), as fp64 d*sc and -dmin*m.
+  template <int J> __device__ static void scales(const Hdr& x, double& w, double& mn) {
+    uint32_t sc, m;
+    if (J < 4) {
+      sc = (x.h.y >> (8 * J)) & 63u;
+      m = (x.h.z >> (8 * J)) & 63u;
+    } else {
+      sc = ((x.h.w >> (8 * (J - 4))) & 15u) | (((x.h.y >> (8 * (J - 4) + 6)) & 3u) << 4);
+      m = ((x.h.w >> (8 * (J - 4) + 4)) & 15u) | (((x.h.z >> (8 * (J - 4) + 6)) & 3u) << 4);
+    }
+    w = (double)(h2f(x.h.x) * (float)sc);
+    mn = -(double)(h2f(x.h.x >> 16) * (float)m);
+  }
+  template <int J> __device__ static v4i codes(const Blk& b, int /*g*/) {
+    const u32x4 v = b.qs;
+    const int s = (J & 1) ? 4 : 0;
+    return v4i{(int)((v.x >> s) & 0x0F0F0F0Fu), (int)((v.y >> s) & 0x0F0F0F0Fu),
+               (int)((v.z >> s) & 0x0F0F0F0Fu), (int)((v.w >> s) & 0x0F0F0F0Fu)};
+  }
+};
+
+template <> struct QmmFmt<IQ4_XS> {
+  static constexpr int BYTES = 136;
+  struct Hdr { u32x2 h; };
+  struct Blk { u32x4 qs; };  // qs[16j .. 16j+16]: low nibbles elements 0-15, high 16-31
+  __device__ static Hdr hdr(const uint8_t* sb) { return Hdr{ld8(sb)}; }
+  __device__ static Blk blk(const uint8_t* sb, int j, int /*g*/) { return Blk{ld16(sb + 8 + 16 * j)}; }
+  template <int J> __device__ static double scale(const Hdr& x) {
+    const int ls = (int)(((x.h.y >> (4 * J)) & 15u) | ((((x.h.x >> 16) >> (2 * J)) & 3u) << 4));
+    return (double)(h2f(x.h.x) * (float)(ls - 32));
+  }
+  template <int J> __device__ static v4i codes(const Blk& b, int g) {
+    const u32x4 v = b.qs;
+    const int s = g ? 4 : 0;
+    return v4i{(int)qmm_cb(v.x >> s), (int)qmm_cb(v.y >> s), (int)qmm_cb(v.z >> s),
+               (int)qmm_cb(v.w >> s)};
+  }
+};
+
+template <> struct QmmFmt<Q6_K> {
+  static constexpr int BYTES = 210;
+  struct Hdr { u32x4 sc; uint32_t d; };
+  // Block j = sub-blocks 2j (first 16 elements) and 2j+1; this lane's K-slice
+  // g covers elements 8g..8g+7 of each: ql and qh bytes for l in those ranges.
+  struct Blk { u32x2 l0, l1, h0, h1; };
+  __device__ static Hdr hdr(const uint8_t* sb) {
+    Hdr x;
+    x.sc = ld16(sb + 192);
+    unsigned short dh;
+    __builtin_memcpy(&dh, sb + 208, 2);
+    x.d = dh;
+    return x;
+  }
+  __device__ static Blk blk(const uint8_t* sb, int j, int g) {
+    const int h = j >> 2, g6 = j & 3;
+    const uint8_t* ql = sb + 64 * h + 32 * (g6 & 1) + 8 * g;
+    const uint8_t* qh = sb + 128 + 32 * h + 8 * g;
+    return Blk{ld8(ql), ld8(ql + 16), ld8(qh), ld8(qh + 16)};
+  }
+  // int8 sub-scales of sub-blocks 2j, 2j+1
+  template <int J> __device__ static void scales(const Hdr& x, int& s0, int& s1) {
+    const uint32_t w = J < 2 ? x.sc.x : (J < 4 ? x.sc.y : (J < 6 ? x.sc.z : x.sc.w));
+    s0 = (int)(int8_t)(w >> (16 * (J & 1)));
+    s1 = (int)(int8_t)(w >> (16 * (J & 1) + 8));
+  }
+  // signed codes of sub-block 2j + half (8 bytes = this lane's K-slice)
+  template <int J> __device__ static long codes(const Blk& b, int half) {
+    constexpr int g6 = J & 3;
+    const u32x2 lq = half ? b.l1 : b.l0, hq = half ? b.h1 : b.h0;
+    uint32_t c[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t low = ((g6 >= 2 ? (lq[k] >> 4) : lq[k]) & 0x0F0F0F0Fu);
+      const uint32_t high = ((hq[k] >> (2 * g6)) & 0x03030303u) << 4;
+      c[k] = q6_signed(low | high);
+    }
+    return (long)((uint64_t)c[0] | ((uint64_t)c[1] << 32));
+  }
+};
+
+// --------------------------------------------------------------- kernel
+// Operands of one 32-element block for this lane: activation codes (A) and
+// the weight codes of the QMM_NT weight tiles (B, raw; decoded at use).
+template <int T> struct QmmOps {
+  u32x4 a;                               // Q6_K: .xy = K-slice of the first 16, .zw of the second
+  typename QmmFmt<T>::Blk w[QMM_NT];
+};
+
+constexpr int QMM_RING = 4;              // operand ring: loads run QMM_RING-1 blocks ahead
+static_assert(8 % QMM_RING == 0, "ring slot of block j must not depend on the superblock");
+
+template <int T, bool DUMP>
+__global__ __launch_bounds__(64 * QMM_WAVES) void qmm_mfma_kernel(
+    const uint8_t* __restrict__ W, int N, int K, const uint8_t* __restrict__ xq, int M,
+    float* __restrict__ y, int32_t* __restrict__ isums, int m_tiles, int n_tiles) {
+  using F = QmmFmt<T>;
+  constexpr int SUB = Geom<T>::SUB;
+  // Activation scales of this wave's 32 rows for one superblock, fp64, two
+  // superblocks in flight: [wave][parity][block][row].  Each wave reads only
+  // its own slice, so a wave-level barrier orders the staging.
+  __shared__ QmmDs lds_ds[QMM_WAVES][2][8][32];
+
+  // XCD-aware tile order: workgroup id i runs on XCD i % 8; the m_tiles
+  // workgroups that share a weight tile get ids with the same residue, so
+  // they run on one XCD and read the weight tile from its L2.
+  const int id = blockIdx.x;
+  const int xcd = id % QMM_XCDS, local = id / QMM_XCDS;
+  const int m_tile = local % m_tiles;
+  const int n_tile = (local / m_tiles) * QMM_XCDS + xcd;
+  if (n_tile >= n_tiles) return;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5, c32 = lane & 31;
+  const int nsb = K / QK, nq8 = K / Q8_BLOCK;
+  const size_t row_bytes = (size_t)nsb * F::BYTES;
+  const int m0 = m_tile * QMM_BM + 32 * wave;
+  const int n0 = n_tile * QMM_BN;
+
+  // This lane's activation row (A operand and scale staging) and weight rows
+  // (B); rows past the edge are clamped to the last one and never stored.
+  const int ma = m0 + c32 < M ? m0 + c32 : M - 1;
+  const uint8_t* xrow = xq + (size_t)ma * nq8 * Q8_BYTES;
+  const uint8_t* wrow[QMM_NT];
+#pragma unroll
+  for (int t = 0; t < QMM_NT; ++t) {
+    const int n = n0 + 32 * t + c32;
+    wrow[t] = W + (size_t)(n < N ? n : N - 1) * row_bytes;
+  }
+  QmmDs(*const stage)[8][32] = lds_ds[wave];
+
+  auto load_ops = [&](int b, int j) {
+    QmmOps<T> o;
+    const uint8_t* xb = xrow + (size_t)(b * 8 + j) * Q8_BYTES + 4;
+    if constexpr (T == Q6_K) {
+      const u32x2 lo = ld8(xb + 8 * g), hi = ld8(xb + 16 + 8 * g);
+      o.a = u32x4{lo.x, lo.y, hi.x, hi.y};
+    } else {
+      o.a = ld16(xb + 16 * g);
+    }
+#pragma unroll
+    for (int t = 0; t < QMM_NT; ++t) o.w[t] = F::blk(wrow[t] + (size_t)b * F::BYTES, j, g);
+    return o;
+  };
+  auto load_hdr = [&](int b, typename F::Hdr* h) {
+#pragma unroll
+    for (int t = 0; t < QMM_NT; ++t) h[t] = F::hdr(wrow[t] + (size_t)b * F::BYTES);
+  };
+  // Scales of row c32, blocks 4g..4g+3 of superblock b (raw fp16 pairs).
+  auto load_ds = [&](int b, uint32_t* ds) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ds[u] = ld4(xrow + (size_t)(b * 8 + 4 * g + u) * Q8_BYTES);
+  };
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  double acc[QMM_NT][16];
+#pragma unroll
+  for (int t = 0; t < QMM_NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.0;
+
+  // Prologue: scales and headers of superblock 0, operands of its first
+  // QMM_RING-1 blocks.
+  uint32_t ds_next[4];
+  typename F::Hdr hd_next[QMM_NT];
+  load_ds(0, ds_next);
+  load_hdr(0, hd_next);
+  QmmOps<T> ring[QMM_RING];
+#pragma unroll
+  for (int j = 0; j < QMM_RING - 1; ++j) ring[j] = load_ops(0, j);
+
+  for (int b = 0; b < nsb; ++b) {
+    const int par = b & 1;
+    const int bn = b + 1 < nsb ? b + 1 : b;  // clamped: the last prefetch is redundant, in bounds
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      stage[par][4 * g + u][c32] = QmmDs{(double)h2f(ds_next[u] & 0xFFFFu), (double)h2f(ds_next[u] >> 16)};
+    typename F::Hdr hd[QMM_NT];
+#pragma unroll
+    for (int t = 0; t < QMM_NT; ++t) hd[t] = hd_next[t];
+    load_ds(bn, ds_next);
+    load_hdr(bn, hd_next);
+    wave_sync();
+
+    auto do_block = [&](auto JC) {
+      constexpr int J = decltype(JC)::value;
+      constexpr int JN = J + QMM_RING - 1;  // block whose operands are fetched now
+      ring[JN % QMM_RING] = JN < 8 ? load_ops(b, JN) : load_ops(bn, JN - 8);
+      const QmmOps<T>& o = ring[J % QMM_RING];
+      if constexpr (T == Q6_K) {
+        const long a0 = (long)((uint64_t)o.a.x | ((uint64_t)o.a.y << 32));
+        const long a1 = (long)((uint64_t)o.a.z | ((uint64_t)o.a.w << 32));
+        v16i I0[QMM_NT], I1[QMM_NT];
+        int s0[QMM_NT], s1[QMM_NT];
+        double d[QMM_NT];
+#pragma unroll
+        for (int t = 0; t < QMM_NT; ++t) {
+          const v16i z = {0};
+          I0[t] = __builtin_amdgcn_mfma_i32_32x32x16_i8(a0, F::template codes<J>(o.w[t], 0), z, 0, 0, 0);
+          I1[t] = __builtin_amdgcn_mfma_i32_32x32x16_i8(a1, F::template codes<J>(o.w[t], 1), z, 0, 0, 0);
+          F::template scales<J>(hd[t], s0[t], s1[t]);
+          d[t] = (double)h2f(hd[t].d);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = mfma_row(r, g);
+          const double D = stage[par][J][i].d;
+#pragma unroll
+          for (int t = 0; t < QMM_NT; ++t) {
+            const int P = s0[t] * I0[t][r] + s1[t] * I1[t][r];   // exact int
+            acc[t][r] = fma(d[t] * D, (double)P, acc[t][r]);     // exact product
+            if (DUMP) {
+              const int m = m0 + i, n = n0 + 32 * t + c32;
+              if (m < M && n < N) {
+                int32_t* p = isums + ((size_t)m * N + n) * (K / SUB) + (size_t)b * (QK / SUB) + 2 * J;
+                p[0] = I0[t][r];
+                p[1] = I1[t][r];
+              }
+            }
+          }
+        }
+      } else {
+        const v4i a = v4i{(int)o.a.x, (int)o.a.y, (int)o.a.z, (int)o.a.w};
+        v16i I[QMM_NT];
+        double w[QMM_NT], mn[QMM_NT];
+#pragma unroll
+        for (int t = 0; t < QMM_NT; ++t) {
+          const v16i z = {0};
+          I[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, F::template codes<J>(o.w[t], g), z, 0, 0, 0);
+          if constexpr (T == Q4_K) F::template scales<J>(hd[t], w[t], mn[t]);
+          else { w[t] = F::template scale<J>(hd[t]); mn[t] = 0.0; }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = mfma_row(r, g);
+          const QmmDs e = stage[par][J][i];
+#pragma unroll
+          for (int t = 0; t < QMM_NT; ++t) {
+            acc[t][r] = fma(w[t] * e.d, (double)I[t][r], acc[t][r]);  // exact product
+            if constexpr (T == Q4_K) acc[t][r] = fma(mn[t], e.s, acc[t][r]);
+            if (DUMP) {
+              const int m = m0 + i, n = n0 + 32 * t + c32;
+              if (m < M && n < N)
+                isums[((size_t)m * N + n) * (K / SUB) + (size_t)b * (QK / SUB) + J] = I[t][r];
+            }
+          }
+        }
+      }
+    };
+    do_block(std::integral_constant<int, 0>{});
+    do_block(std::integral_constant<int, 1>{});
+    do_block(std::integral_constant<int, 2>{});
+    do_block(std::integral_constant<int, 3>{});
+    do_block(std::integral_constant<int, 4>{});
+    do_block(std::integral_constant<int, 5>{});
+    do_block(std::integral_constant<int, 6>{});
+    do_block(std::integral_constant<int, 7>{});
+  }
+
+#pragma unroll
+  for (int t = 0; t < QMM_NT; ++t) {
+    const int n = n0 + 32 * t + c32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + mfma_row(r, g);
+      if (m < M && n < N) y[(size_t)m * N + n] = (float)acc[t][r];
+    }
+  }
+}
+
+template <int T, bool DUMP>
+inline int launch_qmm_t(const uint8_t* W, int N, int K, const uint8_t* xq, int M, float* y,
+                        int32_t* isums, hipStream_t s) {
+  const int m_tiles = (M + QMM_BM - 1) / QMM_BM;
+  const int n_tiles = (N + QMM_BN - 1) / QMM_BN;
+  const long groups = (long)(n_tiles + QMM_XCDS - 1) / QMM_XCDS;
+  const long grid = (long)QMM_XCDS * m_tiles * groups;
+  if (grid > 0x7FFFFFFFL) return -1;
+  hipLaunchKernelGGL((qmm_mfma_kernel<T, DUMP>), dim3((unsigned)grid), dim3(64 * QMM_WAVES), 0, s, W,
+                     N, K, xq, M, y, isums, m_tiles, n_tiles);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace qdot
