@@ -90,13 +90,16 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
-def cpu_baseline(shapes, cfg_idx, Ms, budget_s=20.0):
+def cpu_baseline(shapes, cfg_idx, Ms, budget_s=20.0, prefill=False):
     """The CPU oracle (plain scalar C, fp64, one thread) on a bounded sample:
-    the first layer's projections at each M, stopping once the budget is spent."""
+    the first layer's projections at each M, stopping once the budget is spent.
+    Decode: whole projections, rated in weight GB/s.  Prefill: 64 weight rows
+    of each projection for all M rows, rated in int8 TOP/s (2 ops per MAC)."""
     import numpy as np
     import oracle
     from quant_integer_dot_amd import synth
     done_bytes = 0
+    done_ops = 0
     t_used = 0.0
     parts = []
     for M in Ms:
@@ -107,15 +110,27 @@ def cpu_baseline(shapes, cfg_idx, Ms, budget_s=20.0):
             x = synth.activations(M, K, synth.act_seed(cfg_idx, K, M))
             t0 = time.perf_counter()
             xq = oracle.quantize_q8_1(x)
-            oracle.qmatmul(W, t, N, K, xq, M)
+            if prefill:
+                rows = np.arange(64)
+                oracle.qmatmul_rows(W, t, N, K, xq, M, rows)
+                done_ops += 2 * M * rows.size * K
+            else:
+                oracle.qmatmul(W, t, N, K, xq, M)
             t_used += time.perf_counter() - t0
             done_bytes += W.nbytes
             parts.append(f"{name}@M={M}")
+    cpu = platform.processor() or platform.machine()
+    if prefill:
+        return {"value": round(done_ops / t_used / 1e12, 6), "unit": "TOP/s", "cores": 1,
+                "kind": "oracle",
+                "sample": f"layer 0 of the same workload, weight rows 0-63 of {', '.join(parts)} "
+                          f"({done_ops / 1e9:.1f} G int8 ops, {t_used:.1f} s, single thread, "
+                          f"quantize + qmatmul per projection; CPU: {cpu})"}
     return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
             "sample": f"layer 0 of the same workload: {', '.join(parts)} "
                       f"({done_bytes / 1e6:.1f} MB of weights, {t_used:.1f} s, single thread, "
-                      f"quantize + qmatmul per projection; CPU: {platform.processor() or platform.machine()})"}
+                      f"quantize + qmatmul per projection; CPU: {cpu})"}
 
 
 def main():
@@ -136,6 +151,7 @@ def main():
     qd.load()
     dev = torch.device("cuda:0")
     cfg_idx, shapes, layers, Ms = workload_def(args.workload)
+    prefill = args.workload.endswith("prefill-512")
     if args.layers:
         layers = args.layers
     if args.ms:
@@ -172,23 +188,31 @@ def main():
     lib = qd.load()
     stream = torch.cuda.current_stream(dev)
 
+    # Projections that read the same quantized input share one quantization
+    # per layer (q/k/v, gate/up).  Everything runs in order on one stream:
+    # running the q/k/v and gate/up launches as parallel graph branches on
+    # side streams measured slower on MI355X (12.5 vs 10.3 ms per step).
     def sweep(M, only=None):
         """Launch one M's sweep on the current stream (all layers)."""
         b = bufs[M]
         s = torch.cuda.current_stream(dev).cuda_stream
+        groups = []
+        for pi, (name, N, K, t) in enumerate(shapes):
+            inp = INPUT_OF[name]
+            if not groups or groups[-1][0] != inp:
+                groups.append((inp, []))
+            groups[-1][1].append(pi)
         for layer in range(layers):
-            done_inputs = set()
-            for pi, (name, N, K, t) in enumerate(shapes):
-                inp = INPUT_OF[name]
-                if only is None and inp not in done_inputs:
+            for inp, pis in groups:
+                K = shapes[pis[0]][2]
+                if only is None or only == "quantize":
                     rc = lib.qdot_quantize_q8_1(b["x"][inp].data_ptr(), M, K, b["xq"][inp].data_ptr(), s)
                     assert rc == 0, rc
-                    done_inputs.add(inp)
-                if only == "quantize" and inp not in done_inputs:
-                    rc = lib.qdot_quantize_q8_1(b["x"][inp].data_ptr(), M, K, b["xq"][inp].data_ptr(), s)
-                    assert rc == 0, rc
-                    done_inputs.add(inp)
-                if only is None or only == name:
+                todo = [pi for pi in pis if only is None or only == shapes[pi][0]]
+                if not todo:
+                    continue
+                for pi in todo:
+                    name, N, K, t = shapes[pi]
                     rc = lib.qdot_qmatmul(Wdev[layer][pi].data_ptr(), t, N, K, b["xq"][inp].data_ptr(), M,
                                           b["y"][name].data_ptr(), s)
                     assert rc == 0, rc
@@ -228,7 +252,9 @@ def main():
         for i, M in enumerate(Ms):
             per_m_ms[M].append(marks[k][i].elapsed_time(marks[k][i + 1]))
     value = len(Ms) * wbytes_sweep / (ms_per_step * 1e-3) / 1e9
-    log(f"[bench] step {ms_per_step:.3f} ms -> {value:.1f} GB/s of weights")
+    step_ops = sum(2 * M * N * K for M in Ms for _, N, K, _ in shapes) * layers
+    log(f"[bench] step {ms_per_step:.3f} ms -> {value:.1f} GB/s of weights, "
+        f"{step_ops / (ms_per_step * 1e-3) / 1e12:.1f} int8 TOP/s")
 
     # ------------------------------------- per-projection kernel timing
     reps = args.kernel_reps or args.steps
@@ -254,11 +280,13 @@ def main():
             rows[name] = {"N": N, "K": K, "type": synth.TYPE_NAMES[t], "us": round(us, 3),
                           "weight_GBps": round(wb / us / 1e3, 1),
                           "pct_hbm_peak": round(100 * wb / us / 1e3 / HBM_PEAK_GBS, 1)}
+            rows[name]["TOPs"] = round(2 * M * N * K / us / 1e6, 2)
             kn = qd.qdot_kernel_name(t, M)
-            e = kern.setdefault(kn, [0, 0.0, 0])
+            e = kern.setdefault(kn, [0, 0.0, 0, 0])
             e[0] += alg * layers
             e[1] += us * layers * 1e-3
             e[2] += layers
+            e[3] += 2 * M * N * K * layers
         # quantizer
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -274,7 +302,7 @@ def main():
         nq = layers * len(inputs)
         qus = a.elapsed_time(bb) * 1e3 / (reps * nq)
         qbytes = sum(M * in_K[i] * 4 + qd.qdot_q8_1_bytes(M, in_K[i]) for i in inputs) * layers
-        e = kern.setdefault("quantize_q8_1", [0, 0.0, 0])
+        e = kern.setdefault("quantize_q8_1", [0, 0.0, 0, 0])
         e[0] += qbytes
         e[1] += qus * nq * 1e-3
         e[2] += nq
@@ -284,14 +312,24 @@ def main():
                          "quantize_us": round(qus, 3), "qmatmul": rows}
 
     dom = max(kern.items(), key=lambda kv: kv[1][1])
-    dname, (dbytes, dms, dn) = dom
-    achieved = dbytes / (dms * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "kernel": dname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "launches": dn, "avg_launch_us": round(dms * 1e3 / dn, 3),
-                "algorithmic_bytes_per_launch": round(dbytes / dn)}
+    dname, (dbytes, dms, dn, dops) = dom
+    if prefill:
+        # a dense int8 contraction: priced against the int8 MFMA peak
+        achieved = dops / (dms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dname, "achieved": round(achieved, 2),
+                    "peak": MFMA_I8_PEAK_TOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_I8_PEAK_TOPS, 4),
+                    "traffic": None, "launches": dn, "avg_launch_us": round(dms * 1e3 / dn, 3),
+                    "algorithmic_ops_per_launch": round(dops / dn)}
+    else:
+        achieved = dbytes / (dms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": dname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "launches": dn, "avg_launch_us": round(dms * 1e3 / dn, 3),
+                    "algorithmic_bytes_per_launch": round(dbytes / dn)}
     kernels = {k: {"launches_per_step": v[2], "ms_per_step": round(v[1], 4),
-                   "GBps": round(v[0] / (v[1] * 1e-3) / 1e9, 1)} for k, v in kern.items()}
+                   "GBps": round(v[0] / (v[1] * 1e-3) / 1e9, 1),
+                   **({"TOPs": round(v[3] / (v[1] * 1e-3) / 1e12, 2)} if v[3] else {})}
+               for k, v in kern.items()}
 
     # ------------------------------------------- sampled oracle check
     check = None
@@ -318,12 +356,18 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(shapes, cfg_idx, Ms)
+        cpu = cpu_baseline(shapes, cfg_idx, Ms, prefill=prefill)
 
+    if prefill:
+        metric, unit = "int8 TOP/s (% of MFMA int8 peak), M=512 prefill chunk, Qwen3-8B shapes", "TOP/s"
+        value = step_ops / (ms_per_step * 1e-3) / 1e12
+    else:
+        metric = METRIC if args.workload == "qwen3-8b-decode" else f"weight GB/s, {args.workload}"
+        unit = "GB/s"
     out = {
-        "metric": METRIC if args.workload == "qwen3-8b-decode" else f"weight GB/s, {args.workload}",
-        "value": round(value, 1),
-        "unit": "GB/s",
+        "metric": metric,
+        "value": round(value, 2),
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -337,7 +381,8 @@ def main():
                    "projections": [f"{n} {N}x{K} {synth.TYPE_NAMES[t]}" for n, N, K, t in shapes],
                    "weight_bytes_per_sweep": wbytes_sweep,
                    "launches_per_step": len(Ms) * layers * (len(shapes) + len(inputs))},
-        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+        **({"pct_mfma_i8_peak": round(100 * value / MFMA_I8_PEAK_TOPS, 2)} if prefill else
+           {"pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1)}),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "per_M": per_m,

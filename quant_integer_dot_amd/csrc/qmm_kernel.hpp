@@ -20,10 +20,11 @@
 // codes (columns n), so a lane's 16 outputs share one weight row and need 16
 // activation scales, which the wave stages in LDS as fp64.
 //
-// Tiles: a workgroup has QMM_WAVES waves; wave w owns activation rows
-// m0 + 32w .. +31 and all QMM_BN weight rows of the workgroup (QMM_NT MFMA
-// tiles).  Each output is one lane's sequential sum over all of K, so its
-// value does not depend on M or on the tiling.
+// Tiles: a workgroup has QMM_WAVES waves and covers 32*QMM_WAVES/KP
+// activation rows by QMM_BN weight rows (QMM_NT MFMA tiles per wave).  Wave
+// w takes the 32 rows (w / KP) and the superblocks b = w % KP (mod KP) of K;
+// the KP partial sums of an output are added in fixed order at the end.  KP
+// depends on N and K only, so an output's value does not depend on M.
 #pragma once
 #include <type_traits>
 
@@ -36,7 +37,6 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int QMM_WAVES = 4;             // waves per workgroup
 constexpr int QMM_NT = 2;                // 32-row weight tiles per wave
-constexpr int QMM_BM = 32 * QMM_WAVES;   // activation rows per workgroup
 constexpr int QMM_BN = 32 * QMM_NT;      // weight rows per workgroup
 constexpr int QMM_XCDS = 8;              // MI355X: 8 XCDs, workgroups dealt round-robin
 
@@ -165,16 +165,27 @@ template <int T> struct QmmOps {
 constexpr int QMM_RING = 4;              // operand ring: loads run QMM_RING-1 blocks ahead
 static_assert(8 % QMM_RING == 0, "ring slot of block j must not depend on the superblock");
 
-template <int T, bool DUMP>
+template <int KP> constexpr int qmm_bm() { return 32 * QMM_WAVES / KP; }  // activation rows per workgroup
+template <int KP> constexpr int qmm_lds_bytes() {
+  // scale staging, or the partial sums of the KP-1 later K slices (same memory)
+  return (QMM_WAVES * 2 * 8 * 32 * 16) > ((QMM_WAVES - QMM_WAVES / KP) * QMM_NT * 16 * 64 * 8)
+             ? (QMM_WAVES * 2 * 8 * 32 * 16)
+             : ((QMM_WAVES - QMM_WAVES / KP) * QMM_NT * 16 * 64 * 8);
+}
+
+template <int T, int KP, bool DUMP>
 __global__ __launch_bounds__(64 * QMM_WAVES) void qmm_mfma_kernel(
     const uint8_t* __restrict__ W, int N, int K, const uint8_t* __restrict__ xq, int M,
     float* __restrict__ y, int32_t* __restrict__ isums, int m_tiles, int n_tiles) {
   using F = QmmFmt<T>;
   constexpr int SUB = Geom<T>::SUB;
+  static_assert(QMM_WAVES % KP == 0, "K split must divide the waves");
   // Activation scales of this wave's 32 rows for one superblock, fp64, two
   // superblocks in flight: [wave][parity][block][row].  Each wave reads only
-  // its own slice, so a wave-level barrier orders the staging.
-  __shared__ QmmDs lds_ds[QMM_WAVES][2][8][32];
+  // its own slice, so a wave-level barrier orders the staging.  After the
+  // main loop the same memory holds the K-split partial sums.
+  __shared__ __align__(16) double lds_raw[qmm_lds_bytes<KP>() / 8];
+  QmmDs(*const lds_ds)[2][8][32] = reinterpret_cast<QmmDs(*)[2][8][32]>(lds_raw);
 
   // XCD-aware tile order: workgroup id i runs on XCD i % 8; the m_tiles
   // workgroups that share a weight tile get ids with the same residue, so
@@ -187,9 +198,10 @@ __global__ __launch_bounds__(64 * QMM_WAVES) void qmm_mfma_kernel(
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 5, c32 = lane & 31;
+  const int kp = wave % KP, wq = wave / KP;
   const int nsb = K / QK, nq8 = K / Q8_BLOCK;
   const size_t row_bytes = (size_t)nsb * F::BYTES;
-  const int m0 = m_tile * QMM_BM + 32 * wave;
+  const int m0 = m_tile * qmm_bm<KP>() + 32 * wq;
   const int n0 = n_tile * QMM_BN;
 
   // This lane's activation row (A operand and scale staging) and weight rows
@@ -238,19 +250,21 @@ __global__ __launch_bounds__(64 * QMM_WAVES) void qmm_mfma_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.0;
 
-  // Prologue: scales and headers of superblock 0, operands of its first
-  // QMM_RING-1 blocks.
+  // Prologue: scales and headers of this wave's first superblock, operands
+  // of its first QMM_RING-1 blocks (clamped in bounds when K has fewer
+  // superblocks than the split).
+  const int b0 = kp < nsb ? kp : nsb - 1;
   uint32_t ds_next[4];
   typename F::Hdr hd_next[QMM_NT];
-  load_ds(0, ds_next);
-  load_hdr(0, hd_next);
+  load_ds(b0, ds_next);
+  load_hdr(b0, hd_next);
   QmmOps<T> ring[QMM_RING];
 #pragma unroll
-  for (int j = 0; j < QMM_RING - 1; ++j) ring[j] = load_ops(0, j);
+  for (int j = 0; j < QMM_RING - 1; ++j) ring[j] = load_ops(b0, j);
 
-  for (int b = 0; b < nsb; ++b) {
-    const int par = b & 1;
-    const int bn = b + 1 < nsb ? b + 1 : b;  // clamped: the last prefetch is redundant, in bounds
+  for (int b = kp, it = 0; b < nsb; b += KP, ++it) {
+    const int par = it & 1;
+    const int bn = b + KP < nsb ? b + KP : b;  // clamped: the last prefetch is redundant, in bounds
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       stage[par][4 * g + u][c32] = QmmDs{(double)h2f(ds_next[u] & 0xFFFFu), (double)h2f(ds_next[u] >> 16)};
@@ -336,6 +350,30 @@ __global__ __launch_bounds__(64 * QMM_WAVES) void qmm_mfma_kernel(
     do_block(std::integral_constant<int, 7>{});
   }
 
+  if constexpr (KP > 1) {
+    // Partial sums of K slices 1..KP-1 go through LDS; slice 0 adds them in
+    // slice order and stores.
+    __syncthreads();  // every wave is done with its scale staging
+    double* red = lds_raw;
+    auto slot = [&](int q, int k, int t, int r) {
+      return ((((q * (KP - 1) + (k - 1)) * QMM_NT + t) * 16 + r) * 64) + lane;
+    };
+    if (kp > 0) {
+#pragma unroll
+      for (int t = 0; t < QMM_NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[slot(wq, kp, t, r)] = acc[t][r];
+    }
+    __syncthreads();
+    if (kp > 0) return;
+#pragma unroll
+    for (int k = 1; k < KP; ++k)
+#pragma unroll
+      for (int t = 0; t < QMM_NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] += red[slot(wq, k, t, r)];
+  }
+
 #pragma unroll
   for (int t = 0; t < QMM_NT; ++t) {
     const int n = n0 + 32 * t + c32;
@@ -347,17 +385,42 @@ __global__ __launch_bounds__(64 * QMM_WAVES) void qmm_mfma_kernel(
   }
 }
 
-template <int T, bool DUMP>
-inline int launch_qmm_t(const uint8_t* W, int N, int K, const uint8_t* xq, int M, float* y,
-                        int32_t* isums, hipStream_t s) {
-  const int m_tiles = (M + QMM_BM - 1) / QMM_BM;
+// K split: 1, 2 or 4 waves per output tile, from N and K only (never M), so
+// that the work of an M = 512 chunk fills the 256 CUs at two waves per SIMD.
+inline int qmm_ksplit(int N, int K) {
+#ifdef QMM_FORCE_KP
+  (void)N; (void)K;
+  return QMM_FORCE_KP;
+#else
+  const int n_tiles = (N + QMM_BN - 1) / QMM_BN;
+  const int nsb = K / QK;
+  int kp = 1;
+  while (kp < 4 && n_tiles * 16 * kp < 4096 && nsb >= 4 * kp) kp *= 2;
+  return kp;
+#endif
+}
+
+template <int T, int KP, bool DUMP>
+inline int launch_qmm_kp(const uint8_t* W, int N, int K, const uint8_t* xq, int M, float* y,
+                         int32_t* isums, hipStream_t s) {
+  const int m_tiles = (M + qmm_bm<KP>() - 1) / qmm_bm<KP>();
   const int n_tiles = (N + QMM_BN - 1) / QMM_BN;
   const long groups = (long)(n_tiles + QMM_XCDS - 1) / QMM_XCDS;
   const long grid = (long)QMM_XCDS * m_tiles * groups;
   if (grid > 0x7FFFFFFFL) return -1;
-  hipLaunchKernelGGL((qmm_mfma_kernel<T, DUMP>), dim3((unsigned)grid), dim3(64 * QMM_WAVES), 0, s, W,
-                     N, K, xq, M, y, isums, m_tiles, n_tiles);
+  hipLaunchKernelGGL((qmm_mfma_kernel<T, KP, DUMP>), dim3((unsigned)grid), dim3(64 * QMM_WAVES), 0, s,
+                     W, N, K, xq, M, y, isums, m_tiles, n_tiles);
   return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <int T, bool DUMP>
+inline int launch_qmm_t(const uint8_t* W, int N, int K, const uint8_t* xq, int M, float* y,
+                        int32_t* isums, hipStream_t s) {
+  switch (qmm_ksplit(N, K)) {
+    case 1: return launch_qmm_kp<T, 1, DUMP>(W, N, K, xq, M, y, isums, s);
+    case 2: return launch_qmm_kp<T, 2, DUMP>(W, N, K, xq, M, y, isums, s);
+    default: return launch_qmm_kp<T, 4, DUMP>(W, N, K, xq, M, y, isums, s);
+  }
 }
 
 }  // namespace qdot

@@ -13,13 +13,15 @@
 //  * exact int32 sums inside each sub-block, scales applied afterwards
 //    (Kestrel section 5).
 // What differs from the pages' V100 design: the M=8 V100 kernel was L1-bound
-// (xLLM section B2 ncu table).  Here, for small M each lane reads its two
-// activation blocks straight from L1/L2 (one cache line per quarter serves
-// the 16 rows of a wave); for larger M a workgroup stages the activations
-// once into LDS (int8 codes plus fp64 scales) and each lane reuses every
-// activation dword it reads for R weight rows.  The scale drains are exact
-// fp64 terms (every product exact, one rounding per accumulate), so y is the
-// fp32 rounding of a value within a few fp64 ulps of the exact sum.
+// (xLLM section B2 ncu table).  Here each wave of a workgroup takes every
+// P-th superblock of 16 weight rows (4 lanes per row, 64 weights per lane);
+// the activations of a superblock (8*M Q8_1 blocks) are fetched one block per
+// lane together with its weights and published to the wave's LDS slice just
+// before use, so the 16 rows of the wave read them as LDS broadcasts instead
+// of pulling them through the vector memory path once per row.  The scale
+// drains are exact fp64 terms (every product exact, one rounding per
+// accumulate), so y is the fp32 rounding of a value within a few fp64 ulps
+// of the exact sum.
 
 #include "qdot_common.hpp"
 
@@ -117,16 +119,11 @@ __device__ __forceinline__ uint32_t cb_lookup(uint32_t idx, uint32_t t0, uint32_
 
 // ---------------------------------------------------------------- kernels
 //
-// One lane handles quarter q of superblock b for R weight rows (slot s, rows
-// n0 + s + 16*r).  The P waves of a workgroup split the superblocks of each
-// row: wave w takes b = w, w+P, ...  P is a function of K only, and every
-// kernel below walks a lane's superblocks, halves and rows in the same order
-// with the same fp64 operations, so each output is computed by the same
-// sequence of roundings whatever M is (row m of y does not depend on M).
-//
-// The workgroup stages the activations of a K-chunk once into LDS (int8
-// codes and fp64 scales); each lane reads the activation dwords of its
-// current block from LDS and reuses them for its R weight rows.
+// One lane handles quarter q of superblock b for one weight row (slot s, row
+// n0 + s).  The P waves of a workgroup split the superblocks of each row:
+// wave w takes b = w, w+P, ...  P is a function of K only, and the kernel
+// walks a lane's superblocks and halves in the same order with the same fp64
+// operations for every M, so row m of y does not depend on M.
 
 // Per-row, per-half-quarter weight data: the 8 code dwords (32 int8 codes in
 // activation order) and what the drain needs.
@@ -283,109 +280,106 @@ __device__ __forceinline__ void reduce_store(double (&acc)[R][M], double* lds_re
 // ------------------------------------------------------ the decode kernel
 constexpr int QMV_MGROUP = 4;  // activation rows held in registers at once
 
-template <int T, int M, int R, int DEPTH, bool DUMP>
-__global__ __launch_bounds__(QMV_MAX_THREADS) void qmv_lds_kernel(
+// Each wave stages the activations of its own superblocks: for superblock b
+// the 8*M Q8_1 blocks (M rows x 8 blocks) are loaded one per lane, together
+// with the weights of b, and written to the wave's LDS slice just before b
+// is computed.  A load's data is waited for only when its superblock comes
+// up, so no wait covers weights fetched for later superblocks, and no
+// workgroup barrier sits in the main loop.
+template <int T, int M, int DEPTH, bool DUMP>
+__global__ __launch_bounds__(QMV_MAX_THREADS) void qmv_kernel(
     const uint8_t* __restrict__ W, int N, int K, const uint8_t* __restrict__ xq,
-    float* __restrict__ y, int32_t* __restrict__ isums, int kc) {
+    float* __restrict__ y, int32_t* __restrict__ isums) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int BYTES = Geom<T>::BYTES;
+  constexpr int ITEMS = 8 * M;  // Q8_1 blocks per superblock and activation rows
+  static_assert(ITEMS <= 64, "one activation block per lane");
   const int P = blockDim.x >> 6;
   const int nsb = K / QK;
-  const size_t row_bytes = (size_t)nsb * BYTES;
   const int nq8 = K / Q8_BLOCK;
-  const int kc_sb = kc / QK;  // superblocks per chunk (a multiple of P)
-  uint8_t* lds_x = smem;                                                  // int8 [M][kc]
-  DsEntry* lds_ds = reinterpret_cast<DsEntry*>(smem + (size_t)M * kc);  // [M][kc/32]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, slot = lane >> 2, q = lane & 3;
-  const int n0 = blockIdx.x * (QMV_SLOTS * R);
+  const int n0 = blockIdx.x * QMV_SLOTS;
 
-  const uint8_t* wrow[R];
-  int nrow[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    nrow[r] = n0 + slot + QMV_SLOTS * r;
-    const int nc = nrow[r] < N ? nrow[r] : N - 1;
-    wrow[r] = W + (size_t)nc * row_bytes;
-  }
-  double acc[R][M];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int m = 0; m < M; ++m) acc[r][m] = 0.0;
+  // this wave's LDS slice: codes [M][8][32 B], then scales [M][8]
+  uint8_t* lds_x = smem + (size_t)wave * ITEMS * (Q8_BLOCK + sizeof(DsEntry));
+  DsEntry* lds_ds = reinterpret_cast<DsEntry*>(lds_x + ITEMS * Q8_BLOCK);
 
-  // DEPTH weight stages in flight (a ring of register sets).  The prefetch
-  // loads are unconditional (superblock clamped to the row) so the compiler
+  const int nrow = n0 + slot;
+  const uint8_t* wrow = W + (size_t)(nrow < N ? nrow : N - 1) * nsb * BYTES;
+  // activation block of this lane: item = m*8 + j (lanes past 8*M repeat one)
+  const int item = lane % ITEMS;
+  const uint8_t* xsrc = xq + ((size_t)(item >> 3) * nq8 + (item & 7)) * Q8_BYTES;
+
+  double acc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc[m] = 0.0;
+
+  struct Stage {
+    typename Fmt<T>::Regs w;
+    uint32_t ds;
+    u32x4 c0, c1;
+  };
+  Stage S[DEPTH];
+  // Unconditional loads (superblock clamped to the row): the compiler then
   // waits for exactly the stage a compute step uses.
-  typename Fmt<T>::Regs S[DEPTH][R];
-  auto prefetch = [&](typename Fmt<T>::Regs (&X)[R], int bsb) {
+  auto fetch = [&](Stage& st, int bsb) {
     const int bc = bsb < nsb ? bsb : nsb - 1;
-#pragma unroll
-    for (int r = 0; r < R; ++r) X[r] = Fmt<T>::load(wrow[r] + (size_t)bc * BYTES, q);
+    st.w = Fmt<T>::load(wrow + (size_t)bc * BYTES, q);
+    const uint8_t* src = xsrc + (size_t)bc * 8 * Q8_BYTES;
+    st.ds = ld4(src);
+    st.c0 = ld16(src + 4);
+    st.c1 = ld16(src + 20);
   };
-  // Stage activations [c0, c0 + kc) into LDS: int8 codes and fp64 scales.
-  auto stage = [&](int chunk) {
-    const int c0 = chunk * kc;
-    const int kcc = (K - c0) < kc ? (K - c0) : kc;
-    const int nblk = kcc / Q8_BLOCK;
-    for (int it = tid; it < M * nblk; it += blockDim.x) {
-      const int m = it / nblk, kb = it - m * nblk;
-      const uint8_t* src = xq + ((size_t)m * nq8 + c0 / Q8_BLOCK + kb) * Q8_BYTES;
-      const uint32_t ds = ld4(src);
-      const u32x4 q0 = ld16(src + 4), q1 = ld16(src + 20);
-      *reinterpret_cast<u32x4*>(lds_x + (size_t)m * kc + Q8_BLOCK * kb) = q0;
-      *reinterpret_cast<u32x4*>(lds_x + (size_t)m * kc + Q8_BLOCK * kb + 16) = q1;
-      lds_ds[(size_t)m * (kc / Q8_BLOCK) + kb] = ds_entry(T, ds, q0, q1);
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  auto compute = [&](const Stage& st, int b) {
+    wave_sync();  // the previous superblock's LDS reads are done
+    if (lane < ITEMS) {
+      *reinterpret_cast<u32x4*>(lds_x + item * Q8_BLOCK) = st.c0;
+      *reinterpret_cast<u32x4*>(lds_x + item * Q8_BLOCK + 16) = st.c1;
+      lds_ds[item] = ds_entry(T, st.ds, st.c0, st.c1);
     }
-  };
-  auto compute = [&](const typename Fmt<T>::Regs (&rg)[R], int b, int bl) {
+    wave_sync();
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int kb = bl * (QK / Q8_BLOCK) + Fmt<T>::blk(q, half);  // chunk-local Q8 block
-      Sub<T> sw[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) decode_sub<T>(rg[r], q, half, sw[r]);
+      const int kb = Fmt<T>::blk(q, half);  // Q8_1 block within the superblock
+      Sub<T> sw;
+      decode_sub<T>(st.w, q, half, sw);
 #pragma unroll
       for (int m0 = 0; m0 < M; m0 += QMV_MGROUP) {
-        const int mg = (M - m0) < QMV_MGROUP ? (M - m0) : QMV_MGROUP;
-        uint32_t xa[QMV_MGROUP][8];
-        DsEntry de[QMV_MGROUP];
+        constexpr int G = QMV_MGROUP;
+        uint32_t xa[G][8];
+        DsEntry de[G];
 #pragma unroll
-        for (int mm = 0; mm < QMV_MGROUP; ++mm) {
-          if (mm < mg) {
-            const int m = m0 + mm;
-            const u32x4 v0 = *reinterpret_cast<const u32x4*>(lds_x + (size_t)m * kc + Q8_BLOCK * kb);
-            const u32x4 v1 = *reinterpret_cast<const u32x4*>(lds_x + (size_t)m * kc + Q8_BLOCK * kb + 16);
+        for (int mm = 0; mm < G; ++mm) {
+          if (m0 + mm < M) {
+            const int it = (m0 + mm) * 8 + kb;
+            const u32x4 v0 = *reinterpret_cast<const u32x4*>(lds_x + it * Q8_BLOCK);
+            const u32x4 v1 = *reinterpret_cast<const u32x4*>(lds_x + it * Q8_BLOCK + 16);
             xa[mm][0] = v0.x; xa[mm][1] = v0.y; xa[mm][2] = v0.z; xa[mm][3] = v0.w;
             xa[mm][4] = v1.x; xa[mm][5] = v1.y; xa[mm][6] = v1.z; xa[mm][7] = v1.w;
-            de[mm] = lds_ds[(size_t)m * (kc / Q8_BLOCK) + kb];
+            de[mm] = lds_ds[it];
           }
         }
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-          for (int mm = 0; mm < QMV_MGROUP; ++mm)
-            if (mm < mg)
-              dot_drain<T, DUMP>(sw[r], xa[mm], de[mm], acc[r][m0 + mm],
-                                 isum_ptr<T, M, R, DUMP>(isums, N, K, m0 + mm, nrow[r], b, q, half));
+        for (int mm = 0; mm < G; ++mm)
+          if (m0 + mm < M)
+            dot_drain<T, DUMP>(sw, xa[mm], de[mm], acc[m0 + mm],
+                               isum_ptr<T, M, 1, DUMP>(isums, N, K, m0 + mm, nrow, b, q, half));
       }
     }
   };
 
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) prefetch(S[d], wave + d * P);
-  stage(0);
-  __syncthreads();
-  const int ipc = kc_sb / P;  // iterations per chunk (a multiple of DEPTH)
+  for (int d = 0; d < DEPTH; ++d) fetch(S[d], wave + d * P);
   const int niter = (((nsb + P - 1) / P) + DEPTH - 1) / DEPTH * DEPTH;
-  auto step = [&](typename Fmt<T>::Regs (&X)[R], int ii, bool refill) {
-    if (ii > 0 && ii % ipc == 0) {  // next chunk (only when K does not fit one chunk)
-      __syncthreads();
-      stage(ii / ipc);
-      __syncthreads();
-    }
+  auto step = [&](Stage& st, int ii, bool refill) {
     const int b = wave + ii * P;
-    if (b < nsb) compute(X, b, b - (ii / ipc) * kc_sb);
-    if (refill) prefetch(X, b + DEPTH * P);
+    if (b < nsb) compute(st, b);
+    if (refill) fetch(st, b + DEPTH * P);
   };
   // The last DEPTH iterations are peeled so that no prefetch runs past the
   // row (a redundant load would still have to land before the wave retires).
@@ -396,20 +390,14 @@ __global__ __launch_bounds__(QMV_MAX_THREADS) void qmv_lds_kernel(
   }
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) step(S[d], i + d, false);
-  reduce_store<M, R>(acc, reinterpret_cast<double*>(smem), P, wave, slot, q, tid, n0, N, y);
+
+  double acc2[1][M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) acc2[0][m] = acc[m];
+  reduce_store<M, 1>(acc2, reinterpret_cast<double*>(smem), P, wave, slot, q, tid, n0, N, y);
 }
 
 // ------------------------------------------------------------- launcher
-constexpr int QMV_LDS_BUDGET = 64 * 1024;
-// Tuning constants, chosen by measurement on MI355X (Qwen3-8B shapes, M = 1..8):
-// one weight row per lane beat two at every M (more workgroups matter more
-// than reusing each LDS activation read twice), and two prefetch stages beat
-// four.  Lanes reading their activations straight from L1/L2 instead of LDS
-// was slower at M = 1 and 2 (each lane pulls more activation than weight
-// bytes through the vector memory return path).
-constexpr int QMV_ROWS = 1;   // weight rows per lane (R)
-constexpr int QMV_DEPTH = 2;  // weight prefetch stages in flight
-
 // Waves per workgroup: a function of K only (the K split fixes the fp64
 // summation order, which must not depend on M): about four superblocks per
 // wave, at most eight waves.
@@ -418,34 +406,49 @@ static int qmv_waves(int nsb) {
   return p < 1 ? 1 : (p > 8 ? 8 : p);
 }
 
-template <int T, int M, int R, int DEPTH, bool DUMP>
-static int launch_lds(const uint8_t* W, int N, int K, const uint8_t* xq, float* y, int32_t* isums,
-                      hipStream_t s) {
+// Superblocks in flight per wave (prefetch depth; it changes no arithmetic).
+// Chosen by measurement on MI355X (Qwen3-8B shapes, M = 1..8): the weight
+// bytes one stage of all waves puts in flight decide it.  About 7 MB per
+// stage (12288 x 4096 Q4_K, 4096 x 12288 Q6_K) already saturates HBM with one
+// stage at M <= 4; the 9 MB matrices want all four superblocks of a wave in
+// flight; Q6_K's larger register stage is kept to two.
+static int qmv_depth(int type, int M, int N, int K) {
+  const int nsb = K / QK;
+  const long waves = (long)((N + QMV_SLOTS - 1) / QMV_SLOTS) * qmv_waves(nsb);
+  const long stage_bytes = waves * QMV_SLOTS * (long)(type == Q6_K ? 210 : (type == Q4_K ? 144 : 136));
+  int d;
+  if (stage_bytes >= (4L << 20)) d = M <= 4 ? 1 : 2;
+  else if (stage_bytes >= (3L << 20)) d = 2;
+  else d = 4;
+  if (type == Q6_K && d > 2) d = 2;
+  return d;
+}
+
+template <int T, int M, int DEPTH, bool DUMP>
+static int launch_qmv_k(const uint8_t* W, int N, int K, const uint8_t* xq, float* y, int32_t* isums,
+                        hipStream_t s) {
   const int nsb = K / QK;
   const int P = qmv_waves(nsb);
-  const int per_k = M + M * (int)sizeof(DsEntry) / Q8_BLOCK;  // LDS bytes per activation column
-  // chunk = multiple of P*DEPTH superblocks that fits the budget (the last
-  // chunk may be short), so every wave changes chunk at the same iteration
-  const int unit = P * DEPTH;
-  int kc_sb = (QMV_LDS_BUDGET / per_k) / QK / unit * unit;
-  if (kc_sb < unit) return -1;
-  if (kc_sb >= nsb) kc_sb = ((nsb + unit - 1) / unit) * unit;
-  const int kc = kc_sb * QK;
-  const size_t stage = (size_t)M * kc + (size_t)M * (kc / Q8_BLOCK) * sizeof(DsEntry);
-  const size_t red = (size_t)P * QMV_SLOTS * R * M * sizeof(double);
+  const size_t stage = (size_t)P * 8 * M * (Q8_BLOCK + sizeof(DsEntry));
+  const size_t red = (size_t)P * QMV_SLOTS * M * sizeof(double);
   const size_t lds = stage > red ? stage : red;
-  if (lds > (size_t)QMV_LDS_BUDGET) return -1;
-  const int rows_per_wg = QMV_SLOTS * R;
-  const int grid = (N + rows_per_wg - 1) / rows_per_wg;
-  hipLaunchKernelGGL((qmv_lds_kernel<T, M, R, DEPTH, DUMP>), dim3(grid), dim3(64 * P), lds, s, W, N,
-                     K, xq, y, isums, kc);
+  const int grid = (N + QMV_SLOTS - 1) / QMV_SLOTS;
+  hipLaunchKernelGGL((qmv_kernel<T, M, DEPTH, DUMP>), dim3(grid), dim3(64 * P), lds, s, W, N, K, xq,
+                     y, isums);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 template <int T, int M, bool DUMP>
 static int launch_qmv_r(const uint8_t* W, int N, int K, const uint8_t* xq, float* y,
                         int32_t* isums, hipStream_t s) {
-  return launch_lds<T, M, QMV_ROWS, QMV_DEPTH, DUMP>(W, N, K, xq, y, isums, s);
+  if constexpr (DUMP) return launch_qmv_k<T, M, 2, true>(W, N, K, xq, y, isums, s);
+  switch (qmv_depth(T, M, N, K)) {
+    case 1: return launch_qmv_k<T, M, 1, false>(W, N, K, xq, y, isums, s);
+    case 2: return launch_qmv_k<T, M, 2, false>(W, N, K, xq, y, isums, s);
+    default:
+      if constexpr (T == Q6_K) return launch_qmv_k<T, M, 2, false>(W, N, K, xq, y, isums, s);
+      else return launch_qmv_k<T, M, 4, false>(W, N, K, xq, y, isums, s);
+  }
 }
 
 template <int T, bool DUMP>
