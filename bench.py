@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--no-check", action="store_true", help="skip the sampled oracle check")
     p.add_argument("--kernel-reps", type=int, default=None,
                    help="replays of each per-projection graph (default: steps)")
+    p.add_argument("--eager-only", action="store_true",
+                   help="run the sweep eagerly --steps times per M and exit (for counter passes)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="run only a plain device copy of this size (PMC calibration) and exit")
     return p.parse_args()
@@ -221,6 +223,18 @@ def main():
     for M in Ms:
         sweep(M)
     torch.cuda.synchronize()
+    if args.eager_only:
+        # Plain stream launches, no graphs: what hardware-counter passes profile.
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            for M in Ms:
+                sweep(M)
+        torch.cuda.synchronize()
+        print(json.dumps({"eager_only": True, "workload": args.workload, "M": Ms, "layers": layers,
+                          "steps": args.steps,
+                          "wall_ms_per_step": round((time.perf_counter() - t0) * 1e3 / args.steps, 3)}),
+              flush=True)
+        return
 
     # ------------------------------------------------------- step graphs
     graphs = {}

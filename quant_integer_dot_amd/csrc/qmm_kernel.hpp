@@ -162,8 +162,8 @@ template <int T> struct QmmOps {
   typename QmmFmt<T>::Blk w[QMM_NT];
 };
 
-constexpr int QMM_RING = 4;              // operand ring: loads run QMM_RING-1 blocks ahead
-static_assert(8 % QMM_RING == 0, "ring slot of block j must not depend on the superblock");
+template <int T> constexpr int qmm_ring() { return T == Q6_K ? 2 : 4; }  // operand ring: loads run ring-1 blocks ahead
+
 
 template <int KP> constexpr int qmm_bm() { return 32 * QMM_WAVES / KP; }  // activation rows per workgroup
 template <int KP> constexpr int qmm_lds_bytes() {
@@ -179,6 +179,8 @@ __global__ __launch_bounds__(64 * QMM_WAVES) void qmm_mfma_kernel(
     float* __restrict__ y, int32_t* __restrict__ isums, int m_tiles, int n_tiles) {
   using F = QmmFmt<T>;
   constexpr int SUB = Geom<T>::SUB;
+  constexpr int QMM_RING = qmm_ring<T>();
+  static_assert(8 % QMM_RING == 0, "ring slot of block j must not depend on the superblock");
   static_assert(QMM_WAVES % KP == 0, "K split must divide the waves");
   // Activation scales of this wave's 32 rows for one superblock, fp64, two
   // superblocks in flight: [wave][parity][block][row].  Each wave reads only
@@ -366,7 +368,7 @@ __global__ __launch_bounds__(64 * QMM_WAVES) void qmm_mfma_kernel(
     }
     __syncthreads();
     if (kp > 0) return;
-#pragma unroll
+#pragma unroll 1
     for (int k = 1; k < KP; ++k)
 #pragma unroll
       for (int t = 0; t < QMM_NT; ++t)
@@ -386,7 +388,10 @@ __global__ __launch_bounds__(64 * QMM_WAVES) void qmm_mfma_kernel(
 }
 
 // K split: 1, 2 or 4 waves per output tile, from N and K only (never M), so
-// that the work of an M = 512 chunk fills the 256 CUs at two waves per SIMD.
+// that an output's value does not depend on M.  Measured on MI355X at M = 512
+// (Qwen3-8B and hidden-5120 shapes, occupancy two waves per SIMD): two slices
+// beat one and four for N > 2048; four slices win for N <= 2048, where the
+// grid is otherwise too small to fill 256 CUs.
 inline int qmm_ksplit(int N, int K) {
 #ifdef QMM_FORCE_KP
   (void)N; (void)K;
@@ -394,8 +399,8 @@ inline int qmm_ksplit(int N, int K) {
 #else
   const int n_tiles = (N + QMM_BN - 1) / QMM_BN;
   const int nsb = K / QK;
-  int kp = 1;
-  while (kp < 4 && n_tiles * 16 * kp < 4096 && nsb >= 4 * kp) kp *= 2;
+  int kp = n_tiles <= 32 ? 4 : 2;
+  while (kp > nsb) kp >>= 1;
   return kp;
 #endif
 }
