@@ -79,6 +79,37 @@ INPUT_OF = {"q": "attn", "k": "attn", "v": "attn", "qkv": "attn", "o": "o",
             "gate": "ffn", "up": "ffn", "down": "down", "w": "attn"}
 
 
+def kernel_source_digest(files):
+    """First 16 hex digits of sha256 over the named csrc/ files (in order)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "quant_integer_dot_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch from a committed counter summary (profiles/hbm_traffic_*.md),
+    or None when there is none for this kernel and workload or when the kernel's
+    sources have changed since the counters were taken."""
+    import glob
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "hbm_traffic_*.md"))):
+        kv = {}
+        with open(path) as fh:
+            for line in fh:
+                if ": " in line and not line.startswith(("|", "#", " ")):
+                    k, v = line.rstrip("\n").split(": ", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel") != kernel or kv.get("workload") != workload:
+            continue
+        files = kv.get("source_files", "").split()
+        if not files or kernel_source_digest(files) != kv.get("source_digest"):
+            return None
+        return int(kv["traffic_bytes_per_launch"])
+    return None
+
+
 def copy_calibration(mib):
     import torch
     n = mib * 1024 * 1024
@@ -332,12 +363,14 @@ def main():
         achieved = dops / (dms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "kernel": dname, "achieved": round(achieved, 2),
                     "peak": MFMA_I8_PEAK_TOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_I8_PEAK_TOPS, 4),
-                    "traffic": None, "launches": dn, "avg_launch_us": round(dms * 1e3 / dn, 3),
+                    "traffic": recorded_traffic(dname, args.workload), "launches": dn,
+                    "avg_launch_us": round(dms * 1e3 / dn, 3),
                     "algorithmic_ops_per_launch": round(dops / dn)}
     else:
         achieved = dbytes / (dms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "kernel": dname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": recorded_traffic(dname, args.workload),
                     "launches": dn, "avg_launch_us": round(dms * 1e3 / dn, 3),
                     "algorithmic_bytes_per_launch": round(dbytes / dn)}
     kernels = {k: {"launches_per_step": v[2], "ms_per_step": round(v[1], 4),

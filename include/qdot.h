@@ -44,8 +44,9 @@
  * launched and a negative status is returned:
  *   QDOT_E_ARG   null pointer, M < 1, N < 1, K < 256 or K % 256 != 0 (K % 32
  *                != 0 for the quantizer), unknown type, or a size overflow;
- *   QDOT_E_ALIGN W not 16-byte aligned, or x, x_q8, y, isums not 4-byte
- *                aligned;
+ *   QDOT_E_ALIGN x, x_q8, y or isums not 4-byte aligned (W may sit at any
+ *                byte address: the kernels read it with unaligned vector
+ *                loads, as Q6_K superblocks of 210 bytes require);
  *   QDOT_E_HIP   the launch failed (hipGetLastError after the launch).
  * There is no fallback path and no environment variable.  Inputs must be
  * finite and each Q8_1 block's fp16 d and s finite; otherwise results are
