@@ -100,7 +100,8 @@ int qdot_quantize_q8_1(const float *x, int64_t M, int64_t K, void *x_q8,
  * where I is the exact integer dot of the sub-block's weight codes with the
  * int8 activations and D, S are the activation block's fp16 d and s.  Every
  * scale product is exact and accumulated in fp64; y is rounded once to fp32.
- * M <= 8 runs the decode kernel (v_dot4_i32_i8, M-row register tile); M > 8
+ * M <= 8 runs the decode kernel (v_dot4_i32_i8, M-row tile); 8 < M <= 32 runs
+ * it over chunks of 8 rows (each row bitwise equal to an M <= 8 call); M > 32
  * runs the MFMA i8 prefill kernel.  K % 256 == 0 is required. */
 int qdot_qmatmul(const void *W, int type, int64_t N, int64_t K,
                  const void *x_q8, int64_t M, float *y, void *stream);
@@ -115,8 +116,9 @@ int qdot_qmatmul_dump_isums(const void *W, int type, int64_t N, int64_t K,
 /* Static text for a status code. */
 const char *qdot_status_str(int status);
 
-/* Name of the kernel qdot_qmatmul runs for (type, M), e.g. "qmv_dot4<Q4_K,8>"
- * or "qmm_mfma<Q6_K>"; "invalid" for bad arguments.  Static text. */
+/* Name of the kernel qdot_qmatmul runs for (type, M), e.g. "qmv_dot4<Q4_K,8>",
+ * "qmv_dot4<Q4_K,8-row chunks>" or "qmm_mfma<Q6_K>"; "invalid" for bad
+ * arguments.  Static text. */
 const char *qdot_kernel_name(int type, int64_t M);
 
 /* Build identifier of the library (compile date and time).  Static text. */

@@ -36,6 +36,19 @@ int check_dims(int type, int64_t N, int64_t K, int64_t M) {
   return QDOT_OK;
 }
 
+// Mid-batch dispatch: up to this many activation rows the decode kernel runs
+// over chunks of at most 8 rows (each chunk reads the weights again, but the
+// integer-dot kernel's fixed cost is far below the MFMA kernel's at small M);
+// above it the MFMA kernel takes all rows at once.  Measured on MI355X, the
+// chunks win up to M = 14..80 depending on the shape (about 28 for the
+// 12288 x 4096 and 7168 x 5120 matrices, 56 for 4096 x 4096, 80 for
+// 4096 x 12288 Q6_K, 14 for 17408 x 5120 IQ4_XS); 32 is the compromise.
+// Rows computed through the chunks are bitwise the rows a call with M <= 8
+// returns.
+#ifndef QDOT_QMV_CHUNK_MAX_M
+#define QDOT_QMV_CHUNK_MAX_M 32
+#endif
+
 int run_qmatmul(const void* W, int type, int64_t N, int64_t K, const void* x_q8, int64_t M,
                 float* y, int32_t* isums, void* stream, bool dump) {
   int st = check_dims(type, N, K, M);
@@ -43,11 +56,18 @@ int run_qmatmul(const void* W, int type, int64_t N, int64_t K, const void* x_q8,
   if (!W || !x_q8 || !y || (dump && !isums)) return QDOT_E_ARG;
   if (!aligned4(x_q8) || !aligned4(y) || (dump && !aligned4(isums))) return QDOT_E_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  int rc;
-  if (M <= 8)
-    rc = qdot::launch_qmv(W, type, (int)N, (int)K, x_q8, (int)M, y, dump ? isums : nullptr, s);
-  else
+  int rc = 0;
+  if (M <= QDOT_QMV_CHUNK_MAX_M) {
+    const size_t xq_row = (size_t)(K / 32) * 36;
+    const size_t is_row = (size_t)N * (size_t)(K / sub_len(type));
+    for (int64_t m0 = 0; m0 < M && rc == 0; m0 += 8) {
+      const int mc = (int)(M - m0 < 8 ? M - m0 : 8);
+      rc = qdot::launch_qmv(W, type, (int)N, (int)K, static_cast<const uint8_t*>(x_q8) + m0 * xq_row, mc,
+                            y + m0 * N, dump ? isums + m0 * is_row : nullptr, s);
+    }
+  } else {
     rc = qdot::launch_qmm(W, type, (int)N, (int)K, x_q8, (int)M, y, dump ? isums : nullptr, s);
+  }
   return rc == 0 ? QDOT_OK : QDOT_E_HIP;
 }
 
@@ -116,9 +136,12 @@ const char* qdot_kernel_name(int type, int64_t M) {
        "qmv_dot4<Q6_K,5>", "qmv_dot4<Q6_K,6>", "qmv_dot4<Q6_K,7>", "qmv_dot4<Q6_K,8>"},
       {"qmv_dot4<IQ4_XS,1>", "qmv_dot4<IQ4_XS,2>", "qmv_dot4<IQ4_XS,3>", "qmv_dot4<IQ4_XS,4>",
        "qmv_dot4<IQ4_XS,5>", "qmv_dot4<IQ4_XS,6>", "qmv_dot4<IQ4_XS,7>", "qmv_dot4<IQ4_XS,8>"}};
+  static const char* const mid[3] = {"qmv_dot4<Q4_K,8-row chunks>", "qmv_dot4<Q6_K,8-row chunks>",
+                                     "qmv_dot4<IQ4_XS,8-row chunks>"};
   static const char* const pre[3] = {"qmm_mfma<Q4_K>", "qmm_mfma<Q6_K>", "qmm_mfma<IQ4_XS>"};
   if (type < QDOT_Q4_K || type > QDOT_IQ4_XS || M < 1 || M > kMaxDim) return "invalid";
-  return M <= 8 ? dec[type - 1][M - 1] : pre[type - 1];
+  if (M <= 8) return dec[type - 1][M - 1];
+  return M <= QDOT_QMV_CHUNK_MAX_M ? mid[type - 1] : pre[type - 1];
 }
 
 const char* qdot_build_id(void) { return "libqdot gfx950 " __DATE__ " " __TIME__; }

@@ -151,6 +151,26 @@ def test_qmatmul_m_above_8(wtype, M):
     assert_close(y, y64, f"{TN[wtype]} M={M}")
 
 
+# ------------------------------------------------- mid-batch (8 < M <= 32)
+@pytest.mark.parametrize("wtype", TYPES)
+def test_mid_batch_chunks_equal_decode_rows(wtype):
+    """M = 9..32 runs the decode kernel over 8-row chunks: every row is bitwise
+    the row an M <= 8 call returns, sums stay exact, outputs within 1e-5."""
+    N, K, M = 300, 2048, 27
+    W = synth.weights(wtype, N, K, (2026, 72, wtype))
+    Wd = to_dev(W)
+    x = synth.activations(M, K, (2026, 72, K, M, 7))
+    xqd, xq = quantize(x)
+    y, isums = qmatmul(Wd, wtype, N, K, xqd, M, dump=True)
+    assert np.array_equal(isums, oracle.isums(W, wtype, N, K, xq, M))
+    y64, _, _ = oracle.qmatmul(W, wtype, N, K, xq, M)
+    assert_close(y, y64, f"{TN[wtype]} M={M}")
+    row = K // 32 * 36
+    for m0, mc in ((0, 1), (5, 3), (19, 8), (26, 1)):
+        ys, _ = qmatmul(Wd, wtype, N, K, xqd[m0 * row:(m0 + mc) * row], mc)
+        assert np.array_equal(ys.view(np.uint32), y[m0:m0 + mc].view(np.uint32)), (m0, mc)
+
+
 # --------------------------------------------------- prefill (MFMA path)
 @pytest.mark.parametrize("wtype", TYPES)
 @pytest.mark.parametrize("M,N,K", [(512, 200, 768), (130, 64, 256), (97, 333, 1280)])
