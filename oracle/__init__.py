@@ -13,9 +13,9 @@ import os
 
 import numpy as np
 
-Q4_K, Q6_K, IQ4_XS = 1, 2, 3
-BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, IQ4_XS: 136}
-SUBLEN = {Q4_K: 32, Q6_K: 16, IQ4_XS: 32}
+Q4_K, Q6_K, IQ4_XS, Q4_0, Q8_0 = 1, 2, 3, 4, 5
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, IQ4_XS: 136, Q4_0: 144, Q8_0: 272}   # per 256 weights
+SUBLEN = {Q4_K: 32, Q6_K: 16, IQ4_XS: 32, Q4_0: 32, Q8_0: 32}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")

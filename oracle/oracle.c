@@ -1,6 +1,7 @@
 /*
  * oracle.c -- plain, slow, obviously-correct CPU oracle for the block-quantized
- * integer-dot matmul (Q8_1 activations x Q4_K / Q6_K / IQ4_XS weights -> fp32).
+ * integer-dot matmul (Q8_1 activations x Q4_K / Q6_K / IQ4_XS / Q4_0 / Q8_0
+ * weights -> fp32).
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  The product path (the
@@ -40,8 +41,11 @@
 #define OR_Q4_K 1
 #define OR_Q6_K 2
 #define OR_IQ4_XS 3
+#define OR_Q4_0 4
+#define OR_Q8_0 5
 
-#define OR_QK 256        /* weights per superblock, all three formats   */
+#define OR_QK 256        /* weights per superblock (Q4_0 / Q8_0: a group of
+                            eight consecutive 32-weight blocks)            */
 #define OR_Q8_BLOCK 32   /* activations per Q8_1 block                   */
 #define OR_Q8_BYTES 36   /* fp16 d, fp16 s, 32 x int8                    */
 
@@ -173,6 +177,8 @@ typedef struct {
   double dmin;       /* Q4_K only, else 0                               */
   int sc[16];        /* integer sub-block scale multiplier              */
   int mn[16];        /* Q4_K integer sub-block min multiplier, else 0   */
+  double dj[16];     /* scale of sub-block j's code sum: d*sc_j (exact) */
+  double mj[16];     /* Q4_K min of sub-block j: dmin*m_j (exact), else 0 */
 } oracle_sb;
 
 static int block_bytes(int type) {
@@ -180,6 +186,8 @@ static int block_bytes(int type) {
     case OR_Q4_K: return 144;
     case OR_Q6_K: return 210;
     case OR_IQ4_XS: return 136;
+    case OR_Q4_0: return 8 * 18;
+    case OR_Q8_0: return 8 * 34;
     default: return 0;
   }
 }
@@ -276,11 +284,67 @@ static void decode_iq4_xs(const uint8_t *p, oracle_sb *s) {
   }
 }
 
+/* Q4_0 blocks (18 B per 32 weights), eight per 256-weight group.  The V100TPS
+ * log (2026-08-12 entries) states the layout this oracle follows: a Q4_0 block
+ * holds four 32-bit words of nibbles, low nibbles are elements 0-15 and high
+ * nibbles elements 16-31, one scale d per block, value q - 8.  Reading for the
+ * byte order (plain GGUF): bytes 0-1 d (binary16), 2-17 qs[16]; byte qs[i]
+ * holds element i (low nibble) and element 16 + i (high nibble).
+ *   Weight: w = d * (q - 8). */
+static void decode_q4_0(const uint8_t *p, oracle_sb *s) {
+  s->sublen = 32;
+  s->nsub = 8;
+  s->d = 1.0;
+  s->dmin = 0.0;
+  for (int j = 0; j < 8; ++j) {
+    const uint8_t *blk = p + 18 * j;
+    s->sc[j] = 1;
+    s->mn[j] = 0;
+    s->dj[j] = oracle_half_to_double(rd16(blk));
+    s->mj[j] = 0.0;
+    for (int i = 0; i < 16; ++i) {
+      s->code[32 * j + i] = (blk[2 + i] & 15) - 8;
+      s->code[32 * j + 16 + i] = (blk[2 + i] >> 4) - 8;
+    }
+  }
+}
+
+/* Q8_0 blocks (34 B per 32 weights), eight per 256-weight group.  The pages
+ * name the 34-byte Q8_0 block (xLLM log, Phase B3/B4) without its layout;
+ * reading (plain GGUF): bytes 0-1 d (binary16), 2-33 qs[32] (int8), element i
+ * = qs[i].
+ *   Weight: w = d * q. */
+static void decode_q8_0(const uint8_t *p, oracle_sb *s) {
+  s->sublen = 32;
+  s->nsub = 8;
+  s->d = 1.0;
+  s->dmin = 0.0;
+  for (int j = 0; j < 8; ++j) {
+    const uint8_t *blk = p + 34 * j;
+    s->sc[j] = 1;
+    s->mn[j] = 0;
+    s->dj[j] = oracle_half_to_double(rd16(blk));
+    s->mj[j] = 0.0;
+    for (int i = 0; i < 32; ++i) s->code[32 * j + i] = (int8_t)blk[2 + i];
+  }
+}
+
+/* For the superblock formats the per-sub-block multipliers are d*sc_j and
+ * dmin*m_j (each exact in fp64: 11 + 8 significant bits). */
+static void fill_multipliers(oracle_sb *s) {
+  for (int j = 0; j < s->nsub; ++j) {
+    s->dj[j] = s->d * (double)s->sc[j];
+    s->mj[j] = s->dmin * (double)s->mn[j];
+  }
+}
+
 static int decode_sb(int type, const uint8_t *p, oracle_sb *s) {
   switch (type) {
-    case OR_Q4_K: decode_q4_k(p, s); return 0;
-    case OR_Q6_K: decode_q6_k(p, s); return 0;
-    case OR_IQ4_XS: decode_iq4_xs(p, s); return 0;
+    case OR_Q4_K: decode_q4_k(p, s); fill_multipliers(s); return 0;
+    case OR_Q6_K: decode_q6_k(p, s); fill_multipliers(s); return 0;
+    case OR_IQ4_XS: decode_iq4_xs(p, s); fill_multipliers(s); return 0;
+    case OR_Q4_0: decode_q4_0(p, s); return 0;
+    case OR_Q8_0: decode_q8_0(p, s); return 0;
     default: return -1;
   }
 }
@@ -302,15 +366,14 @@ int oracle_dequant(const uint8_t *W, int type, int64_t N, int64_t K, double *w) 
       decode_sb(type, W + (n * nsb + b) * bb, &s);
       for (int e = 0; e < OR_QK; ++e) {
         int j = e / s.sublen;
-        w[n * K + b * OR_QK + e] =
-            s.d * (double)s.sc[j] * (double)s.code[e] - s.dmin * (double)s.mn[j];
+        w[n * K + b * OR_QK + e] = s.dj[j] * (double)s.code[e] - s.mj[j];
       }
     }
   return 0;
 }
 
 /* Integer sub-block sums I[m][n][k/S] = sum over the sub-block of
- * code_w * q_x (S = 32 for Q4_K and IQ4_XS, 16 for Q6_K).  These are the
+ * code_w * q_x (S = 16 for Q6_K, 32 for every other format).  These are the
  * exact int32 block dots of the Kestrel page, section 5. */
 int oracle_isums(const uint8_t *W, int type, int64_t N, int64_t K,
                  const uint8_t *xq, int64_t M, int64_t *isums) {
@@ -366,11 +429,11 @@ int oracle_qmatmul(const uint8_t *W, int type, int64_t N, int64_t K,
           for (int i = 0; i < s.sublen; ++i)
             I += (int64_t)s.code[j * s.sublen + i] *
                  (int8_t)blk[4 + (k0 + i) % OR_Q8_BLOCK];
-          double term = ((s.d * (double)s.sc[j]) * D) * (double)I; /* exact */
+          double term = (s.dj[j] * D) * (double)I; /* exact */
           acc += term;
           aabs += fabs(term);
           if (s.mn[j] != 0) {
-            double mterm = (s.dmin * (double)s.mn[j]) * S; /* exact */
+            double mterm = s.mj[j] * S; /* exact */
             acc -= mterm;
             aabs += fabs(mterm);
           }

@@ -13,15 +13,18 @@ weights are not available, so seeded inputs of the same shapes stand in):
             clipped to [-128, 127]; d ~ |N(0, 1e-3)| as binary16.
   * IQ4_XS: index, scales_h and scales_l bytes uniform random (indices 0..15,
             6-bit scales 0..63); d ~ |N(0, 1e-3)| as binary16.
+  * Q4_0 / Q8_0: per 32-weight block, quant bytes uniform random (nibbles
+            0..15, int8 codes -128..127) and d ~ |N(0, 1e-3)| as binary16;
+            eight blocks make up each 256-weight group.
   * activations: fp32 N(0, 1).
 Seeds: numpy SeedSequence([2026, config, layer, projection]) for weights and
 SeedSequence([2026, config, K, M, 7]) for activations.
 """
 import numpy as np
 
-Q4_K, Q6_K, IQ4_XS = 1, 2, 3
-TYPE_NAMES = {Q4_K: "Q4_K", Q6_K: "Q6_K", IQ4_XS: "IQ4_XS"}
-BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, IQ4_XS: 136}
+Q4_K, Q6_K, IQ4_XS, Q4_0, Q8_0 = 1, 2, 3, 4, 5
+TYPE_NAMES = {Q4_K: "Q4_K", Q6_K: "Q6_K", IQ4_XS: "IQ4_XS", Q4_0: "Q4_0", Q8_0: "Q8_0"}
+BLOCK_BYTES = {Q4_K: 144, Q6_K: 210, IQ4_XS: 136, Q4_0: 144, Q8_0: 272}   # per 256 weights
 
 # (name, N, K, type) per projection; N = output rows, K = input width.
 QWEN25_1P5B = [
@@ -80,6 +83,11 @@ def weights(wtype, N, K, seed):
         raw[:, :, 208:210] = _half_bytes(d).reshape(N, nb, 2)
     elif wtype == IQ4_XS:
         raw[:, :, 0:2] = _half_bytes(d).reshape(N, nb, 2)
+    elif wtype in (Q4_0, Q8_0):
+        bb = B // 8
+        dj = np.abs(rng.standard_normal((N, nb, 8)) * 1e-3)
+        blk = raw.reshape(N, nb, 8, bb)
+        blk[:, :, :, 0:2] = _half_bytes(dj).reshape(N, nb, 8, 2)
     else:
         raise ValueError(f"unknown weight type {wtype}")
     return raw.reshape(N, nb * B)

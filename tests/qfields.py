@@ -10,7 +10,7 @@ from fractions import Fraction
 
 import numpy as np
 
-Q4_K, Q6_K, IQ4_XS = 1, 2, 3
+Q4_K, Q6_K, IQ4_XS, Q4_0, Q8_0 = 1, 2, 3, 4, 5
 
 
 def placeholder_codebook():
@@ -111,9 +111,39 @@ def iq4_xs_fields(rng):
                 idx=[int(v) for v in rng.integers(0, 16, 256)])
 
 
+# ------------------------------------------------------ Q4_0 / Q8_0 (x 8)
+# The fields of a 256-weight group: eight blocks of 32, each its own d.
+def encode_q4_0(d, q):
+    """d: 8 fp16 bits; q: 256 raw nibbles in 0..15 (value = d_j * (q - 8))."""
+    b = bytearray()
+    for j in range(8):
+        b += d[j].to_bytes(2, "little")
+        b += bytes(q[32 * j + i] | (q[32 * j + 16 + i] << 4) for i in range(16))
+    return bytes(b)
+
+
+def encode_q8_0(d, q):
+    """d: 8 fp16 bits; q: 256 ints in -128..127 (value = d_j * q)."""
+    b = bytearray()
+    for j in range(8):
+        b += d[j].to_bytes(2, "little") + bytes(v & 255 for v in q[32 * j:32 * j + 32])
+    return bytes(b)
+
+
+def q4_0_fields(rng):
+    return dict(d=[random_f16_bits(rng) for _ in range(8)],
+                q=[int(v) for v in rng.integers(0, 16, 256)])
+
+
+def q8_0_fields(rng):
+    return dict(d=[random_f16_bits(rng) for _ in range(8)],
+                q=[int(v) for v in rng.integers(-128, 128, 256)])
+
+
 # --------------------------------------------------------- generic helpers
 def random_fields(wtype, rng):
-    return {Q4_K: q4_k_fields, Q6_K: q6_k_fields, IQ4_XS: iq4_xs_fields}[wtype](rng)
+    return {Q4_K: q4_k_fields, Q6_K: q6_k_fields, IQ4_XS: iq4_xs_fields,
+            Q4_0: q4_0_fields, Q8_0: q8_0_fields}[wtype](rng)
 
 
 def encode(wtype, f):
@@ -121,6 +151,10 @@ def encode(wtype, f):
         return encode_q4_k(f["d"], f["dmin"], f["sc"], f["mn"], f["q"])
     if wtype == Q6_K:
         return encode_q6_k(f["d"], f["sc"], f["code"])
+    if wtype == Q4_0:
+        return encode_q4_0(f["d"], f["q"])
+    if wtype == Q8_0:
+        return encode_q8_0(f["d"], f["q"])
     return encode_iq4_xs(f["d"], f["ls"], f["idx"])
 
 
@@ -136,6 +170,10 @@ def codes_and_scales(wtype, f):
     if wtype == Q6_K:
         d = f16_frac(f["d"])
         return list(f["code"]), [(d * f["sc"][t], Fraction(0)) for t in range(16)]
+    if wtype == Q4_0:
+        return [v - 8 for v in f["q"]], [(f16_frac(f["d"][j]), Fraction(0)) for j in range(8)]
+    if wtype == Q8_0:
+        return list(f["q"]), [(f16_frac(f["d"][j]), Fraction(0)) for j in range(8)]
     cb = placeholder_codebook()
     d = f16_frac(f["d"])
     return [cb[i] for i in f["idx"]], [(d * (f["ls"][j] - 32), Fraction(0)) for j in range(8)]

@@ -24,7 +24,7 @@ import qfields as qf
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-TYPES = [qf.Q4_K, qf.Q6_K, qf.IQ4_XS]
+TYPES = [qf.Q4_K, qf.Q6_K, qf.IQ4_XS, qf.Q4_0, qf.Q8_0]
 
 
 # ------------------------------------------------------------- binary16
@@ -153,6 +153,10 @@ def test_decoder_single_bit_positions(oracle_lib, wtype):
         base["code"] = [-32] * 256
         base["sc"] = [int(v) or 1 for v in base["sc"]]
         key, val = "code", 21
+    elif wtype in (qf.Q4_0, qf.Q8_0):
+        base["d"] = [v or 0x3C00 for v in base["d"]]
+        base["q"] = [0] * 256
+        key, val = "q", 9 if wtype == qf.Q4_0 else 77
     else:
         base["idx"] = [0] * 256
         base["ls"] = [v if v != 32 else 33 for v in base["ls"]]
@@ -268,6 +272,21 @@ def test_special_cases(oracle_lib):
     wf[0][0]["sc"] = [0] * 16
     W = np.frombuffer(qf.encode(qf.Q6_K, wf[0][0]), np.uint8)
     assert not oracle_lib.qmatmul(W, qf.Q6_K, 1, 256, X, 1)[0].any()
+    # Q4_0 nibbles all 8 (value q - 8 = 0) and Q8_0 codes all 0 give exactly 0
+    for wtype, zero in ((qf.Q4_0, 8), (qf.Q8_0, 0)):
+        wf, xf, W, X = _build(wtype, rng, 1, 256, 1)
+        wf[0][0]["q"] = [zero] * 256
+        W = np.frombuffer(qf.encode(wtype, wf[0][0]), np.uint8)
+        assert not oracle_lib.qmatmul(W, wtype, 1, 256, X, 1)[0].any()
+    # Q4_0 nibbles all 0 and 15: codes -8 and +7 times each block's d
+    wf, xf, W, X = _build(qf.Q4_0, rng, 1, 256, 1)
+    for nib, code in ((0, -8), (15, 7)):
+        wf[0][0]["q"] = [nib] * 256
+        W = np.frombuffer(qf.encode(qf.Q4_0, wf[0][0]), np.uint8)
+        y64 = oracle_lib.qmatmul(W, qf.Q4_0, 1, 256, X, 1)[0][0, 0]
+        exp = sum(qf.f16_frac(wf[0][0]["d"][j]) * code * qf.f16_frac(xf[0][j][0]) * sum(xf[0][j][2])
+                  for j in range(8))
+        assert abs(Fraction(float(y64)) - exp) <= abs(exp) * Fraction(1, 2 ** 48) + Fraction(1, 2 ** 200)
 
 
 def test_rows_subset_matches_full(oracle_lib):
