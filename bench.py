@@ -46,7 +46,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="qwen3-8b-decode",
                    choices=["qwen3-8b-decode", "qwen3-8b-prefill-512", "iq4xs-h5120-decode",
-                            "qwen2.5-1.5b-decode"])
+                            "qwen2.5-1.5b-decode", "qwen3-8b-q4_0-q8_0-decode"])
     p.add_argument("--ms", default=None, help="comma-separated M values (default per workload)")
     p.add_argument("--layers", type=int, default=None, help="override the layer count")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -70,6 +70,8 @@ def workload_def(name):
         return 3, synth.IQ4XS_H5120, 64, [1, 2, 4, 8]
     if name == "qwen2.5-1.5b-decode":
         return 1, synth.QWEN25_1P5B, 28, [1, 2, 4, 8]
+    if name == "qwen3-8b-q4_0-q8_0-decode":
+        return 5, synth.QWEN3_8B_Q40_Q80, 36, [1, 2, 4, 8]
     raise ValueError(name)
 
 

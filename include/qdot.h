@@ -3,7 +3,8 @@
  * (gfx950).  Library: libqdot.so.
  *
  * The operation.  Decode in GGUF-quantized LLM inference multiplies raw
- * block-quantized weights (Q4_K, Q6_K, IQ4_XS superblocks of 256 weights)
+ * block-quantized weights (Q4_K, Q6_K, IQ4_XS superblocks of 256 weights;
+ * Q4_0 and Q8_0 blocks of 32, taken eight at a time)
  * against activations quantized to Q8_1 blocks of 32, using integer dot
  * products on the raw quantized values, and only then produces fp32; the
  * weights are never dequantized to fp32 (xLLM v0.7 dev log,
@@ -28,6 +29,12 @@
  *         locked to Q4_0"); w = d*(ls-32)*codebook[idx].  The 16-entry
  *         codebook is a placeholder (the pages do not print kvalues_iq4nl):
  *         round_half_away(-127 + 240*(i/15)^1.4), i = 0..15.
+ *   Q4_0   18 B per 32 weights: fp16 d, 16 B of 4-bit codes, low nibbles =
+ *         elements 0-15, high nibbles = 16-31 (V100TPS log, same entry);
+ *         w = d*(q-8).  Eight blocks (144 B) form one 256-weight group.
+ *   Q8_0   34 B per 32 weights: fp16 d, int8 q[32] (the xLLM page's 34-byte
+ *         block, Phase B3/B4); w = d*q.  Eight blocks (272 B) form one
+ *         256-weight group; blocks sit at 2-byte alignment.
  *
  * Layouts.  Every buffer is contiguous and row-major: x is fp32 [M][K];
  * x_q8 is [M][K/32] Q8_1 blocks; W is [N][K/256] superblocks (GGUF row
@@ -62,12 +69,14 @@
 extern "C" {
 #endif
 
-typedef enum { QDOT_Q4_K = 1, QDOT_Q6_K = 2, QDOT_IQ4_XS = 3 } qdot_type;
+typedef enum {
+  QDOT_Q4_K = 1, QDOT_Q6_K = 2, QDOT_IQ4_XS = 3, QDOT_Q4_0 = 4, QDOT_Q8_0 = 5
+} qdot_type;
 
 enum { QDOT_OK = 0, QDOT_E_ARG = -1, QDOT_E_ALIGN = -2, QDOT_E_HIP = -3 };
 
-/* Bytes per 256-weight superblock: 144 (Q4_K), 210 (Q6_K), 136 (IQ4_XS);
- * 0 for an unknown type. */
+/* Bytes per 256 weights: 144 (Q4_K), 210 (Q6_K), 136 (IQ4_XS), 144 (Q4_0,
+ * eight blocks), 272 (Q8_0, eight blocks); 0 for an unknown type. */
 size_t qdot_block_bytes(int type);
 
 /* Bytes of an N x K weight matrix: N * (K/256) * qdot_block_bytes(type);
@@ -78,7 +87,7 @@ size_t qdot_weight_bytes(int type, int64_t N, int64_t K);
 size_t qdot_q8_1_bytes(int64_t M, int64_t K);
 
 /* Number of int32 sub-block sums written by qdot_qmatmul_dump_isums:
- * M * N * (K/S), S = 32 (Q4_K, IQ4_XS) or 16 (Q6_K); 0 if invalid. */
+ * M * N * (K/S), S = 16 (Q6_K) or 32 (every other type); 0 if invalid. */
 size_t qdot_isum_count(int type, int64_t N, int64_t K, int64_t M);
 
 /* Quantize fp32 activations x [M][K] (device) to Q8_1 blocks x_q8 (device,
@@ -97,6 +106,7 @@ int qdot_quantize_q8_1(const float *x, int64_t M, int64_t K, void *x_q8,
  *   Q4_K   d*sc*D*I - dmin*m*S
  *   Q6_K   d*sc*D*I            (sub-blocks of 16)
  *   IQ4_XS d*(ls-32)*D*I
+ *   Q4_0, Q8_0  d*D*I  (d the block's own scale; Q4_0 codes are q-8)
  * where I is the exact integer dot of the sub-block's weight codes with the
  * int8 activations and D, S are the activation block's fp16 d and s.  Every
  * scale product is exact and accumulated in fp64; y is rounded once to fp32.

@@ -9,7 +9,7 @@ missing, every call raises.
 import ctypes
 import os
 
-QDOT_Q4_K, QDOT_Q6_K, QDOT_IQ4_XS = 1, 2, 3
+QDOT_Q4_K, QDOT_Q6_K, QDOT_IQ4_XS, QDOT_Q4_0, QDOT_Q8_0 = 1, 2, 3, 4, 5
 QDOT_OK, QDOT_E_ARG, QDOT_E_ALIGN, QDOT_E_HIP = 0, -1, -2, -3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

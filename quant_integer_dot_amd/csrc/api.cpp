@@ -31,7 +31,7 @@ int check_dims(int type, int64_t N, int64_t K, int64_t M) {
   if (N < 1 || M < 1 || K < 256 || K % 256 != 0) return QDOT_E_ARG;
   if (N > kMaxDim || K > kMaxDim || M > kMaxDim) return QDOT_E_ARG;
   // products that index memory must fit in 63 bits
-  if ((double)N * (double)(K / 256) * 210.0 > 9.0e18) return QDOT_E_ARG;
+  if ((double)N * (double)(K / 256) * (double)qdot_block_bytes(type) > 9.0e18) return QDOT_E_ARG;
   if ((double)M * (double)N * (double)(K / 16) > 9.0e18) return QDOT_E_ARG;
   return QDOT_OK;
 }
@@ -80,6 +80,8 @@ size_t qdot_block_bytes(int type) {
     case QDOT_Q4_K: return 144;
     case QDOT_Q6_K: return 210;
     case QDOT_IQ4_XS: return 136;
+    case QDOT_Q4_0: return 8 * 18;
+    case QDOT_Q8_0: return 8 * 34;
     default: return 0;
   }
 }
@@ -129,17 +131,23 @@ const char* qdot_status_str(int status) {
 }
 
 const char* qdot_kernel_name(int type, int64_t M) {
-  static const char* const dec[3][8] = {
+  static const char* const dec[5][8] = {
       {"qmv_dot4<Q4_K,1>", "qmv_dot4<Q4_K,2>", "qmv_dot4<Q4_K,3>", "qmv_dot4<Q4_K,4>",
        "qmv_dot4<Q4_K,5>", "qmv_dot4<Q4_K,6>", "qmv_dot4<Q4_K,7>", "qmv_dot4<Q4_K,8>"},
       {"qmv_dot4<Q6_K,1>", "qmv_dot4<Q6_K,2>", "qmv_dot4<Q6_K,3>", "qmv_dot4<Q6_K,4>",
        "qmv_dot4<Q6_K,5>", "qmv_dot4<Q6_K,6>", "qmv_dot4<Q6_K,7>", "qmv_dot4<Q6_K,8>"},
       {"qmv_dot4<IQ4_XS,1>", "qmv_dot4<IQ4_XS,2>", "qmv_dot4<IQ4_XS,3>", "qmv_dot4<IQ4_XS,4>",
-       "qmv_dot4<IQ4_XS,5>", "qmv_dot4<IQ4_XS,6>", "qmv_dot4<IQ4_XS,7>", "qmv_dot4<IQ4_XS,8>"}};
-  static const char* const mid[3] = {"qmv_dot4<Q4_K,8-row chunks>", "qmv_dot4<Q6_K,8-row chunks>",
-                                     "qmv_dot4<IQ4_XS,8-row chunks>"};
-  static const char* const pre[3] = {"qmm_mfma<Q4_K>", "qmm_mfma<Q6_K>", "qmm_mfma<IQ4_XS>"};
-  if (type < QDOT_Q4_K || type > QDOT_IQ4_XS || M < 1 || M > kMaxDim) return "invalid";
+       "qmv_dot4<IQ4_XS,5>", "qmv_dot4<IQ4_XS,6>", "qmv_dot4<IQ4_XS,7>", "qmv_dot4<IQ4_XS,8>"},
+      {"qmv_dot4<Q4_0,1>", "qmv_dot4<Q4_0,2>", "qmv_dot4<Q4_0,3>", "qmv_dot4<Q4_0,4>",
+       "qmv_dot4<Q4_0,5>", "qmv_dot4<Q4_0,6>", "qmv_dot4<Q4_0,7>", "qmv_dot4<Q4_0,8>"},
+      {"qmv_dot4<Q8_0,1>", "qmv_dot4<Q8_0,2>", "qmv_dot4<Q8_0,3>", "qmv_dot4<Q8_0,4>",
+       "qmv_dot4<Q8_0,5>", "qmv_dot4<Q8_0,6>", "qmv_dot4<Q8_0,7>", "qmv_dot4<Q8_0,8>"}};
+  static const char* const mid[5] = {"qmv_dot4<Q4_K,8-row chunks>", "qmv_dot4<Q6_K,8-row chunks>",
+                                     "qmv_dot4<IQ4_XS,8-row chunks>", "qmv_dot4<Q4_0,8-row chunks>",
+                                     "qmv_dot4<Q8_0,8-row chunks>"};
+  static const char* const pre[5] = {"qmm_mfma<Q4_K>", "qmm_mfma<Q6_K>", "qmm_mfma<IQ4_XS>",
+                                     "qmm_mfma<Q4_0>", "qmm_mfma<Q8_0>"};
+  if (type < QDOT_Q4_K || type > QDOT_Q8_0 || M < 1 || M > kMaxDim) return "invalid";
   if (M <= 8) return dec[type - 1][M - 1];
   return M <= QDOT_QMV_CHUNK_MAX_M ? mid[type - 1] : pre[type - 1];
 }

@@ -15,12 +15,15 @@ constexpr int Q8_BLOCK = 32;     // activations per Q8_1 block
 constexpr int Q8_BYTES = 36;     // fp16 d, fp16 s, int8 q[32]
 constexpr int QUARTER = 64;      // weights handled by one lane per superblock
 
-enum Type : int { Q4_K = 1, Q6_K = 2, IQ4_XS = 3 };
+enum Type : int { Q4_K = 1, Q6_K = 2, IQ4_XS = 3, Q4_0 = 4, Q8_0 = 5 };
 
 template <int T> struct Geom;
 template <> struct Geom<Q4_K>   { static constexpr int BYTES = 144; static constexpr int SUB = 32; };
 template <> struct Geom<Q6_K>   { static constexpr int BYTES = 210; static constexpr int SUB = 16; };
 template <> struct Geom<IQ4_XS> { static constexpr int BYTES = 136; static constexpr int SUB = 32; };
+// Q4_0 / Q8_0: eight consecutive 32-weight blocks stand in for a superblock.
+template <> struct Geom<Q4_0>   { static constexpr int BYTES = 8 * 18; static constexpr int SUB = 32; };
+template <> struct Geom<Q8_0>   { static constexpr int BYTES = 8 * 34; static constexpr int SUB = 32; };
 static_assert(Geom<Q4_K>::BYTES == 4 + 12 + QK / 2, "Q4_K superblock size");
 static_assert(Geom<Q6_K>::BYTES == QK / 2 + QK / 4 + QK / 16 + 2, "Q6_K superblock size");
 static_assert(Geom<IQ4_XS>::BYTES == 2 + 2 + 4 + QK / 2, "IQ4_XS superblock size");
@@ -55,6 +58,12 @@ __device__ __forceinline__ float h2f(uint32_t bits16) {
 // Integer dot of four int8 pairs, accumulated (v_dot4_i32_i8).
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
   return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+// Bytes 2..5 of the 8-byte pair {hi:lo} (v_alignbyte_b32): the dword that
+// starts 2 bytes into lo, for 2-byte-aligned block fields.
+__device__ __forceinline__ uint32_t shr16(uint32_t hi, uint32_t lo) {
+  return __builtin_amdgcn_alignbyte(hi, lo, 2);
 }
 
 // Byte permute: byte k of the result is byte sel[k] of {hi:lo} (v_perm_b32).

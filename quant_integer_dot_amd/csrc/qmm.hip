@@ -17,6 +17,8 @@ int launch_qmm(const void* W, int type, int N, int K, const void* xq, int M, flo
     case Q4_K: return launch_qmm_t<Q4_K, false>(w8, N, K, x8, M, y, nullptr, s);
     case Q6_K: return launch_qmm_t<Q6_K, false>(w8, N, K, x8, M, y, nullptr, s);
     case IQ4_XS: return launch_qmm_t<IQ4_XS, false>(w8, N, K, x8, M, y, nullptr, s);
+    case Q4_0: return launch_qmm_t<Q4_0, false>(w8, N, K, x8, M, y, nullptr, s);
+    case Q8_0: return launch_qmm_t<Q8_0, false>(w8, N, K, x8, M, y, nullptr, s);
     default: return -2;
   }
 }

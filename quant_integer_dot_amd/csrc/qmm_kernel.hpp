@@ -101,7 +101,7 @@ template <> struct QmmFmt<IQ4_XS> {
   struct Blk { u32x4 qs; };  // qs[16j .. 16j+16]: low nibbles elements 0-15, high 16-31
   __device__ static Hdr hdr(const uint8_t* sb) { return Hdr{ld8(sb)}; }
   __device__ static Blk blk(const uint8_t* sb, int j, int /*g*/) { return Blk{ld16(sb + 8 + 16 * j)}; }
-  template <int J> __device__ static double scale(const Hdr& x) {
+  template <int J> __device__ static double scale(const Hdr& x, const Blk&) {
     const int ls = (int)(((x.h.y >> (4 * J)) & 15u) | ((((x.h.x >> 16) >> (2 * J)) & 3u) << 4));
     return (double)(h2f(x.h.x) * (float)(ls - 32));
   }
@@ -110,6 +110,45 @@ template <> struct QmmFmt<IQ4_XS> {
     const int s = g ? 4 : 0;
     return v4i{(int)qmm_cb(v.x >> s), (int)qmm_cb(v.y >> s), (int)qmm_cb(v.z >> s),
                (int)qmm_cb(v.w >> s)};
+  }
+};
+
+// Q4_0 / Q8_0: no superblock header; each 32-weight block carries its own
+// fp16 d, loaded with the block's codes.
+template <> struct QmmFmt<Q4_0> {
+  static constexpr int BYTES = 8 * 18;
+  struct Hdr {};
+  struct Blk { u32x4 qs; uint32_t d; };  // qs[0..15] of block j; K-slice g = low / high nibbles
+  __device__ static Hdr hdr(const uint8_t*) { return Hdr{}; }
+  __device__ static Blk blk(const uint8_t* sb, int j, int /*g*/) {
+    unsigned short dh;
+    __builtin_memcpy(&dh, sb + 18 * j, 2);
+    return Blk{ld16(sb + 18 * j + 2), dh};
+  }
+  template <int J> __device__ static double scale(const Hdr&, const Blk& b) { return (double)h2f(b.d); }
+  // nibble q (0..15) -> int8 q - 8, four bytes at once without borrows
+  template <int J> __device__ static v4i codes(const Blk& b, int g) {
+    const int s = g ? 4 : 0;
+    auto c = [&](uint32_t v) {
+      return (int)((((v >> s) & 0x0F0F0F0Fu) | 0x80808080u) - 0x08080808u) ^ (int)0x80808080u;
+    };
+    return v4i{c(b.qs.x), c(b.qs.y), c(b.qs.z), c(b.qs.w)};
+  }
+};
+
+template <> struct QmmFmt<Q8_0> {
+  static constexpr int BYTES = 8 * 34;
+  struct Hdr {};
+  struct Blk { u32x4 qs; uint32_t d; };  // int8 codes 16g .. 16g+15 of block j
+  __device__ static Hdr hdr(const uint8_t*) { return Hdr{}; }
+  __device__ static Blk blk(const uint8_t* sb, int j, int g) {
+    unsigned short dh;
+    __builtin_memcpy(&dh, sb + 34 * j, 2);
+    return Blk{ld16(sb + 34 * j + 2 + 16 * g), dh};
+  }
+  template <int J> __device__ static double scale(const Hdr&, const Blk& b) { return (double)h2f(b.d); }
+  template <int J> __device__ static v4i codes(const Blk& b, int /*g*/) {
+    return v4i{(int)b.qs.x, (int)b.qs.y, (int)b.qs.z, (int)b.qs.w};
   }
 };
 
@@ -323,7 +362,7 @@ __global__ __launch_bounds__(64 * QMM_WAVES) void qmm_mfma_kernel(
           const v16i z = {0};
           I[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, F::template codes<J>(o.w[t], g), z, 0, 0, 0);
           if constexpr (T == Q4_K) F::template scales<J>(hd[t], w[t], mn[t]);
-          else { w[t] = F::template scale<J>(hd[t]); mn[t] = 0.0; }
+          else { w[t] = F::template scale<J>(hd[t], o.w[t]); mn[t] = 0.0; }
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {

@@ -96,6 +96,36 @@ template <> struct Fmt<IQ4_XS> {
   __device__ static int blk(int q, int half) { return 2 * q + half; }
 };
 
+// Q4_0: eight 18-byte blocks {fp16 d, qs[16]} per 256-weight group; quarter
+// q = blocks 2q and 2q+1 = bytes 36q .. 36q+35 (2-byte aligned fields).
+template <> struct Fmt<Q4_0> {
+  struct Regs { u32x4 a, b; uint32_t c; };
+  __device__ static Regs load(const uint8_t* sb, int q) {
+    Regs r;
+    r.a = ld16(sb + 36 * q);
+    r.b = ld16(sb + 36 * q + 16);
+    r.c = ld4(sb + 36 * q + 32);
+    return r;
+  }
+  __device__ static int blk(int q, int half) { return 2 * q + half; }
+};
+
+// Q8_0: eight 34-byte blocks {fp16 d, int8 qs[32]} per group; quarter q =
+// blocks 2q and 2q+1 = bytes 68q .. 68q+67.
+template <> struct Fmt<Q8_0> {
+  struct Regs { u32x4 a, b, c, e; uint32_t f; };
+  __device__ static Regs load(const uint8_t* sb, int q) {
+    Regs r;
+    r.a = ld16(sb + 68 * q);
+    r.b = ld16(sb + 68 * q + 16);
+    r.c = ld16(sb + 68 * q + 32);
+    r.e = ld16(sb + 68 * q + 48);
+    r.f = ld4(sb + 68 * q + 64);
+    return r;
+  }
+  __device__ static int blk(int q, int half) { return 2 * q + half; }
+};
+
 // IQ4_NL-style codebook as four little-endian dwords (entries 0-3, 4-7, 8-11,
 // 12-15).  Placeholder values (the pages name kvalues_iq4nl without printing
 // it): round_half_away(-127 + 240*(i/15)^1.4).
@@ -131,6 +161,8 @@ template <int T> struct Sub;
 template <> struct Sub<Q4_K> { uint32_t cw[8]; double wsc, wmn; };
 template <> struct Sub<IQ4_XS> { uint32_t cw[8]; double wsc; };
 template <> struct Sub<Q6_K> { uint32_t cw[8]; int s0, s1; double d; };
+template <> struct Sub<Q4_0> { uint32_t cw[8]; double wsc; };
+template <> struct Sub<Q8_0> { uint32_t cw[8]; double wsc; };
 
 template <int T>
 __device__ __forceinline__ void decode_sub(const typename Fmt<T>::Regs& g, int q, int half,
@@ -162,6 +194,37 @@ __device__ __forceinline__ void decode_sub(const typename Fmt<T>::Regs& g, int q
       o.cw[i] = cb_lookup(pk[i], CB0, CB1, CB2, CB3);           // elements 4i..4i+3
       o.cw[i + 4] = cb_lookup(pk[i] >> 4, CB0, CB1, CB2, CB3);  // elements 16+4i..
     }
+  } else if constexpr (T == Q4_0) {
+    // block 2q (bytes 0-17) or 2q+1 (bytes 18-35); raw nibbles 0..15, the -8
+    // offset is applied through the activation block sum
+    const uint32_t w[9] = {g.a.x, g.a.y, g.a.z, g.a.w, g.b.x, g.b.y, g.b.z, g.b.w, g.c};
+    uint32_t qs[4];
+    if (half == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qs[i] = shr16(w[i + 1], w[i]);
+      o.wsc = (double)h2f(w[0]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qs[i] = w[5 + i];
+      o.wsc = (double)h2f(w[4] >> 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o.cw[i] = qs[i] & 0x0F0F0F0Fu;             // elements 4i..4i+3
+      o.cw[i + 4] = (qs[i] >> 4) & 0x0F0F0F0Fu;  // elements 16+4i..
+    }
+  } else if constexpr (T == Q8_0) {
+    const uint32_t w[17] = {g.a.x, g.a.y, g.a.z, g.a.w, g.b.x, g.b.y, g.b.z, g.b.w,
+                            g.c.x, g.c.y, g.c.z, g.c.w, g.e.x, g.e.y, g.e.z, g.e.w, g.f};
+    if (half == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o.cw[i] = shr16(w[i + 1], w[i]);
+      o.wsc = (double)h2f(w[0]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o.cw[i] = w[9 + i];
+      o.wsc = (double)h2f(w[8] >> 16);
+    }
   } else {  // Q6_K
     const int h = q >> 1, gp = q & 1;
     // codes of Q8 block 4h+gp (half 0: g = gp, low nibbles) or 4h+gp+2 (half
@@ -192,11 +255,18 @@ template <int T> __device__ __forceinline__ int sub_index(int q, int half) {
 }
 
 // fp64 view of one Q8_1 block's scales: D and (Q4_K) S, or (Q6_K) 32 times
-// the integer sum of each 16-element half of q (for the -32 code offset).
+// the integer sum of each 16-element half of q (for the -32 code offset), or
+// (Q4_0) 8 times the integer sum of q (for the -8 code offset).
 __device__ __forceinline__ DsEntry ds_entry(int T, uint32_t ds, const u32x4& q0, const u32x4& q1) {
   DsEntry e;
   e.d = (double)h2f(ds & 0xFFFFu);
-  if (T == Q6_K) {
+  if (T == Q4_0) {
+    const uint32_t ones = 0x01010101u;
+    const int lo = dot4(q0.w, ones, dot4(q0.z, ones, dot4(q0.y, ones, dot4(q0.x, ones, 0))));
+    const int sum = dot4(q1.w, ones, dot4(q1.z, ones, dot4(q1.y, ones, dot4(q1.x, ones, lo))));
+    e.xs32[0] = 8 * sum;
+    e.xs32[1] = 0;
+  } else if (T == Q6_K) {
     const uint32_t ones = 0x01010101u;
     const int lo = dot4(q0.w, ones, dot4(q0.z, ones, dot4(q0.y, ones, dot4(q0.x, ones, 0))));
     const int hi = dot4(q1.w, ones, dot4(q1.z, ones, dot4(q1.y, ones, dot4(q1.x, ones, 0))));
@@ -228,6 +298,7 @@ __device__ __forceinline__ void dot_drain(const Sub<T>& sw, const uint32_t (&xa)
     int I = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) I = dot4(sw.cw[i], xa[i], I);
+    if constexpr (T == Q4_0) I -= de.xs32[0];             // sum (q - 8) x
     acc = fma(sw.wsc * de.d, (double)I, acc);             // exact product, one rounding
     if constexpr (T == Q4_K) acc = fma(sw.wmn, de.s, acc);
     if (DUMP && isp) isp[0] = I;
@@ -415,12 +486,13 @@ static int qmv_waves(int nsb) {
 static int qmv_depth(int type, int M, int N, int K) {
   const int nsb = K / QK;
   const long waves = (long)((N + QMV_SLOTS - 1) / QMV_SLOTS) * qmv_waves(nsb);
-  const long stage_bytes = waves * QMV_SLOTS * (long)(type == Q6_K ? 210 : (type == Q4_K ? 144 : 136));
+  const int bytes = type == Q6_K ? 210 : (type == IQ4_XS ? 136 : (type == Q8_0 ? 272 : 144));
+  const long stage_bytes = waves * QMV_SLOTS * (long)bytes;
   int d;
   if (stage_bytes >= (4L << 20)) d = M <= 4 ? 1 : 2;
   else if (stage_bytes >= (3L << 20)) d = 2;
   else d = 4;
-  if (type == Q6_K && d > 2) d = 2;
+  if ((type == Q6_K || type == Q8_0) && d > 2) d = 2;
   return d;
 }
 
@@ -446,7 +518,7 @@ static int launch_qmv_r(const uint8_t* W, int N, int K, const uint8_t* xq, float
     case 1: return launch_qmv_k<T, M, 1, false>(W, N, K, xq, y, isums, s);
     case 2: return launch_qmv_k<T, M, 2, false>(W, N, K, xq, y, isums, s);
     default:
-      if constexpr (T == Q6_K) return launch_qmv_k<T, M, 2, false>(W, N, K, xq, y, isums, s);
+      if constexpr (T == Q6_K || T == Q8_0) return launch_qmv_k<T, M, 2, false>(W, N, K, xq, y, isums, s);
       else return launch_qmv_k<T, M, 4, false>(W, N, K, xq, y, isums, s);
   }
 }
@@ -482,6 +554,12 @@ int launch_qmv(const void* W, int type, int N, int K, const void* xq, int M, flo
     case IQ4_XS:
       return dump ? launch_qmv_m<IQ4_XS, true>(w8, N, K, x8, M, y, isums, s)
                   : launch_qmv_m<IQ4_XS, false>(w8, N, K, x8, M, y, isums, s);
+    case Q4_0:
+      return dump ? launch_qmv_m<Q4_0, true>(w8, N, K, x8, M, y, isums, s)
+                  : launch_qmv_m<Q4_0, false>(w8, N, K, x8, M, y, isums, s);
+    case Q8_0:
+      return dump ? launch_qmv_m<Q8_0, true>(w8, N, K, x8, M, y, isums, s)
+                  : launch_qmv_m<Q8_0, false>(w8, N, K, x8, M, y, isums, s);
     default:
       return -2;
   }

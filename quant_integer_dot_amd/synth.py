@@ -37,6 +37,9 @@ QWEN3_8B = [
     ("o", 4096, 4096, Q4_K), ("gate", 12288, 4096, Q4_K), ("up", 12288, 4096, Q4_K),
     ("down", 4096, 12288, Q6_K),
 ]
+# The same shapes in the simple block formats: Q4_0 where the mixed model has
+# Q4_K, Q8_0 where it has Q6_K.
+QWEN3_8B_Q40_Q80 = [(n, N, K, Q4_0 if t == Q4_K else Q8_0) for (n, N, K, t) in QWEN3_8B]
 IQ4XS_H5120 = [
     ("qkv", 7168, 5120, IQ4_XS), ("o", 5120, 5120, IQ4_XS),
     ("gate", 17408, 5120, IQ4_XS), ("up", 17408, 5120, IQ4_XS),
@@ -50,6 +53,7 @@ WORKLOADS = {
     2: dict(name="qwen3-8b-decode", shapes=QWEN3_8B, layers=36, Ms=list(range(1, 9))),
     3: dict(name="iq4xs-h5120-decode", shapes=IQ4XS_H5120, layers=64, Ms=list(range(1, 9))),
     4: dict(name="qwen3-8b-prefill-512", shapes=QWEN3_8B, layers=36, Ms=[512]),
+    5: dict(name="qwen3-8b-q4_0-q8_0-decode", shapes=QWEN3_8B_Q40_Q80, layers=36, Ms=[1, 2, 4, 8]),
 }
 
 

@@ -35,7 +35,11 @@ def test_sizes(lib):
     assert qd.qdot_block_bytes(qd.QDOT_Q4_K) == 144
     assert qd.qdot_block_bytes(qd.QDOT_Q6_K) == 210
     assert qd.qdot_block_bytes(qd.QDOT_IQ4_XS) == 136
-    assert qd.qdot_block_bytes(0) == 0 and qd.qdot_block_bytes(4) == 0
+    assert qd.qdot_block_bytes(qd.QDOT_Q4_0) == 8 * 18
+    assert qd.qdot_block_bytes(qd.QDOT_Q8_0) == 8 * 34
+    assert qd.qdot_block_bytes(0) == 0 and qd.qdot_block_bytes(6) == 0
+    assert qd.qdot_weight_bytes(qd.QDOT_Q8_0, 4096, 12288) == 4096 * 384 * 34
+    assert qd.qdot_isum_count(qd.QDOT_Q4_0, 3, 512, 2) == 2 * 3 * 16
     assert qd.qdot_weight_bytes(qd.QDOT_Q4_K, 12288, 4096) == 12288 * 16 * 144
     assert qd.qdot_weight_bytes(qd.QDOT_Q6_K, 4096, 12288) == 4096 * 48 * 210
     assert qd.qdot_weight_bytes(qd.QDOT_Q4_K, 10, 100) == 0
@@ -48,6 +52,8 @@ def test_sizes(lib):
 def test_names_and_status(lib):
     assert qd.qdot_kernel_name(qd.QDOT_Q4_K, 8) == "qmv_dot4<Q4_K,8>"
     assert qd.qdot_kernel_name(qd.QDOT_IQ4_XS, 1) == "qmv_dot4<IQ4_XS,1>"
+    assert qd.qdot_kernel_name(qd.QDOT_Q8_0, 4) == "qmv_dot4<Q8_0,4>"
+    assert qd.qdot_kernel_name(qd.QDOT_Q4_0, 100) == "qmm_mfma<Q4_0>"
     assert qd.qdot_kernel_name(qd.QDOT_Q6_K, 512) == "qmm_mfma<Q6_K>"
     assert qd.qdot_kernel_name(qd.QDOT_Q4_K, 9) == "qmv_dot4<Q4_K,8-row chunks>"
     assert qd.qdot_kernel_name(qd.QDOT_Q4_K, 32) == "qmv_dot4<Q4_K,8-row chunks>"

@@ -15,7 +15,7 @@ from quant_integer_dot_amd import synth
 from gpu_util import assert_close, qmatmul, quantize, to_dev
 
 pytestmark = pytest.mark.gpu
-TYPES = [synth.Q4_K, synth.Q6_K, synth.IQ4_XS]
+TYPES = [synth.Q4_K, synth.Q6_K, synth.IQ4_XS, synth.Q4_0, synth.Q8_0]
 TN = synth.TYPE_NAMES
 
 
@@ -113,6 +113,26 @@ def test_one_hot_probes_rebuild_dequant(wtype):
         y, _ = qmatmul(Wd, wtype, N, K, xqd, 8)
         exp = (127 / 64) * wdeq[:, k0:k0 + 8].T
         assert np.array_equal(y, exp.astype(np.float32)), f"{TN[wtype]} k0={k0}"
+
+
+@pytest.mark.parametrize("wtype", TYPES)
+def test_one_hot_probes_prefill_path(wtype):
+    """The same closed form through the MFMA kernel (M = 40 one-hot rows per
+    launch): pins the MFMA operand and result layouts element by element."""
+    N, K, M = 70, 512, 40
+    W = synth.weights(wtype, N, K, (6, wtype))
+    Wd = to_dev(W)
+    wdeq = oracle.dequant(W, wtype, N, K)
+    for k0 in range(0, K, M):
+        x = np.zeros((M, K), np.float32)
+        ks = [k0 + i for i in range(M) if k0 + i < K]
+        for i, k in enumerate(ks):
+            x[i, k] = np.float32(127 * 2.0 ** -6)
+        xqd, _ = quantize(x)
+        y, _ = qmatmul(Wd, wtype, N, K, xqd, M)
+        exp = (127 / 64) * wdeq[:, ks].T
+        assert np.array_equal(y[:len(ks)], exp.astype(np.float32)), f"{TN[wtype]} k0={k0}"
+        assert not y[len(ks):].any()
 
 
 @pytest.mark.parametrize("wtype", TYPES)
@@ -215,7 +235,8 @@ def test_prefill_full_size_sampled(name, N, K, wtype):
 # ------------------------------------------- full-size shapes, sampled rows
 FULL = [(name, N, K, t) for (name, N, K, t) in synth.QWEN3_8B] + \
        [(name, N, K, t) for (name, N, K, t) in synth.IQ4XS_H5120] + \
-       [("c1-down", 1536, 8960, synth.Q4_K), ("c0", 1536, 1536, synth.Q4_K)]
+       [("c1-down", 1536, 8960, synth.Q4_K), ("c0", 1536, 1536, synth.Q4_K),
+        ("q4_0-gate", 12288, 4096, synth.Q4_0), ("q8_0-down", 4096, 12288, synth.Q8_0)]
 
 
 @pytest.mark.parametrize("name,N,K,wtype", FULL)
