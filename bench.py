@@ -46,7 +46,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="qwen3-8b-decode",
                    choices=["qwen3-8b-decode", "qwen3-8b-prefill-512", "iq4xs-h5120-decode",
-                            "qwen2.5-1.5b-decode", "qwen3-8b-q4_0-q8_0-decode"])
+                            "qwen2.5-1.5b-decode", "qwen3-8b-q4_0-q8_0-decode", "qwen3-8b-mid-batch"])
     p.add_argument("--ms", default=None, help="comma-separated M values (default per workload)")
     p.add_argument("--layers", type=int, default=None, help="override the layer count")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -72,6 +72,8 @@ def workload_def(name):
         return 1, synth.QWEN25_1P5B, 28, [1, 2, 4, 8]
     if name == "qwen3-8b-q4_0-q8_0-decode":
         return 5, synth.QWEN3_8B_Q40_Q80, 36, [1, 2, 4, 8]
+    if name == "qwen3-8b-mid-batch":
+        return 6, synth.QWEN3_8B, 36, [16, 32, 64]
     raise ValueError(name)
 
 
@@ -411,7 +413,8 @@ def main():
         metric, unit = "int8 TOP/s (% of MFMA int8 peak), M=512 prefill chunk, Qwen3-8B shapes", "TOP/s"
         value = step_ops / (ms_per_step * 1e-3) / 1e12
     else:
-        metric = METRIC if args.workload == "qwen3-8b-decode" else f"weight GB/s, {args.workload}"
+        metric = METRIC if args.workload == "qwen3-8b-decode" and Ms == [1, 2, 4, 8] else \
+            f"weight GB/s, {args.workload}, M={','.join(str(m) for m in Ms)}"
         unit = "GB/s"
     out = {
         "metric": metric,

@@ -110,9 +110,12 @@ int qdot_quantize_q8_1(const float *x, int64_t M, int64_t K, void *x_q8,
  * where I is the exact integer dot of the sub-block's weight codes with the
  * int8 activations and D, S are the activation block's fp16 d and s.  Every
  * scale product is exact and accumulated in fp64; y is rounded once to fp32.
- * M <= 8 runs the decode kernel (v_dot4_i32_i8, M-row tile); 8 < M <= 32 runs
- * it over chunks of 8 rows (each row bitwise equal to an M <= 8 call); M > 32
- * runs the MFMA i8 prefill kernel.  K % 256 == 0 is required. */
+ * M <= 8 runs the decode kernel (v_dot4_i32_i8, M-row tile); 8 < M <= 64 a
+ * mid-batch MFMA i8 kernel (16-row activation tiles, K split eight ways);
+ * M > 64 the MFMA i8 prefill kernel.  Within each of these three ranges a row
+ * of y is bitwise the same whatever M it is computed with; across them it may
+ * differ in the last fp32 bit (different fp64 summation orders).  K % 256 == 0
+ * is required. */
 int qdot_qmatmul(const void *W, int type, int64_t N, int64_t K,
                  const void *x_q8, int64_t M, float *y, void *stream);
 
@@ -127,7 +130,7 @@ int qdot_qmatmul_dump_isums(const void *W, int type, int64_t N, int64_t K,
 const char *qdot_status_str(int status);
 
 /* Name of the kernel qdot_qmatmul runs for (type, M), e.g. "qmv_dot4<Q4_K,8>",
- * "qmv_dot4<Q4_K,8-row chunks>" or "qmm_mfma<Q6_K>"; "invalid" for bad
+ * "qmm_skinny<Q4_K>" or "qmm_mfma<Q6_K>"; "invalid" for bad
  * arguments.  Static text. */
 const char *qdot_kernel_name(int type, int64_t M);
 

@@ -15,6 +15,8 @@ int launch_qmv(const void* W, int type, int N, int K, const void* xq, int M, flo
                int32_t* isums, hipStream_t s);
 int launch_qmm(const void* W, int type, int N, int K, const void* xq, int M, float* y,
                int32_t* isums, hipStream_t s);
+int launch_qmm_skinny(const void* W, int type, int N, int K, const void* xq, int M, float* y,
+                      int32_t* isums, hipStream_t s);
 }  // namespace qdot
 
 namespace {
@@ -36,17 +38,17 @@ int check_dims(int type, int64_t N, int64_t K, int64_t M) {
   return QDOT_OK;
 }
 
-// Mid-batch dispatch: up to this many activation rows the decode kernel runs
-// over chunks of at most 8 rows (each chunk reads the weights again, but the
-// integer-dot kernel's fixed cost is far below the MFMA kernel's at small M);
-// above it the MFMA kernel takes all rows at once.  Measured on MI355X, the
-// chunks win up to M = 14..80 depending on the shape (about 28 for the
-// 12288 x 4096 and 7168 x 5120 matrices, 56 for 4096 x 4096, 80 for
-// 4096 x 12288 Q6_K, 14 for 17408 x 5120 IQ4_XS); 32 is the compromise.
-// Rows computed through the chunks are bitwise the rows a call with M <= 8
-// returns.
-#ifndef QDOT_QMV_CHUNK_MAX_M
-#define QDOT_QMV_CHUNK_MAX_M 32
+// Mid-batch dispatch: 9 <= M <= QDOT_SKINNY_MAX_M runs the mid-batch MFMA
+// kernel (16 activation rows per tile, K split eight ways), larger M the
+// prefill kernel (64 or 32 activation rows per tile).  Measured on MI355X at
+// the Qwen3-8B shapes the mid-batch kernel beats running the decode kernel
+// over 8-row chunks at every M from 9 to 32 (4096 x 4096, M = 16: 11.8 vs
+// 15.8 us) and the prefill kernel up to M = 48 on every shape; at M = 64 it
+// is 2x faster on 4096 x 4096, 4096 x 12288 and 1024 x 4096 and 15 % slower
+// on 12288 x 4096 (a whole layer: 270 vs 437 us).  The choice depends on M
+// only, so the kernel a call runs is known from (type, M).
+#ifndef QDOT_SKINNY_MAX_M
+#define QDOT_SKINNY_MAX_M 64
 #endif
 
 int run_qmatmul(const void* W, int type, int64_t N, int64_t K, const void* x_q8, int64_t M,
@@ -57,14 +59,10 @@ int run_qmatmul(const void* W, int type, int64_t N, int64_t K, const void* x_q8,
   if (!aligned4(x_q8) || !aligned4(y) || (dump && !aligned4(isums))) return QDOT_E_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   int rc = 0;
-  if (M <= QDOT_QMV_CHUNK_MAX_M) {
-    const size_t xq_row = (size_t)(K / 32) * 36;
-    const size_t is_row = (size_t)N * (size_t)(K / sub_len(type));
-    for (int64_t m0 = 0; m0 < M && rc == 0; m0 += 8) {
-      const int mc = (int)(M - m0 < 8 ? M - m0 : 8);
-      rc = qdot::launch_qmv(W, type, (int)N, (int)K, static_cast<const uint8_t*>(x_q8) + m0 * xq_row, mc,
-                            y + m0 * N, dump ? isums + m0 * is_row : nullptr, s);
-    }
+  if (M <= 8) {
+    rc = qdot::launch_qmv(W, type, (int)N, (int)K, x_q8, (int)M, y, dump ? isums : nullptr, s);
+  } else if (M <= QDOT_SKINNY_MAX_M) {
+    rc = qdot::launch_qmm_skinny(W, type, (int)N, (int)K, x_q8, (int)M, y, dump ? isums : nullptr, s);
   } else {
     rc = qdot::launch_qmm(W, type, (int)N, (int)K, x_q8, (int)M, y, dump ? isums : nullptr, s);
   }
@@ -142,14 +140,13 @@ const char* qdot_kernel_name(int type, int64_t M) {
        "qmv_dot4<Q4_0,5>", "qmv_dot4<Q4_0,6>", "qmv_dot4<Q4_0,7>", "qmv_dot4<Q4_0,8>"},
       {"qmv_dot4<Q8_0,1>", "qmv_dot4<Q8_0,2>", "qmv_dot4<Q8_0,3>", "qmv_dot4<Q8_0,4>",
        "qmv_dot4<Q8_0,5>", "qmv_dot4<Q8_0,6>", "qmv_dot4<Q8_0,7>", "qmv_dot4<Q8_0,8>"}};
-  static const char* const mid[5] = {"qmv_dot4<Q4_K,8-row chunks>", "qmv_dot4<Q6_K,8-row chunks>",
-                                     "qmv_dot4<IQ4_XS,8-row chunks>", "qmv_dot4<Q4_0,8-row chunks>",
-                                     "qmv_dot4<Q8_0,8-row chunks>"};
+  static const char* const mid[5] = {"qmm_skinny<Q4_K>", "qmm_skinny<Q6_K>", "qmm_skinny<IQ4_XS>",
+                                     "qmm_skinny<Q4_0>", "qmm_skinny<Q8_0>"};
   static const char* const pre[5] = {"qmm_mfma<Q4_K>", "qmm_mfma<Q6_K>", "qmm_mfma<IQ4_XS>",
                                      "qmm_mfma<Q4_0>", "qmm_mfma<Q8_0>"};
   if (type < QDOT_Q4_K || type > QDOT_Q8_0 || M < 1 || M > kMaxDim) return "invalid";
   if (M <= 8) return dec[type - 1][M - 1];
-  return M <= QDOT_QMV_CHUNK_MAX_M ? mid[type - 1] : pre[type - 1];
+  return M <= QDOT_SKINNY_MAX_M ? mid[type - 1] : pre[type - 1];
 }
 
 const char* qdot_build_id(void) { return "libqdot gfx950 " __DATE__ " " __TIME__; }

@@ -54,10 +54,11 @@ def test_names_and_status(lib):
     assert qd.qdot_kernel_name(qd.QDOT_IQ4_XS, 1) == "qmv_dot4<IQ4_XS,1>"
     assert qd.qdot_kernel_name(qd.QDOT_Q8_0, 4) == "qmv_dot4<Q8_0,4>"
     assert qd.qdot_kernel_name(qd.QDOT_Q4_0, 100) == "qmm_mfma<Q4_0>"
+    assert qd.qdot_kernel_name(qd.QDOT_Q8_0, 16) == "qmm_skinny<Q8_0>"
     assert qd.qdot_kernel_name(qd.QDOT_Q6_K, 512) == "qmm_mfma<Q6_K>"
-    assert qd.qdot_kernel_name(qd.QDOT_Q4_K, 9) == "qmv_dot4<Q4_K,8-row chunks>"
-    assert qd.qdot_kernel_name(qd.QDOT_Q4_K, 32) == "qmv_dot4<Q4_K,8-row chunks>"
-    assert qd.qdot_kernel_name(qd.QDOT_Q4_K, 33) == "qmm_mfma<Q4_K>"
+    assert qd.qdot_kernel_name(qd.QDOT_Q4_K, 9) == "qmm_skinny<Q4_K>"
+    assert qd.qdot_kernel_name(qd.QDOT_IQ4_XS, 64) == "qmm_skinny<IQ4_XS>"
+    assert qd.qdot_kernel_name(qd.QDOT_Q4_K, 65) == "qmm_mfma<Q4_K>"
     assert qd.qdot_kernel_name(9, 1) == "invalid"
     assert qd.qdot_status_str(qd.QDOT_E_ALIGN) == "misaligned pointer"
     assert "gfx950" in qd.qdot_build_id()

@@ -3,7 +3,8 @@
 Bars: Q8_1 bytes bit-exact; integer sub-block sums bit-exact (debug dump);
 fp32 y within relative 1e-5 of the oracle's fp64 result on every output;
 y fully written (NaN-poisoned before each call); bitwise determinism and
-batch invariance (row m of y is identical for every M in 1..8).
+batch invariance (row m of y is identical for every M within one kernel's
+range: 1..8, 9..64, above 64).
 """
 import numpy as np
 import pytest
@@ -158,7 +159,7 @@ def test_zero_activations_give_zero():
 
 
 @pytest.mark.parametrize("wtype", TYPES)
-@pytest.mark.parametrize("M", [9, 16, 33])
+@pytest.mark.parametrize("M", [9, 16, 33, 64, 65])
 def test_qmatmul_m_above_8(wtype, M):
     N, K = 70, 1536
     W = synth.weights(wtype, N, K, (9, wtype, M))
@@ -171,24 +172,66 @@ def test_qmatmul_m_above_8(wtype, M):
     assert_close(y, y64, f"{TN[wtype]} M={M}")
 
 
-# ------------------------------------------------- mid-batch (8 < M <= 32)
+# ------------------------------------------------- mid-batch (8 < M <= 64)
 @pytest.mark.parametrize("wtype", TYPES)
-def test_mid_batch_chunks_equal_decode_rows(wtype):
-    """M = 9..32 runs the decode kernel over 8-row chunks: every row is bitwise
-    the row an M <= 8 call returns, sums stay exact, outputs within 1e-5."""
+def test_mid_batch_parity_and_invariance(wtype):
+    """M = 9..64 runs the 16-row MFMA kernel with an eight-way K split: sums
+    exact, outputs within 1e-5, and every row bitwise the same whatever M of
+    that range it is computed in."""
     N, K, M = 300, 2048, 27
     W = synth.weights(wtype, N, K, (2026, 72, wtype))
     Wd = to_dev(W)
-    x = synth.activations(M, K, (2026, 72, K, M, 7))
+    x = synth.activations(64, K, (2026, 72, K, 64, 7))
     xqd, xq = quantize(x)
-    y, isums = qmatmul(Wd, wtype, N, K, xqd, M, dump=True)
-    assert np.array_equal(isums, oracle.isums(W, wtype, N, K, xq, M))
-    y64, _, _ = oracle.qmatmul(W, wtype, N, K, xq, M)
-    assert_close(y, y64, f"{TN[wtype]} M={M}")
     row = K // 32 * 36
-    for m0, mc in ((0, 1), (5, 3), (19, 8), (26, 1)):
-        ys, _ = qmatmul(Wd, wtype, N, K, xqd[m0 * row:(m0 + mc) * row], mc)
-        assert np.array_equal(ys.view(np.uint32), y[m0:m0 + mc].view(np.uint32)), (m0, mc)
+    y, isums = qmatmul(Wd, wtype, N, K, xqd[:M * row], M, dump=True)
+    assert np.array_equal(isums, oracle.isums(W, wtype, N, K, xq[:M * row], M))
+    y64, _, _ = oracle.qmatmul(W, wtype, N, K, xq[:M * row], M)
+    assert_close(y, y64, f"{TN[wtype]} M={M}")
+    ym64, _ = qmatmul(Wd, wtype, N, K, xqd, 64)
+    y9, _ = qmatmul(Wd, wtype, N, K, xqd, 9)
+    assert np.array_equal(ym64[:M].view(np.uint32), y.view(np.uint32)), "M=64 vs M=27"
+    assert np.array_equal(y9.view(np.uint32), y[:9].view(np.uint32)), "M=9 vs M=27"
+
+
+@pytest.mark.parametrize("wtype", [synth.Q4_K, synth.Q6_K])
+def test_mid_batch_tile_width_invariance(wtype):
+    """N = 4096: M = 16 runs one 16-row weight tile per wave, M = 17 two (the
+    grid reaches 144 workgroups); the shared rows are bitwise equal and both
+    calls match the oracle."""
+    N, K = 4096, 512
+    W = synth.weights(wtype, N, K, (2026, 73, wtype))
+    Wd = to_dev(W)
+    x = synth.activations(17, K, (2026, 73, K, 17, 7))
+    xqd, xq = quantize(x)
+    y17, _ = qmatmul(Wd, wtype, N, K, xqd, 17)
+    y16, _ = qmatmul(Wd, wtype, N, K, xqd, 16)
+    assert np.array_equal(y16.view(np.uint32), y17[:16].view(np.uint32))
+    y64, _, _ = oracle.qmatmul(W, wtype, N, K, xq, 17)
+    assert_close(y17, y64, f"{TN[wtype]} N={N} M=17")
+
+
+MID_FULL = [(name, N, K, t) for (name, N, K, t) in synth.QWEN3_8B] + \
+           [(name, N, K, t) for (name, N, K, t) in synth.IQ4XS_H5120] + \
+           [("q4_0-gate", 12288, 4096, synth.Q4_0), ("q8_0-down", 4096, 12288, synth.Q8_0)]
+
+
+@pytest.mark.parametrize("name,N,K,wtype", MID_FULL)
+def test_mid_batch_full_size_sampled(name, N, K, wtype):
+    """M = 32 at the full projection shapes: sampled weight rows against the
+    oracle, and the rows of an M = 9 call bitwise equal to them."""
+    M = 32
+    W = synth.weights(wtype, N, K, (2026, 74, N, K))
+    Wd = to_dev(W)
+    x = synth.activations(M, K, (2026, 74, K, M, 7))
+    xqd, xq = quantize(x)
+    y, _ = qmatmul(Wd, wtype, N, K, xqd, M)
+    rng = np.random.default_rng(N + K + 2)
+    rows = np.unique(np.concatenate([rng.integers(0, N, 24), [0, N - 1]]))
+    y64, _ = oracle.qmatmul_rows(W, wtype, N, K, xq, M, rows)
+    assert_close(y[:, rows], y64, f"{name} {N}x{K} M={M}")
+    y9, _ = qmatmul(Wd, wtype, N, K, xqd[: qd.qdot_q8_1_bytes(9, K)], 9)
+    assert np.array_equal(y9.view(np.uint32), y[:9].view(np.uint32)), "M invariance"
 
 
 # --------------------------------------------------- prefill (MFMA path)
@@ -227,7 +270,7 @@ def test_prefill_full_size_sampled(name, N, K, wtype):
     rows = np.unique(np.concatenate([rng.integers(0, N, 24), [0, N - 1]]))
     y64, _ = oracle.qmatmul_rows(W, wtype, N, K, xq, M, rows)
     assert_close(y[:, rows], y64, f"{name} {N}x{K} M=512")
-    Ms = 40
+    Ms = 100
     y_s, _ = qmatmul(Wd, wtype, N, K, xqd[: qd.qdot_q8_1_bytes(Ms, K)], Ms)
     assert np.array_equal(y_s.view(np.uint32), y[:Ms].view(np.uint32)), "M invariance"
 
