@@ -21,6 +21,7 @@ Output: one JSON line (metric, value = whole-step weight GB/s, roofline of the
 dominant kernel, the CPU oracle's rate on a bounded sample, per-M details).
 """
 import argparse
+import ctypes
 import json
 import os
 import platform
@@ -53,6 +54,9 @@ def parse():
     p.add_argument("--no-check", action="store_true", help="skip the sampled oracle check")
     p.add_argument("--kernel-reps", type=int, default=None,
                    help="replays of each per-projection graph (default: steps)")
+    p.add_argument("--separate", action="store_true",
+                   help="one launch per projection (default: projections sharing an input in one "
+                        "qdot_qmatmul_multi launch for M <= 8)")
     p.add_argument("--eager-only", action="store_true",
                    help="run the sweep eagerly --steps times per M and exit (for counter passes)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -226,32 +230,64 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     # Projections that read the same quantized input share one quantization
-    # per layer (q/k/v, gate/up).  Everything runs in order on one stream:
-    # running the q/k/v and gate/up launches as parallel graph branches on
-    # side streams measured slower on MI355X (12.5 vs 10.3 ms per step).
+    # per layer (q/k/v, gate/up), and for M <= 8 one qdot_qmatmul_multi launch
+    # (unless --separate).  Everything runs in order on one stream: running
+    # the q/k/v and gate/up launches as parallel graph branches on side
+    # streams measured slower on MI355X (12.5 vs 10.3 ms per step).
+    groups = []
+    for pi, (name, N, K, t) in enumerate(shapes):
+        inp = INPUT_OF[name]
+        if not groups or groups[-1][0] != inp:
+            groups.append((inp, []))
+        groups[-1][1].append(pi)
+
+    def units(M):
+        """The launches of one layer after each quantization: (label, [proj indices])."""
+        out = []
+        for inp, pis in groups:
+            if not args.separate and M <= 8 and len(pis) > 1:
+                out.append(("+".join(shapes[pi][0] for pi in pis), pis))
+            else:
+                out.extend((shapes[pi][0], [pi]) for pi in pis)
+        return out
+
+    def unit_kernel(M, pis):
+        if len(pis) == 1:
+            return qd.qdot_kernel_name(shapes[pis[0]][3], M)
+        return f"qmv_dot4_multi<{'+'.join(synth.TYPE_NAMES[shapes[pi][3]] for pi in pis)},{M}>"
+
+    P_, I32_, I64_ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    multi_args = {}   # (M, layer, label) -> prebuilt ctypes arrays
+
     def sweep(M, only=None):
         """Launch one M's sweep on the current stream (all layers)."""
         b = bufs[M]
         s = torch.cuda.current_stream(dev).cuda_stream
-        groups = []
-        for pi, (name, N, K, t) in enumerate(shapes):
-            inp = INPUT_OF[name]
-            if not groups or groups[-1][0] != inp:
-                groups.append((inp, []))
-            groups[-1][1].append(pi)
+        us = units(M)
         for layer in range(layers):
             for inp, pis in groups:
                 K = shapes[pis[0]][2]
                 if only is None or only == "quantize":
                     rc = lib.qdot_quantize_q8_1(b["x"][inp].data_ptr(), M, K, b["xq"][inp].data_ptr(), s)
                     assert rc == 0, rc
-                todo = [pi for pi in pis if only is None or only == shapes[pi][0]]
-                if not todo:
-                    continue
-                for pi in todo:
-                    name, N, K, t = shapes[pi]
-                    rc = lib.qdot_qmatmul(Wdev[layer][pi].data_ptr(), t, N, K, b["xq"][inp].data_ptr(), M,
-                                          b["y"][name].data_ptr(), s)
+                for label, upis in us:
+                    if upis[0] not in pis or (only is not None and only != label):
+                        continue
+                    if len(upis) == 1:
+                        name, N, K, t = shapes[upis[0]]
+                        rc = lib.qdot_qmatmul(Wdev[layer][upis[0]].data_ptr(), t, N, K, b["xq"][inp].data_ptr(),
+                                              M, b["y"][name].data_ptr(), s)
+                    else:
+                        key = (M, layer, label)
+                        if key not in multi_args:
+                            n = len(upis)
+                            multi_args[key] = (
+                                (P_ * n)(*[Wdev[layer][pi].data_ptr() for pi in upis]),
+                                (I32_ * n)(*[shapes[pi][3] for pi in upis]),
+                                (I64_ * n)(*[shapes[pi][1] for pi in upis]),
+                                (P_ * n)(*[b["y"][shapes[pi][0]].data_ptr() for pi in upis]))
+                        wa, ta, na, ya = multi_args[key]
+                        rc = lib.qdot_qmatmul_multi(len(upis), wa, ta, na, K, b["xq"][inp].data_ptr(), M, ya, s)
                     assert rc == 0, rc
 
     # eager run once (also fills every xq buffer)
@@ -311,10 +347,10 @@ def main():
     per_m = {}
     for M in Ms:
         rows = {}
-        for pi, (name, N, K, t) in enumerate(shapes):
+        for label, upis in units(M):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                sweep(M, only=name)
+                sweep(M, only=label)
             g.replay()
             torch.cuda.synchronize()
             a, bb = ev(), ev()
@@ -324,18 +360,21 @@ def main():
             bb.record()
             torch.cuda.synchronize()
             us = a.elapsed_time(bb) * 1e3 / (reps * layers)
-            wb = qd.qdot_weight_bytes(t, N, K)
-            alg = wb + qd.qdot_q8_1_bytes(M, K) + 4 * M * N
-            rows[name] = {"N": N, "K": K, "type": synth.TYPE_NAMES[t], "us": round(us, 3),
-                          "weight_GBps": round(wb / us / 1e3, 1),
-                          "pct_hbm_peak": round(100 * wb / us / 1e3 / HBM_PEAK_GBS, 1)}
-            rows[name]["TOPs"] = round(2 * M * N * K / us / 1e6, 2)
-            kn = qd.qdot_kernel_name(t, M)
+            K = shapes[upis[0]][2]
+            Ns = [shapes[pi][1] for pi in upis]
+            wb = sum(qd.qdot_weight_bytes(shapes[pi][3], shapes[pi][1], K) for pi in upis)
+            alg = wb + qd.qdot_q8_1_bytes(M, K) + 4 * M * sum(Ns)
+            rows[label] = {"N": Ns[0] if len(Ns) == 1 else Ns, "K": K,
+                           "type": "+".join(synth.TYPE_NAMES[shapes[pi][3]] for pi in upis),
+                           "us": round(us, 3), "weight_GBps": round(wb / us / 1e3, 1),
+                           "pct_hbm_peak": round(100 * wb / us / 1e3 / HBM_PEAK_GBS, 1)}
+            rows[label]["TOPs"] = round(2 * M * sum(Ns) * K / us / 1e6, 2)
+            kn = unit_kernel(M, upis)
             e = kern.setdefault(kn, [0, 0.0, 0, 0])
             e[0] += alg * layers
             e[1] += us * layers * 1e-3
             e[2] += layers
-            e[3] += 2 * M * N * K * layers
+            e[3] += 2 * M * sum(Ns) * K * layers
         # quantizer
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -360,19 +399,29 @@ def main():
                          "sweep_weight_GBps": round(wb_m / (np.median(per_m_ms[M]) * 1e-3) / 1e9, 1),
                          "quantize_us": round(qus, 3), "qmatmul": rows}
 
-    dom = max(kern.items(), key=lambda kv: kv[1][1])
-    dname, (dbytes, dms, dn, dops) = dom
+    # The dominant kernel is the HIP kernel function with the largest share of
+    # the step, summed over its template instances (weight types, M tile,
+    # prefetch depth): its rate is its algorithmic bytes (or ops) over all its
+    # launches of a step divided by their summed duration.
+    fam = {}
+    for k, v in kern.items():
+        f = fam.setdefault(k.split("<")[0], [0, 0.0, 0, 0, []])
+        for i in range(4):
+            f[i] += v[i]
+        f[4].append(k)
+    dname, (dbytes, dms, dn, dops, dinst) = max(fam.items(), key=lambda kv: kv[1][1])
     if prefill:
         # a dense int8 contraction: priced against the int8 MFMA peak
         achieved = dops / (dms * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "kernel": dname, "achieved": round(achieved, 2),
+        roofline = {"bound": "mfma", "kernel": dname, "instances": dinst, "achieved": round(achieved, 2),
                     "peak": MFMA_I8_PEAK_TOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_I8_PEAK_TOPS, 4),
                     "traffic": recorded_traffic(dname, args.workload), "launches": dn,
                     "avg_launch_us": round(dms * 1e3 / dn, 3),
                     "algorithmic_ops_per_launch": round(dops / dn)}
     else:
         achieved = dbytes / (dms * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "kernel": dname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+        roofline = {"bound": "hbm", "kernel": dname, "instances": dinst, "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": recorded_traffic(dname, args.workload),
                     "launches": dn, "avg_launch_us": round(dms * 1e3 / dn, 3),
@@ -432,7 +481,8 @@ def main():
         "config": {"workload": args.workload, "layers": layers, "M": Ms,
                    "projections": [f"{n} {N}x{K} {synth.TYPE_NAMES[t]}" for n, N, K, t in shapes],
                    "weight_bytes_per_sweep": wbytes_sweep,
-                   "launches_per_step": len(Ms) * layers * (len(shapes) + len(inputs))},
+                   "launches_per_step": sum(len(units(M)) for M in Ms) * layers + len(Ms) * layers * len(inputs),
+                   "grouped_launches": not args.separate},
         **({"pct_mfma_i8_peak": round(100 * value / MFMA_I8_PEAK_TOPS, 2)} if prefill else
            {"pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1)}),
         "roofline": roofline,

@@ -126,6 +126,26 @@ int qdot_qmatmul_dump_isums(const void *W, int type, int64_t N, int64_t K,
                             const void *x_q8, int64_t M, float *y,
                             int32_t *isums, void *stream);
 
+/* Up to QDOT_MULTI_MAX weight matrices that read the same activation rows
+ * (same K and M), e.g. the Q, K and V projections of an attention layer or
+ * the gate and up projections of an FFN, in one launch: y[i] = W[i] x for
+ * i < n, each exactly as qdot_qmatmul(W[i], types[i], N[i], K, x_q8, M, y[i])
+ * computes it (bitwise the same y).  The pages fuse Q/K/V behind one shared
+ * Q8_1 quantization (the IQ4_XS hidden-5120 model's QKV matrix; xLLM v0.7
+ * log, section C.1, one activation quantization shared by every slot); this
+ * call does the same without requiring the matrices to share a weight type.
+ * W, types, N and y are host arrays of n entries; W[i] and y[i] are device
+ * pointers with the alignment qdot_qmatmul requires.  For M <= 8 the decode
+ * tiles of all matrices run in one launch (Q4_K with Q6_K, Q4_0 with Q8_0, or
+ * a single type; other mixes take one launch per type); for M > 8 the
+ * matrices are launched one after another.  The saving is the fixed cost of
+ * the launches replaced.  Errors as qdot_qmatmul; n outside 1..QDOT_MULTI_MAX
+ * is E_ARG.  Every argument is checked before anything is launched. */
+#define QDOT_MULTI_MAX 4
+int qdot_qmatmul_multi(int n, const void *const *W, const int *types,
+                       const int64_t *N, int64_t K, const void *x_q8,
+                       int64_t M, float *const *y, void *stream);
+
 /* Static text for a status code. */
 const char *qdot_status_str(int status);
 

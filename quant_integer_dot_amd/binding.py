@@ -53,6 +53,9 @@ def load():
     L.qdot_qmatmul.restype = i32
     L.qdot_qmatmul_dump_isums.argtypes = [P, i32, i64, i64, P, i64, P, P, P]
     L.qdot_qmatmul_dump_isums.restype = i32
+    L.qdot_qmatmul_multi.argtypes = [i32, ctypes.POINTER(P), ctypes.POINTER(i32), ctypes.POINTER(i64),
+                                     i64, P, i64, ctypes.POINTER(P), P]
+    L.qdot_qmatmul_multi.restype = i32
     L.qdot_status_str.argtypes = [i32]
     L.qdot_status_str.restype = ctypes.c_char_p
     L.qdot_kernel_name.argtypes = [i32, i64]
@@ -114,6 +117,21 @@ def qdot_qmatmul(W, wtype, N, K, x_q8, M, y, stream=None):
     s = _stream(stream, W, x_q8, y)
     _check(load().qdot_qmatmul(_addr(W), wtype, N, K, _addr(x_q8), M, _addr(y), s),
            "qdot_qmatmul")
+
+
+def qdot_qmatmul_multi(Ws, wtypes, Ns, K, x_q8, M, ys, stream=None):
+    """One launch over several matrices sharing x_q8: ys[i] = Ws[i] x."""
+    n = len(Ws)
+    if not (len(wtypes) == n and len(Ns) == n and len(ys) == n):
+        raise ValueError("Ws, wtypes, Ns and ys must have the same length")
+    s = _stream(stream, x_q8, *Ws, *ys)
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    w_arr = (P * max(n, 1))(*[_addr(w) for w in Ws])
+    t_arr = (i32 * max(n, 1))(*wtypes)
+    n_arr = (i64 * max(n, 1))(*Ns)
+    y_arr = (P * max(n, 1))(*[_addr(y) for y in ys])
+    _check(load().qdot_qmatmul_multi(n, w_arr, t_arr, n_arr, K, _addr(x_q8), M, y_arr, s),
+           "qdot_qmatmul_multi")
 
 
 def qdot_qmatmul_dump_isums(W, wtype, N, K, x_q8, M, y, isums, stream=None):

@@ -17,6 +17,8 @@ int launch_qmm(const void* W, int type, int N, int K, const void* xq, int M, flo
                int32_t* isums, hipStream_t s);
 int launch_qmm_skinny(const void* W, int type, int N, int K, const void* xq, int M, float* y,
                       int32_t* isums, hipStream_t s);
+int launch_qmv_multi(int n, const void* const* W, const int* types, const int* N, int K, const void* xq,
+                     int M, float* const* y, hipStream_t s);
 }  // namespace qdot
 
 namespace {
@@ -116,6 +118,31 @@ int qdot_qmatmul(const void* W, int type, int64_t N, int64_t K, const void* x_q8
 int qdot_qmatmul_dump_isums(const void* W, int type, int64_t N, int64_t K, const void* x_q8,
                             int64_t M, float* y, int32_t* isums, void* stream) {
   return run_qmatmul(W, type, N, K, x_q8, M, y, isums, stream, true);
+}
+
+int qdot_qmatmul_multi(int n, const void* const* W, const int* types, const int64_t* N, int64_t K,
+                       const void* x_q8, int64_t M, float* const* y, void* stream) {
+  if (n < 1 || n > QDOT_MULTI_MAX || !W || !types || !N || !y || !x_q8) return QDOT_E_ARG;
+  for (int i = 0; i < n; ++i) {
+    const int st = check_dims(types[i], N[i], K, M);
+    if (st) return st;
+    if (!W[i] || !y[i]) return QDOT_E_ARG;
+  }
+  if (!aligned4(x_q8)) return QDOT_E_ALIGN;
+  for (int i = 0; i < n; ++i)
+    if (!aligned4(y[i])) return QDOT_E_ALIGN;
+  if (M > 8) {  // mid-batch and prefill: one launch per matrix
+    for (int i = 0; i < n; ++i) {
+      const int st = run_qmatmul(W[i], types[i], N[i], K, x_q8, M, y[i], nullptr, stream, false);
+      if (st) return st;
+    }
+    return QDOT_OK;
+  }
+  int n32[QDOT_MULTI_MAX];
+  for (int i = 0; i < n; ++i) n32[i] = (int)N[i];
+  const int rc = qdot::launch_qmv_multi(n, W, types, n32, (int)K, x_q8, (int)M, y,
+                                        static_cast<hipStream_t>(stream));
+  return rc == 0 ? QDOT_OK : QDOT_E_HIP;
 }
 
 const char* qdot_status_str(int status) {

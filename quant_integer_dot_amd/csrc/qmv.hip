@@ -1,503 +1,8 @@
-// qmv.hip -- decode matmul for M = 1..8 token rows (rows a2-a5 of the hot
-// path): y[m][n] = sum_k w[n][k] * xhat[m][k] on the raw Q4_K / Q6_K / IQ4_XS
-// superblocks, with v_dot4_i32_i8 integer dots against Q8_1 activations.
-//
-// What the pages fix, and what this kernel keeps:
-//  * integer dots on the raw quantized weights, fp32 out, no fp32 weight copy
-//    (xLLM v0.7 log, section 1);
-//  * an M-row tile, so each weight byte is read from HBM once for all M rows
-//    (xLLM section B2, q4k_dp4a_matmul_q8_v2_kernel<M>; V100TPS 2026-08-12,
-//    "batched MMVQ: weights read once, not once per token position");
-//  * the weight decode and the IQ4_NL lookup done once per weight, not once per
-//    row (V100TPS 2026-08-12: moving the kvalues lookup to load time gave 1.5x);
-//  * exact int32 sums inside each sub-block, scales applied afterwards
-//    (Kestrel section 5).
-// What differs from the pages' V100 design: the M=8 V100 kernel was L1-bound
-// (xLLM section B2 ncu table).  Here each wave of a workgroup takes every
-// P-th superblock of 16 weight rows (4 lanes per row, 64 weights per lane);
-// the activations of a superblock (8*M Q8_1 blocks) are fetched one block per
-// lane together with its weights and published to the wave's LDS slice just
-// before use, so the 16 rows of the wave read them as LDS broadcasts instead
-// of pulling them through the vector memory path once per row.  The scale
-// drains are exact fp64 terms (every product exact, one rounding per
-// accumulate), so y is the fp32 rounding of a value within a few fp64 ulps
-// of the exact sum.
-
-#include "qdot_common.hpp"
+// qmv.hip -- launches of the decode kernel (M = 1..8) for one matrix; the
+// kernel is in qmv_kernel.hpp.
+#include "qmv_kernel.hpp"
 
 namespace qdot {
-
-constexpr int QMV_MAX_THREADS = 512;  // up to 8 waves per workgroup
-constexpr int QMV_SLOTS = 16;  // row slots per wave (64 lanes / 4 quarters)
-
-// One LDS entry per Q8_1 block and row m: the fp64 scale D and a second field
-// (Q4_K: fp64 S; Q6_K: 32 * sum of each 16-element half of q; IQ4_XS: unused).
-struct __attribute__((aligned(16))) DsEntry {
-  double d;
-  union {
-    double s;
-    int xs32[2];
-  };
-};
-static_assert(sizeof(DsEntry) == 16, "DsEntry is 16 bytes");
-
-// --------------------------------------------------------------- formats
-template <int T> struct Fmt;
-
-// Q4_K: bytes 0-1 d, 2-3 dmin, 4-15 scales[12], 16-143 qs.  Quarter q holds
-// qs[32q .. 32q+31]: low nibbles = sub-block 2q, high nibbles = sub-block 2q+1.
-template <> struct Fmt<Q4_K> {
-  struct Regs { u32x4 h, a, b; };
-  __device__ static Regs load(const uint8_t* sb, int q) {
-    Regs r;
-    r.h = ld16(sb);
-    r.a = ld16(sb + 16 + 32 * q);
-    r.b = ld16(sb + 32 + 32 * q);
-    return r;
-  }
-  // Q8_1 blocks (within the superblock) used by quarter q, and which sub-block
-  // of the superblock each is.
-  __device__ static int blk(int q, int half) { return 2 * q + half; }
-};
-
-// Q6_K: bytes 0-127 ql, 128-191 qh, 192-207 int8 scales, 208-209 d.  Quarter
-// q = (h = q/2, gp = q%2) holds ql[64h + 32gp ..+32] and qh[32h ..+32]: low
-// nibbles = Q8 block 4h+gp, high nibbles = Q8 block 4h+gp+2.
-template <> struct Fmt<Q6_K> {
-  struct Regs { u32x4 a, b, c, e, sc; uint32_t d; };
-  __device__ static Regs load(const uint8_t* sb, int q) {
-    const int h = q >> 1, gp = q & 1;
-    Regs r;
-    r.a = ld16(sb + 64 * h + 32 * gp);
-    r.b = ld16(sb + 64 * h + 32 * gp + 16);
-    r.c = ld16(sb + 128 + 32 * h);
-    r.e = ld16(sb + 128 + 32 * h + 16);
-    r.sc = ld16(sb + 192);
-    unsigned short dh;
-    __builtin_memcpy(&dh, sb + 208, 2);
-    r.d = dh;
-    return r;
-  }
-  __device__ static int blk(int q, int half) { return 4 * (q >> 1) + (q & 1) + 2 * half; }
-};
-
-// IQ4_XS: bytes 0-1 d, 2-3 scales_h, 4-7 scales_l, 8-135 qs.  Quarter q holds
-// qs[32q .. 32q+31] = sub-blocks 2q (bytes 0-15) and 2q+1 (bytes 16-31); in
-// each, low nibbles are elements 0-15 and high nibbles elements 16-31.
-template <> struct Fmt<IQ4_XS> {
-  struct Regs { u32x2 h; u32x4 a, b; };
-  __device__ static Regs load(const uint8_t* sb, int q) {
-    Regs r;
-    r.h = ld8(sb);
-    r.a = ld16(sb + 8 + 32 * q);
-    r.b = ld16(sb + 24 + 32 * q);
-    return r;
-  }
-  __device__ static int blk(int q, int half) { return 2 * q + half; }
-};
-
-// Q4_0: eight 18-byte blocks {fp16 d, qs[16]} per 256-weight group; quarter
-// q = blocks 2q and 2q+1 = bytes 36q .. 36q+35 (2-byte aligned fields).
-template <> struct Fmt<Q4_0> {
-  struct Regs { u32x4 a, b; uint32_t c; };
-  __device__ static Regs load(const uint8_t* sb, int q) {
-    Regs r;
-    r.a = ld16(sb + 36 * q);
-    r.b = ld16(sb + 36 * q + 16);
-    r.c = ld4(sb + 36 * q + 32);
-    return r;
-  }
-  __device__ static int blk(int q, int half) { return 2 * q + half; }
-};
-
-// Q8_0: eight 34-byte blocks {fp16 d, int8 qs[32]} per group; quarter q =
-// blocks 2q and 2q+1 = bytes 68q .. 68q+67.
-template <> struct Fmt<Q8_0> {
-  struct Regs { u32x4 a, b, c, e; uint32_t f; };
-  __device__ static Regs load(const uint8_t* sb, int q) {
-    Regs r;
-    r.a = ld16(sb + 68 * q);
-    r.b = ld16(sb + 68 * q + 16);
-    r.c = ld16(sb + 68 * q + 32);
-    r.e = ld16(sb + 68 * q + 48);
-    r.f = ld4(sb + 68 * q + 64);
-    return r;
-  }
-  __device__ static int blk(int q, int half) { return 2 * q + half; }
-};
-
-// IQ4_NL-style codebook as four little-endian dwords (entries 0-3, 4-7, 8-11,
-// 12-15).  Placeholder values (the pages name kvalues_iq4nl without printing
-// it): round_half_away(-127 + 240*(i/15)^1.4).
-//   -127 -122 -113 -102 | -89 -75 -60 -44 | -27 -10 9 28 | 49 69 91 113
-constexpr uint32_t CB0 = 0x9A8F8681u;  // 0x81=-127 0x86=-122 0x8F=-113 0x9A=-102
-constexpr uint32_t CB1 = 0xD4C4B5A7u;  // 0xA7=-89 0xB5=-75 0xC4=-60 0xD4=-44
-constexpr uint32_t CB2 = 0x1C09F6E5u;  // 0xE5=-27 0xF6=-10 0x09=9 0x1C=28
-constexpr uint32_t CB3 = 0x715B4531u;  // 0x31=49 0x45=69 0x5B=91 0x71=113
-
-// Four 4-bit indices (one per byte, values 0..15) -> four int8 codebook
-// values: two v_perm lookups on entries 0-7 and 8-15, then a v_perm that
-// picks, per byte, the first or the second result by bit 3 of the index.
-__device__ __forceinline__ uint32_t cb_lookup(uint32_t idx, uint32_t t0, uint32_t t1,
-                                              uint32_t t2, uint32_t t3) {
-  const uint32_t sel = idx & 0x07070707u;
-  const uint32_t lo = perm(t1, t0, sel);
-  const uint32_t hi = perm(t3, t2, sel);
-  const uint32_t pick = ((idx >> 1) & 0x04040404u) | 0x03020100u;
-  return perm(hi, lo, pick);
-}
-
-// ---------------------------------------------------------------- kernels
-//
-// One lane handles quarter q of superblock b for one weight row (slot s, row
-// n0 + s).  The P waves of a workgroup split the superblocks of each row:
-// wave w takes b = w, w+P, ...  P is a function of K only, and the kernel
-// walks a lane's superblocks and halves in the same order with the same fp64
-// operations for every M, so row m of y does not depend on M.
-
-// Per-row, per-half-quarter weight data: the 8 code dwords (32 int8 codes in
-// activation order) and what the drain needs.
-template <int T> struct Sub;
-template <> struct Sub<Q4_K> { uint32_t cw[8]; double wsc, wmn; };
-template <> struct Sub<IQ4_XS> { uint32_t cw[8]; double wsc; };
-template <> struct Sub<Q6_K> { uint32_t cw[8]; int s0, s1; double d; };
-template <> struct Sub<Q4_0> { uint32_t cw[8]; double wsc; };
-template <> struct Sub<Q8_0> { uint32_t cw[8]; double wsc; };
-
-template <int T>
-__device__ __forceinline__ void decode_sub(const typename Fmt<T>::Regs& g, int q, int half,
-                                           Sub<T>& o) {
-  if constexpr (T == Q4_K) {
-    // sub-block j = 2q + half: 6-bit scale and min (plain GGUF packing); q < 2
-    // reads scales[j], scales[j+4]; q >= 2 splices the nibbles of scales[j+4]
-    // with the top two bits of scales[j-4] (scale) and scales[j] (min).
-    const int sh = 8 * (((2 * q) & 3) + half);
-    const bool lo = q < 2;
-    const uint32_t Ys = g.h.y >> sh, Zs = g.h.z >> sh, Ws = g.h.w >> sh;
-    const uint32_t sc = lo ? (Ys & 63u) : ((Ws & 15u) | ((Ys >> 2) & 0x30u));
-    const uint32_t mn = lo ? (Zs & 63u) : (((Ws >> 4) & 15u) | ((Zs >> 2) & 0x30u));
-    o.wsc = (double)(h2f(g.h.x) * (float)sc);          // d*sc, exact in fp32
-    o.wmn = -(double)(h2f(g.h.x >> 16) * (float)mn);   // -dmin*m, exact in fp32
-    const uint32_t pk[8] = {g.a.x, g.a.y, g.a.z, g.a.w, g.b.x, g.b.y, g.b.z, g.b.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o.cw[i] = (half ? (pk[i] >> 4) : pk[i]) & 0x0F0F0F0Fu;
-  } else if constexpr (T == IQ4_XS) {
-    const int j = 2 * q + half;
-    const uint32_t sl = (g.h.y >> (4 * j)) & 15u;
-    const uint32_t shb = ((g.h.x >> 16) >> (2 * j)) & 3u;
-    const int ls = (int)(sl | (shb << 4));
-    o.wsc = (double)(h2f(g.h.x) * (float)(ls - 32));  // d*(ls-32), exact in fp32
-    const u32x4 pq = half ? g.b : g.a;
-    const uint32_t pk[4] = {pq.x, pq.y, pq.z, pq.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o.cw[i] = cb_lookup(pk[i], CB0, CB1, CB2, CB3);           // elements 4i..4i+3
-      o.cw[i + 4] = cb_lookup(pk[i] >> 4, CB0, CB1, CB2, CB3);  // elements 16+4i..
-    }
-  } else if constexpr (T == Q4_0) {
-    // block 2q (bytes 0-17) or 2q+1 (bytes 18-35); raw nibbles 0..15, the -8
-    // offset is applied through the activation block sum
-    const uint32_t w[9] = {g.a.x, g.a.y, g.a.z, g.a.w, g.b.x, g.b.y, g.b.z, g.b.w, g.c};
-    uint32_t qs[4];
-    if (half == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) qs[i] = shr16(w[i + 1], w[i]);
-      o.wsc = (double)h2f(w[0]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) qs[i] = w[5 + i];
-      o.wsc = (double)h2f(w[4] >> 16);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o.cw[i] = qs[i] & 0x0F0F0F0Fu;             // elements 4i..4i+3
-      o.cw[i + 4] = (qs[i] >> 4) & 0x0F0F0F0Fu;  // elements 16+4i..
-    }
-  } else if constexpr (T == Q8_0) {
-    const uint32_t w[17] = {g.a.x, g.a.y, g.a.z, g.a.w, g.b.x, g.b.y, g.b.z, g.b.w,
-                            g.c.x, g.c.y, g.c.z, g.c.w, g.e.x, g.e.y, g.e.z, g.e.w, g.f};
-    if (half == 0) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o.cw[i] = shr16(w[i + 1], w[i]);
-      o.wsc = (double)h2f(w[0]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o.cw[i] = w[9 + i];
-      o.wsc = (double)h2f(w[8] >> 16);
-    }
-  } else {  // Q6_K
-    const int h = q >> 1, gp = q & 1;
-    // codes of Q8 block 4h+gp (half 0: g = gp, low nibbles) or 4h+gp+2 (half
-    // 1: g = gp+2, high nibbles): values 0..63; the -32 offset is applied
-    // through the activation half-sums.
-    const uint32_t pl[8] = {g.a.x, g.a.y, g.a.z, g.a.w, g.b.x, g.b.y, g.b.z, g.b.w};
-    const uint32_t ph[8] = {g.c.x, g.c.y, g.c.z, g.c.w, g.e.x, g.e.y, g.e.z, g.e.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (half == 0)
-        o.cw[i] = (pl[i] & 0x0F0F0F0Fu) | ((ph[i] << (4 - 2 * gp)) & 0x30303030u);
-      else
-        o.cw[i] = ((pl[i] >> 4) & 0x0F0F0F0Fu) | ((ph[i] >> (2 * gp)) & 0x30303030u);
-    }
-    // int8 sub-scales of sub-blocks t0 = 8h + 2gp + 4*half and t0 + 1
-    const uint32_t scw = h ? (half ? g.sc.w : g.sc.z) : (half ? g.sc.y : g.sc.x);
-    o.s0 = (int)(int8_t)(scw >> (16 * gp));
-    o.s1 = (int)(int8_t)(scw >> (16 * gp + 8));
-    o.d = (double)h2f(g.d);
-  }
-}
-
-// Index of the first sub-block (of length SUB) that (q, half) covers inside
-// its superblock; Q6_K covers two consecutive 16-element sub-blocks.
-template <int T> __device__ __forceinline__ int sub_index(int q, int half) {
-  if constexpr (T == Q6_K) return 8 * (q >> 1) + 2 * (q & 1) + 4 * half;
-  else return 2 * q + half;
-}
-
-// fp64 view of one Q8_1 block's scales: D and (Q4_K) S, or (Q6_K) 32 times
-// the integer sum of each 16-element half of q (for the -32 code offset), or
-// (Q4_0) 8 times the integer sum of q (for the -8 code offset).
-__device__ __forceinline__ DsEntry ds_entry(int T, uint32_t ds, const u32x4& q0, const u32x4& q1) {
-  DsEntry e;
-  e.d = (double)h2f(ds & 0xFFFFu);
-  if (T == Q4_0) {
-    const uint32_t ones = 0x01010101u;
-    const int lo = dot4(q0.w, ones, dot4(q0.z, ones, dot4(q0.y, ones, dot4(q0.x, ones, 0))));
-    const int sum = dot4(q1.w, ones, dot4(q1.z, ones, dot4(q1.y, ones, dot4(q1.x, ones, lo))));
-    e.xs32[0] = 8 * sum;
-    e.xs32[1] = 0;
-  } else if (T == Q6_K) {
-    const uint32_t ones = 0x01010101u;
-    const int lo = dot4(q0.w, ones, dot4(q0.z, ones, dot4(q0.y, ones, dot4(q0.x, ones, 0))));
-    const int hi = dot4(q1.w, ones, dot4(q1.z, ones, dot4(q1.y, ones, dot4(q1.x, ones, 0))));
-    e.xs32[0] = 32 * lo;
-    e.xs32[1] = 32 * hi;
-  } else {
-    e.s = (double)h2f(ds >> 16);
-  }
-  return e;
-}
-
-// The integer dots of one (row, activation row, half quarter) and their
-// exact-term fp64 drain into acc.  Optionally stores the int32 sums.
-template <int T, bool DUMP>
-__device__ __forceinline__ void dot_drain(const Sub<T>& sw, const uint32_t (&xa)[8],
-                                          const DsEntry& de, double& acc, int32_t* isp) {
-  if constexpr (T == Q6_K) {
-    int I0 = 0, I1 = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) I0 = dot4(sw.cw[i], xa[i], I0);
-#pragma unroll
-    for (int i = 4; i < 8; ++i) I1 = dot4(sw.cw[i], xa[i], I1);
-    I0 -= de.xs32[0];
-    I1 -= de.xs32[1];
-    const int Pq = sw.s0 * I0 + sw.s1 * I1;               // exact int
-    acc = fma(sw.d * de.d, (double)Pq, acc);              // exact product, one rounding
-    if (DUMP && isp) { isp[0] = I0; isp[1] = I1; }
-  } else {
-    int I = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) I = dot4(sw.cw[i], xa[i], I);
-    if constexpr (T == Q4_0) I -= de.xs32[0];             // sum (q - 8) x
-    acc = fma(sw.wsc * de.d, (double)I, acc);             // exact product, one rounding
-    if constexpr (T == Q4_K) acc = fma(sw.wmn, de.s, acc);
-    if (DUMP && isp) isp[0] = I;
-  }
-}
-
-template <int T, int M, int R, bool DUMP>
-__device__ __forceinline__ int32_t* isum_ptr(int32_t* isums, int N, int K, int m, int n, int b, int q,
-                                             int half) {
-  constexpr int SUB = Geom<T>::SUB;
-  if (!DUMP || n >= N) return nullptr;
-  return isums + ((size_t)m * N + n) * (K / SUB) + (size_t)b * (QK / SUB) + sub_index<T>(q, half);
-}
-
-// Quad reduction (the 4 quarter lanes of a slot), then over the P waves in
-// order through LDS, then the fp32 store.  lds_red holds P*16*R*M doubles.
-template <int M, int R>
-__device__ __forceinline__ void reduce_store(double (&acc)[R][M], double* lds_red, int P, int wave,
-                                             int slot, int q, int tid, int n0, int N,
-                                             float* __restrict__ y) {
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      double v = acc[r][m];
-      v += __shfl_xor(v, 1);
-      v += __shfl_xor(v, 2);
-      acc[r][m] = v;
-    }
-  __syncthreads();  // the staging area is reused for the reduction
-  if (q == 0) {
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int m = 0; m < M; ++m)
-        lds_red[((wave * QMV_SLOTS + slot) * R + r) * M + m] = acc[r][m];
-  }
-  __syncthreads();
-  for (int o = tid; o < QMV_SLOTS * R * M; o += 64 * P) {
-    const int m = o % M;
-    const int r = (o / M) % R;
-    const int s = o / (M * R);
-    const int n = n0 + s + QMV_SLOTS * r;
-    double v = lds_red[(s * R + r) * M + m];
-    for (int w = 1; w < P; ++w) v += lds_red[((w * QMV_SLOTS + s) * R + r) * M + m];
-    if (n < N) y[(size_t)m * N + n] = (float)v;
-  }
-}
-
-// ------------------------------------------------------ the decode kernel
-constexpr int QMV_MGROUP = 4;  // activation rows held in registers at once
-
-// Each wave stages the activations of its own superblocks: for superblock b
-// the 8*M Q8_1 blocks (M rows x 8 blocks) are loaded one per lane, together
-// with the weights of b, and written to the wave's LDS slice just before b
-// is computed.  A load's data is waited for only when its superblock comes
-// up, so no wait covers weights fetched for later superblocks, and no
-// workgroup barrier sits in the main loop.
-template <int T, int M, int DEPTH, bool DUMP>
-__global__ __launch_bounds__(QMV_MAX_THREADS) void qmv_kernel(
-    const uint8_t* __restrict__ W, int N, int K, const uint8_t* __restrict__ xq,
-    float* __restrict__ y, int32_t* __restrict__ isums) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr int BYTES = Geom<T>::BYTES;
-  constexpr int ITEMS = 8 * M;  // Q8_1 blocks per superblock and activation rows
-  static_assert(ITEMS <= 64, "one activation block per lane");
-  const int P = blockDim.x >> 6;
-  const int nsb = K / QK;
-  const int nq8 = K / Q8_BLOCK;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, slot = lane >> 2, q = lane & 3;
-  const int n0 = blockIdx.x * QMV_SLOTS;
-
-  // this wave's LDS slice: codes [M][8][32 B], then scales [M][8]
-  uint8_t* lds_x = smem + (size_t)wave * ITEMS * (Q8_BLOCK + sizeof(DsEntry));
-  DsEntry* lds_ds = reinterpret_cast<DsEntry*>(lds_x + ITEMS * Q8_BLOCK);
-
-  const int nrow = n0 + slot;
-  const uint8_t* wrow = W + (size_t)(nrow < N ? nrow : N - 1) * nsb * BYTES;
-  // activation block of this lane: item = m*8 + j (lanes past 8*M repeat one)
-  const int item = lane % ITEMS;
-  const uint8_t* xsrc = xq + ((size_t)(item >> 3) * nq8 + (item & 7)) * Q8_BYTES;
-
-  double acc[M];
-#pragma unroll
-  for (int m = 0; m < M; ++m) acc[m] = 0.0;
-
-  struct Stage {
-    typename Fmt<T>::Regs w;
-    uint32_t ds;
-    u32x4 c0, c1;
-  };
-  Stage S[DEPTH];
-  // Unconditional loads (superblock clamped to the row): the compiler then
-  // waits for exactly the stage a compute step uses.
-  auto fetch = [&](Stage& st, int bsb) {
-    const int bc = bsb < nsb ? bsb : nsb - 1;
-    st.w = Fmt<T>::load(wrow + (size_t)bc * BYTES, q);
-    const uint8_t* src = xsrc + (size_t)bc * 8 * Q8_BYTES;
-    st.ds = ld4(src);
-    st.c0 = ld16(src + 4);
-    st.c1 = ld16(src + 20);
-  };
-  auto wave_sync = [] {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  };
-  auto compute = [&](const Stage& st, int b) {
-    wave_sync();  // the previous superblock's LDS reads are done
-    if (lane < ITEMS) {
-      *reinterpret_cast<u32x4*>(lds_x + item * Q8_BLOCK) = st.c0;
-      *reinterpret_cast<u32x4*>(lds_x + item * Q8_BLOCK + 16) = st.c1;
-      lds_ds[item] = ds_entry(T, st.ds, st.c0, st.c1);
-    }
-    wave_sync();
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int kb = Fmt<T>::blk(q, half);  // Q8_1 block within the superblock
-      Sub<T> sw;
-      decode_sub<T>(st.w, q, half, sw);
-#pragma unroll
-      for (int m0 = 0; m0 < M; m0 += QMV_MGROUP) {
-        constexpr int G = QMV_MGROUP;
-        uint32_t xa[G][8];
-        DsEntry de[G];
-#pragma unroll
-        for (int mm = 0; mm < G; ++mm) {
-          if (m0 + mm < M) {
-            const int it = (m0 + mm) * 8 + kb;
-            const u32x4 v0 = *reinterpret_cast<const u32x4*>(lds_x + it * Q8_BLOCK);
-            const u32x4 v1 = *reinterpret_cast<const u32x4*>(lds_x + it * Q8_BLOCK + 16);
-            xa[mm][0] = v0.x; xa[mm][1] = v0.y; xa[mm][2] = v0.z; xa[mm][3] = v0.w;
-            xa[mm][4] = v1.x; xa[mm][5] = v1.y; xa[mm][6] = v1.z; xa[mm][7] = v1.w;
-            de[mm] = lds_ds[it];
-          }
-        }
-#pragma unroll
-        for (int mm = 0; mm < G; ++mm)
-          if (m0 + mm < M)
-            dot_drain<T, DUMP>(sw, xa[mm], de[mm], acc[m0 + mm],
-                               isum_ptr<T, M, 1, DUMP>(isums, N, K, m0 + mm, nrow, b, q, half));
-      }
-    }
-  };
-
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d) fetch(S[d], wave + d * P);
-  const int niter = (((nsb + P - 1) / P) + DEPTH - 1) / DEPTH * DEPTH;
-  auto step = [&](Stage& st, int ii, bool refill) {
-    const int b = wave + ii * P;
-    if (b < nsb) compute(st, b);
-    if (refill) fetch(st, b + DEPTH * P);
-  };
-  // The last DEPTH iterations are peeled so that no prefetch runs past the
-  // row (a redundant load would still have to land before the wave retires).
-  int i = 0;
-  for (; i + DEPTH < niter; i += DEPTH) {
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) step(S[d], i + d, true);
-  }
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d) step(S[d], i + d, false);
-
-  double acc2[1][M];
-#pragma unroll
-  for (int m = 0; m < M; ++m) acc2[0][m] = acc[m];
-  reduce_store<M, 1>(acc2, reinterpret_cast<double*>(smem), P, wave, slot, q, tid, n0, N, y);
-}
-
-// ------------------------------------------------------------- launcher
-// Waves per workgroup: a function of K only (the K split fixes the fp64
-// summation order, which must not depend on M): about four superblocks per
-// wave, rounded up to a power of two, at most eight waves.  (Measured on
-// MI355X with K = 5120, 20 superblocks: eight waves beat five by 8-30 %.)
-static int qmv_waves(int nsb) {
-  const int p = (nsb + 3) / 4;
-  int q = 1;
-  while (q < p && q < 8) q *= 2;
-  return q;
-}
-
-// Superblocks in flight per wave (prefetch depth; it changes no arithmetic).
-// Chosen by measurement on MI355X (Qwen3-8B shapes, M = 1..8): the weight
-// bytes one stage of all waves puts in flight decide it.  About 7 MB per
-// stage (12288 x 4096 Q4_K, 4096 x 12288 Q6_K) already saturates HBM with one
-// stage at M <= 4; the 9 MB matrices want all four superblocks of a wave in
-// flight; Q6_K's larger register stage is kept to two.
-static int qmv_depth(int type, int M, int N, int K) {
-  const int nsb = K / QK;
-  const long waves = (long)((N + QMV_SLOTS - 1) / QMV_SLOTS) * qmv_waves(nsb);
-  const int bytes = type == Q6_K ? 210 : (type == IQ4_XS ? 136 : (type == Q8_0 ? 272 : 144));
-  const long stage_bytes = waves * QMV_SLOTS * (long)bytes;
-  int d;
-  if (stage_bytes >= (4L << 20)) d = M <= 4 ? 1 : 2;
-  else if (stage_bytes >= (3L << 20)) d = 2;
-  else d = 4;
-  if ((type == Q6_K || type == Q8_0) && d > 2) d = 2;
-  return d;
-}
 
 template <int T, int M, int DEPTH, bool DUMP>
 static int launch_qmv_k(const uint8_t* W, int N, int K, const uint8_t* xq, float* y, int32_t* isums,

@@ -117,3 +117,35 @@ def test_product_path_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in txt and "liboracle" not in txt, f
+
+
+def _multi(lib, n, Ws, types, Ns, K, xq, M, ys):
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    m = max(len(Ws), 1)
+    return lib.qdot_qmatmul_multi(n, (P * m)(*Ws), (i32 * m)(*types), (i64 * m)(*Ns), K, xq, M,
+                                  (P * m)(*ys), None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(n=0), qd.QDOT_E_ARG),
+    (dict(n=5, Ws=[16] * 5, types=[1] * 5, Ns=[16] * 5, ys=[16] * 5), qd.QDOT_E_ARG),
+    (dict(K=100), qd.QDOT_E_ARG),
+    (dict(types=[1, 9]), qd.QDOT_E_ARG),
+    (dict(Ns=[16, 0]), qd.QDOT_E_ARG),
+    (dict(M=0), qd.QDOT_E_ARG),
+    (dict(Ws=[16, 0]), qd.QDOT_E_ARG),
+    (dict(ys=[16, 0]), qd.QDOT_E_ARG),
+    (dict(xq=0), qd.QDOT_E_ARG),
+    (dict(xq=18), qd.QDOT_E_ALIGN),
+    (dict(ys=[16, 34]), qd.QDOT_E_ALIGN),
+])
+def test_qmatmul_multi_validation(lib, case, status):
+    """Every argument of the grouped call is checked before anything is launched."""
+    a = dict(n=2, Ws=[16, 16], types=[1, 2], Ns=[16, 16], K=256, xq=16, M=1, ys=[16, 16])
+    a.update(case)
+    assert _multi(lib, a["n"], a["Ws"], a["types"], a["Ns"], a["K"], a["xq"], a["M"], a["ys"]) == status
+
+
+def test_binding_multi_lengths(lib):
+    with pytest.raises(ValueError):
+        qd.qdot_qmatmul_multi([16, 16], [1], [16, 16], 256, 16, 1, [16, 16], stream=0)

@@ -1,0 +1,87 @@
+"""GPU: the grouped call (qdot_qmatmul_multi) against single-matrix calls and
+the oracle.  Each matrix of a group must come out bitwise equal to its own
+qdot_qmatmul call (same tile code, K split and summation order), so the
+single-call parity tests carry over; sampled rows are also checked against
+the oracle directly."""
+import numpy as np
+import pytest
+
+import oracle
+from quant_integer_dot_amd import binding as qd
+from quant_integer_dot_amd import synth
+
+from gpu_util import assert_close, dev, qmatmul, quantize, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qd.load()
+
+
+def run_multi(Wds, types, Ns, K, xqd, M):
+    import torch
+    ys = [torch.full((M, N), float("nan"), dtype=torch.float32, device=dev()) for N in Ns]
+    qd.qdot_qmatmul_multi(Wds, types, Ns, K, xqd, M, ys)
+    torch.cuda.synchronize()
+    return [y.cpu().numpy() for y in ys]
+
+
+def check_group(mats, K, M, seed, n_oracle_rows=6):
+    Ws = [synth.weights(t, N, K, (2026, 80, seed, i)) for i, (N, t) in enumerate(mats)]
+    Wds = [to_dev(W) for W in Ws]
+    x = synth.activations(M, K, (2026, 80, seed, K, M))
+    xqd, xq = quantize(x)
+    types = [t for _, t in mats]
+    Ns = [N for N, _ in mats]
+    ys = run_multi(Wds, types, Ns, K, xqd, M)
+    for i, (N, t) in enumerate(mats):
+        y1, _ = qmatmul(Wds[i], t, N, K, xqd, M)
+        assert np.array_equal(ys[i].view(np.uint32), y1.view(np.uint32)), \
+            f"matrix {i} ({synth.TYPE_NAMES[t]} {N}x{K}) M={M}: group != single call"
+        rows = np.unique(np.concatenate([np.random.default_rng(seed + i).integers(0, N, n_oracle_rows),
+                                         [0, N - 1]]))
+        y64, _ = oracle.qmatmul_rows(Ws[i], t, N, K, xq, M, rows)
+        assert_close(ys[i][:, rows], y64, f"group matrix {i} M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_qkv_mixed_q4k_q6k(M):
+    """Q (Q4_K), K (Q4_K), V (Q6_K), ragged row counts, one launch."""
+    check_group([(200, synth.Q4_K), (70, synth.Q4_K), (33, synth.Q6_K)], 1024, M, seed=M)
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_gate_up_full_size(M):
+    """Gate and up of the 8B FFN (two 12288 x 4096 Q4_K) in one launch."""
+    check_group([(12288, synth.Q4_K), (12288, synth.Q4_K)], 4096, M, seed=10 + M, n_oracle_rows=8)
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_qkv_full_size(M):
+    check_group([(4096, synth.Q4_K), (1024, synth.Q4_K), (1024, synth.Q6_K)], 4096, M, seed=20 + M)
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_q4_0_with_q8_0(M):
+    check_group([(130, synth.Q4_0), (64, synth.Q8_0), (17, synth.Q4_0)], 768, M, seed=30 + M)
+
+
+@pytest.mark.parametrize("M", [2, 7])
+def test_unfused_mix_runs_per_type(M):
+    """IQ4_XS with Q4_K and Q8_0: one launch per type, same results."""
+    check_group([(48, synth.IQ4_XS), (40, synth.Q4_K), (24, synth.Q8_0), (16, synth.IQ4_XS)], 512, M,
+                seed=40 + M)
+
+
+@pytest.mark.parametrize("M", [9, 40, 100])
+def test_above_decode_launches_each(M):
+    check_group([(96, synth.Q4_K), (50, synth.Q6_K)], 512, M, seed=50 + M)
+
+
+def test_single_matrix_group():
+    check_group([(300, synth.IQ4_XS)], 5120, 3, seed=60)
