@@ -81,6 +81,12 @@ def workload_def(name):
     raise ValueError(name)
 
 
+# The HIP kernel function behind each kernel label of qdot_kernel_name (and
+# of the grouped decode launch).
+KERNEL_FUNCTION = {"qmv_dot4": "qmv_kernel", "qmv_mfma": "qmv_kernel", "qmv_multi": "qmv_multi_kernel",
+                   "qmm_skinny": "qmm_skinny_kernel", "qmm_mfma": "qmm_mfma_kernel",
+                   "quantize_q8_1": "quantize_q8_1_kernel"}
+
 # The input each projection reads: projections sharing an input share one
 # activation quantization (xLLM v0.7 log, section C: one d_xn_q8 per step).
 INPUT_OF = {"q": "attn", "k": "attn", "v": "attn", "qkv": "attn", "o": "o",
@@ -254,7 +260,7 @@ def main():
     def unit_kernel(M, pis):
         if len(pis) == 1:
             return qd.qdot_kernel_name(shapes[pis[0]][3], M)
-        return f"qmv_dot4_multi<{'+'.join(synth.TYPE_NAMES[shapes[pi][3]] for pi in pis)},{M}>"
+        return "qmv_multi<" + "+".join(qd.qdot_kernel_name(shapes[pi][3], M) for pi in pis) + ">"
 
     P_, I32_, I64_ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     multi_args = {}   # (M, layer, label) -> prebuilt ctypes arrays
@@ -405,7 +411,7 @@ def main():
     # launches of a step divided by their summed duration.
     fam = {}
     for k, v in kern.items():
-        f = fam.setdefault(k.split("<")[0], [0, 0.0, 0, 0, []])
+        f = fam.setdefault(KERNEL_FUNCTION[k.split("<")[0]], [0, 0.0, 0, 0, []])
         for i in range(4):
             f[i] += v[i]
         f[4].append(k)

@@ -110,7 +110,9 @@ int qdot_quantize_q8_1(const float *x, int64_t M, int64_t K, void *x_q8,
  * where I is the exact integer dot of the sub-block's weight codes with the
  * int8 activations and D, S are the activation block's fp16 d and s.  Every
  * scale product is exact and accumulated in fp64; y is rounded once to fp32.
- * M <= 8 runs the decode kernel (v_dot4_i32_i8, M-row tile); 8 < M <= 64 a
+ * M <= 8 runs the decode kernel (v_dot4_i32_i8, M-row tile; for Q4_K at
+ * M = 7, 8 the integer dots run on v_mfma_i32_32x32x32_i8 instead, summed in
+ * the same order, so the rows are bitwise those of the dot4 tile); 8 < M <= 64 a
  * mid-batch MFMA i8 kernel (16-row activation tiles, K split eight ways);
  * M > 64 the MFMA i8 prefill kernel.  Within each of these three ranges a row
  * of y is bitwise the same whatever M it is computed with; across them it may
@@ -137,8 +139,9 @@ int qdot_qmatmul_dump_isums(const void *W, int type, int64_t N, int64_t K,
  * W, types, N and y are host arrays of n entries; W[i] and y[i] are device
  * pointers with the alignment qdot_qmatmul requires.  For M <= 8 the decode
  * tiles of all matrices run in one launch (Q4_K with Q6_K, Q4_0 with Q8_0, or
- * a single type; other mixes take one launch per type); for M > 8 the
- * matrices are launched one after another.  The saving is the fixed cost of
+ * a single type; other mixes take one launch per type), Q4_K tiles on the
+ * MFMA units from M = 5; for M > 8 the matrices are launched one after
+ * another.  The saving is the fixed cost of
  * the launches replaced.  Errors as qdot_qmatmul; n outside 1..QDOT_MULTI_MAX
  * is E_ARG.  Every argument is checked before anything is launched. */
 #define QDOT_MULTI_MAX 4
@@ -149,8 +152,8 @@ int qdot_qmatmul_multi(int n, const void *const *W, const int *types,
 /* Static text for a status code. */
 const char *qdot_status_str(int status);
 
-/* Name of the kernel qdot_qmatmul runs for (type, M), e.g. "qmv_dot4<Q4_K,8>",
- * "qmm_skinny<Q4_K>" or "qmm_mfma<Q6_K>"; "invalid" for bad
+/* Name of the kernel qdot_qmatmul runs for (type, M), e.g. "qmv_dot4<Q4_K,4>",
+ * "qmv_mfma<Q4_K,8>", "qmm_skinny<Q4_K>" or "qmm_mfma<Q6_K>"; "invalid" for bad
  * arguments.  Static text. */
 const char *qdot_kernel_name(int type, int64_t M);
 

@@ -158,7 +158,7 @@ const char* qdot_status_str(int status) {
 const char* qdot_kernel_name(int type, int64_t M) {
   static const char* const dec[5][8] = {
       {"qmv_dot4<Q4_K,1>", "qmv_dot4<Q4_K,2>", "qmv_dot4<Q4_K,3>", "qmv_dot4<Q4_K,4>",
-       "qmv_dot4<Q4_K,5>", "qmv_dot4<Q4_K,6>", "qmv_dot4<Q4_K,7>", "qmv_dot4<Q4_K,8>"},
+       "qmv_dot4<Q4_K,5>", "qmv_dot4<Q4_K,6>", "qmv_mfma<Q4_K,7>", "qmv_mfma<Q4_K,8>"},
       {"qmv_dot4<Q6_K,1>", "qmv_dot4<Q6_K,2>", "qmv_dot4<Q6_K,3>", "qmv_dot4<Q6_K,4>",
        "qmv_dot4<Q6_K,5>", "qmv_dot4<Q6_K,6>", "qmv_dot4<Q6_K,7>", "qmv_dot4<Q6_K,8>"},
       {"qmv_dot4<IQ4_XS,1>", "qmv_dot4<IQ4_XS,2>", "qmv_dot4<IQ4_XS,3>", "qmv_dot4<IQ4_XS,4>",

@@ -7,12 +7,10 @@ namespace qdot {
 template <int T, int M, int DEPTH, bool DUMP>
 static int launch_qmv_k(const uint8_t* W, int N, int K, const uint8_t* xq, float* y, int32_t* isums,
                         hipStream_t s) {
-  const int nsb = K / QK;
-  const int P = qmv_waves(nsb);
-  const size_t stage = (size_t)P * 8 * M * (Q8_BLOCK + sizeof(DsEntry));
-  const size_t red = (size_t)P * QMV_SLOTS * M * sizeof(double);
-  const size_t lds = stage > red ? stage : red;
-  const int grid = (N + QMV_SLOTS - 1) / QMV_SLOTS;
+  const int P = qmv_waves(K / QK);
+  const size_t lds = qmv_lds_bytes<T, M>(P);
+  constexpr int ROWS = qmv_tile_rows<T, M>();
+  const int grid = (N + ROWS - 1) / ROWS;
   hipLaunchKernelGGL((qmv_kernel<T, M, DEPTH, DUMP>), dim3(grid), dim3(64 * P), lds, s, W, N, K, xq,
                      y, isums);
   return hipGetLastError() == hipSuccess ? 0 : -1;
@@ -22,11 +20,12 @@ template <int T, int M, bool DUMP>
 static int launch_qmv_r(const uint8_t* W, int N, int K, const uint8_t* xq, float* y,
                         int32_t* isums, hipStream_t s) {
   if constexpr (DUMP) return launch_qmv_k<T, M, 2, true>(W, N, K, xq, y, isums, s);
-  switch (qmv_depth(T, M, N, K)) {
+  switch (qmf_ok<T, M>() ? qmf_depth(qmv_stage_bytes(T, N, K)) : qmv_depth(T, M, N, K)) {
     case 1: return launch_qmv_k<T, M, 1, false>(W, N, K, xq, y, isums, s);
     case 2: return launch_qmv_k<T, M, 2, false>(W, N, K, xq, y, isums, s);
     default:
-      if constexpr (T == Q6_K || T == Q8_0) return launch_qmv_k<T, M, 2, false>(W, N, K, xq, y, isums, s);
+      if constexpr (T == Q6_K || T == Q8_0 || qmf_ok<T, M>())
+        return launch_qmv_k<T, M, 2, false>(W, N, K, xq, y, isums, s);
       else return launch_qmv_k<T, M, 4, false>(W, N, K, xq, y, isums, s);
   }
 }

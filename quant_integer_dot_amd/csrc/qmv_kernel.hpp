@@ -470,12 +470,195 @@ __device__ __forceinline__ void qmv_tile(const uint8_t* __restrict__ W, int N, i
   reduce_store<M, 1>(acc2, reinterpret_cast<double*>(smem), P, wave, slot, q, tid, n0, N, y);
 }
 
+// ------------------------------------------ the MFMA tile for M = 7, 8
+//
+// The same sums as qmv_tile, in the same fp64 order, with the integer dots
+// on v_mfma_i32_32x32x32_i8 (Q4_K weights).  At M = 8 each of qmv_tile's 16
+// row slots reads all 8*M activation blocks of a superblock from LDS (48 KB
+// per wave and superblock); here the matrix unit reuses every activation byte
+// across 32 weight rows, and only the fp64 scales go through LDS.
+//
+// A workgroup owns 32 weight rows; its P waves split K exactly as qmv_tile's
+// (wave w takes superblocks w, w+P, ...).  Lane l supplies weight row
+// n = l%32 (B operand: 16 codes of K-slice s = l/32) and row i = l%32 of the
+// A operand, which holds activation row m = i%8 of the Q8_1 block in "slot"
+// i/8: the 32-row A tile stacks the four blocks of a group (sub-blocks 4g ..
+// 4g+3, i.e. quarters 2g and 2g+1) for 8 activation rows, and the MFMA of
+// sub-block 4g+j zeroes the other slots' rows, so after the group's four
+// MFMAs result register r of lane l holds the exact int32 sum of activation
+// row 4s + r%4, weight row n and sub-block 4g + r/4 (gfx950 layout:
+// D[8(r/4) + 4s + r%4][l%32]).  Lane l then drains its 4 activation rows into
+// per-quarter fp64 accumulators in qmv_tile's order (sub-block 2q before
+// 2q+1, superblocks in wave order), and the quarters and waves are added in
+// qmv_tile's order, so every output is bitwise the same as qmv_tile's: rows
+// stay M-invariant across the two tiles.
+typedef int qmf_v4i __attribute__((ext_vector_type(4)));
+typedef int qmf_v16i __attribute__((ext_vector_type(16)));
+
+constexpr int QMF_ROWS = 32;  // weight rows per workgroup
+// Smallest M that runs the MFMA tile, measured on MI355X (Qwen3-8B shapes):
+// alone, a 4096 x 4096 launch is faster on the dot4 tile up to M = 6 (its
+// 128 MFMA workgroups are too few), while the grouped launches (q+k+v,
+// gate+up: 2-3x the workgroups) gain 7-12 % per sweep already at M = 5, 6.
+constexpr int QMF_MIN_M = 7;
+constexpr int QMF_MIN_M_GROUPED = 5;
+template <int T, int M, bool GROUPED = false> constexpr bool qmf_ok() {
+  return M >= (GROUPED ? QMF_MIN_M_GROUPED : QMF_MIN_M) && T == Q4_K;
+}
+template <int T, int M, bool GROUPED = false> constexpr int qmv_tile_rows() {
+  return qmf_ok<T, M, GROUPED>() ? QMF_ROWS : QMV_SLOTS;
+}
+
+struct __attribute__((aligned(16))) QmfDs { double d, s; };  // fp64 D and S of one Q8_1 block
+
+template <int T, int M, int DEPTH, bool DUMP>
+__device__ __forceinline__ void qmf_tile(const uint8_t* __restrict__ W, int N, int K,
+                                         const uint8_t* __restrict__ xq, float* __restrict__ y,
+                                         int32_t* __restrict__ isums, int tile, uint8_t* smem) {
+  static_assert(T == Q4_K, "the MFMA decode tile takes Q4_K weights");
+  constexpr int BYTES = Geom<T>::BYTES;
+  constexpr int SUB = Geom<T>::SUB;
+  const int P = blockDim.x >> 6;
+  const int nsb = K / QK;
+  const int nq8 = K / Q8_BLOCK;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 31, s = lane >> 5;
+  const int slot = (lane & 31) >> 3, mrow = lane & 7;  // this lane's A row: block slot, activation row
+  const int n0 = tile * QMF_ROWS;
+  const int nrow = n0 + n;
+  const uint8_t* wrow = W + (size_t)(nrow < N ? nrow : N - 1) * nsb * BYTES;
+  // this lane's A data: row mrow (rows >= M read row 0 and are masked to zero)
+  const uint8_t* xa_row = xq + ((size_t)(mrow < M ? mrow : 0) * nq8 + slot) * Q8_BYTES + 4 + 16 * s;
+  const uint32_t amask = mrow < M ? 0xFFFFFFFFu : 0u;
+  // scale entry this lane publishes per superblock: activation row lane/8, block lane%8
+  const int dm = lane >> 3, dj = lane & 7;
+  const uint8_t* xd_src = xq + ((size_t)(dm < M ? dm : 0) * nq8 + dj) * Q8_BYTES;
+  QmfDs* lds_ds = reinterpret_cast<QmfDs*>(smem) + wave * 64;
+
+  double acc[4][4];  // [quarter][activation row 4s + mm]
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) acc[q][mm] = 0.0;
+
+  struct Stage {
+    u32x4 h, q[4];  // header (d, dmin, scales); K-slice s code bytes of each quarter
+    u32x4 a[2];     // this lane's A data in groups 0 and 1
+    uint32_t ds;    // d, s of the published scale entry
+  };
+  Stage S[DEPTH];
+  auto fetch = [&](Stage& st, int bsb) {
+    const int bc = bsb < nsb ? bsb : nsb - 1;
+    const uint8_t* sb = wrow + (size_t)bc * BYTES;
+    st.h = ld16(sb);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) st.q[q] = ld16(sb + 16 + 32 * q + 16 * s);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) st.a[g] = ld16(xa_row + (size_t)(8 * bc + 4 * g) * Q8_BYTES);
+    st.ds = ld4(xd_src + (size_t)8 * bc * Q8_BYTES);
+  };
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  auto compute = [&](const Stage& st, int b) {
+    wave_sync();  // the previous superblock's scale reads are done
+    lds_ds[lane] = QmfDs{(double)h2f(st.ds & 0xFFFFu), (double)h2f(st.ds >> 16)};
+    wave_sync();
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const qmf_v4i a = qmf_v4i{(int)(st.a[g].x & amask), (int)(st.a[g].y & amask),
+                                (int)(st.a[g].z & amask), (int)(st.a[g].w & amask)};
+      const qmf_v4i z4 = {0, 0, 0, 0};
+      qmf_v16i C = {0};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        // sub-block 4g + jj: quarter 2g + jj/2, low (jj even) or high nibbles
+        const u32x4 v = st.q[2 * g + (jj >> 1)];
+        const int sh = 4 * (jj & 1);
+        const qmf_v4i bq = qmf_v4i{(int)((v.x >> sh) & 0x0F0F0F0Fu), (int)((v.y >> sh) & 0x0F0F0F0Fu),
+                                   (int)((v.z >> sh) & 0x0F0F0F0Fu), (int)((v.w >> sh) & 0x0F0F0F0Fu)};
+        C = __builtin_amdgcn_mfma_i32_32x32x32_i8(slot == jj ? a : z4, bq, C, 0, 0, 0);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = 4 * g + jj;
+        // 6-bit scale and min of sub-block j, as qmv_tile's decode_sub computes them
+        const int sh = 8 * jj;
+        const uint32_t Ys = st.h.y >> sh, Zs = st.h.z >> sh, Ws = st.h.w >> sh;
+        const uint32_t sc = g == 0 ? (Ys & 63u) : ((Ws & 15u) | ((Ys >> 2) & 0x30u));
+        const uint32_t mn = g == 0 ? (Zs & 63u) : (((Ws >> 4) & 15u) | ((Zs >> 2) & 0x30u));
+        const double wsc = (double)(h2f(st.h.x) * (float)sc);
+        const double wmn = -(double)(h2f(st.h.x >> 16) * (float)mn);
+        // rows m >= M (upper-half lanes at M = 7) drain zero dots against
+        // row 0's scales and are never stored
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+          const int m = 4 * s + mm;
+          const QmfDs e = lds_ds[(m < M ? m : 0) * 8 + j];
+          const int I = C[4 * jj + mm];
+          acc[j >> 1][mm] = fma(wsc * e.d, (double)I, acc[j >> 1][mm]);
+          acc[j >> 1][mm] = fma(wmn, e.s, acc[j >> 1][mm]);
+          if (DUMP && m < M && nrow < N)
+            isums[((size_t)m * N + nrow) * (K / SUB) + (size_t)b * (QK / SUB) + j] = I;
+        }
+      }
+    }
+  };
+
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) fetch(S[d], wave + d * P);
+  const int niter = (((nsb + P - 1) / P) + DEPTH - 1) / DEPTH * DEPTH;
+  auto step = [&](Stage& st, int ii, bool refill) {
+    const int b = wave + ii * P;
+    if (b < nsb) compute(st, b);
+    if (refill) fetch(st, b + DEPTH * P);
+  };
+  int i = 0;
+  for (; i + DEPTH < niter; i += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) step(S[d], i + d, true);
+  }
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) step(S[d], i + d, false);
+
+  // quarters in qmv_tile's order ((q0 + q1) + (q2 + q3)), then the waves in order
+  double* red = reinterpret_cast<double*>(smem);
+  __syncthreads();  // the staging area is reused for the reduction
+#pragma unroll
+  for (int mm = 0; mm < 4; ++mm) {
+    const int m = 4 * s + mm;
+    if (m < M) red[(wave * QMF_ROWS + n) * M + m] = (acc[0][mm] + acc[1][mm]) + (acc[2][mm] + acc[3][mm]);
+  }
+  __syncthreads();
+  for (int o = tid; o < QMF_ROWS * M; o += 64 * P) {
+    const int m = o % M, r = o / M;
+    double v = red[r * M + m];
+    for (int w = 1; w < P; ++w) v += red[(w * QMF_ROWS + r) * M + m];
+    if (n0 + r < N) y[(size_t)m * N + n0 + r] = (float)v;
+  }
+}
+
+// LDS bytes a decode workgroup of P waves needs (either tile).
+template <int T, int M, bool GROUPED = false> constexpr size_t qmv_lds_bytes_per_wave_stage() {
+  return qmf_ok<T, M, GROUPED>() ? 64 * sizeof(QmfDs) : (size_t)8 * M * (Q8_BLOCK + sizeof(DsEntry));
+}
+template <int T, int M, bool GROUPED = false> inline size_t qmv_lds_bytes(int waves) {
+  const size_t stage = (size_t)waves * qmv_lds_bytes_per_wave_stage<T, M, GROUPED>();
+  const size_t red = (size_t)waves * qmv_tile_rows<T, M, GROUPED>() * M * sizeof(double);
+  return stage > red ? stage : red;
+}
+
 template <int T, int M, int DEPTH, bool DUMP>
 __global__ __launch_bounds__(QMV_MAX_THREADS) void qmv_kernel(
     const uint8_t* __restrict__ W, int N, int K, const uint8_t* __restrict__ xq,
     float* __restrict__ y, int32_t* __restrict__ isums) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  qmv_tile<T, M, DEPTH, DUMP>(W, N, K, xq, y, isums, blockIdx.x, smem);
+  if constexpr (qmf_ok<T, M>())
+    qmf_tile<T, M, DEPTH, DUMP>(W, N, K, xq, y, isums, blockIdx.x, smem);
+  else
+    qmv_tile<T, M, DEPTH, DUMP>(W, N, K, xq, y, isums, blockIdx.x, smem);
 }
 
 // Several matrices that share the activation (same K and M) in one launch:
@@ -503,10 +686,17 @@ __global__ __launch_bounds__(QMV_MAX_THREADS) void qmv_multi_kernel(QmvMulti a, 
   for (int j = 0; j < QMV_MULTI_MAX - 1; ++j)
     if (j < a.n - 1 && g >= a.tile_end[j]) i = j + 1;
   const int tile = g - (i > 0 ? a.tile_end[i - 1] : 0);
-  if (TA == TB || a.type[i] == TA)
-    qmv_tile<TA, M, DEPTH, false>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
-  else
-    qmv_tile<TB, M, DEPTH, false>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
+  if (TA == TB || a.type[i] == TA) {
+    if constexpr (qmf_ok<TA, M, true>())
+      qmf_tile<TA, M, DEPTH, false>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
+    else
+      qmv_tile<TA, M, DEPTH, false>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
+  } else {
+    if constexpr (qmf_ok<TB, M, true>())
+      qmf_tile<TB, M, DEPTH, false>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
+    else
+      qmv_tile<TB, M, DEPTH, false>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
+  }
 }
 
 // ------------------------------------------------ launch-shape helpers
@@ -527,6 +717,11 @@ inline int qmv_waves(int nsb) {
 // stage (12288 x 4096 Q4_K, 4096 x 12288 Q6_K) already saturates HBM with one
 // stage at M <= 4; the 9 MB matrices want all four superblocks of a wave in
 // flight; Q6_K's larger register stage is kept to two.
+// Weight rows per workgroup of the decode kernels for (type, M).
+inline int qmv_rows(int type, int M, bool grouped) {
+  return (M >= (grouped ? QMF_MIN_M_GROUPED : QMF_MIN_M) && type == Q4_K) ? QMF_ROWS : QMV_SLOTS;
+}
+
 inline long qmv_stage_bytes(int type, int N, int K) {
   const long waves = (long)((N + QMV_SLOTS - 1) / QMV_SLOTS) * qmv_waves(K / QK);
   const int bytes = type == Q6_K ? 210 : (type == IQ4_XS ? 136 : (type == Q8_0 ? 272 : 144));
@@ -540,6 +735,13 @@ inline int qmv_depth_for(long stage_bytes, int M, bool wide_stage) {
   if (wide_stage && d > 2) d = 2;
   return d;
 }
+// Prefetch depth of a launch with MFMA tiles (the stage holds a whole
+// superblock per lane): one for the 28 MB-class matrices and groups (at
+// least 4 MB in flight per stage), else two.  Measured on MI355X at M = 8:
+// gate+up 18.6 us at depth 1 against 19.9 at 2; q+k+v 9.7 us at 2 against
+// 10.7 at 1; depth 4 spills registers at M = 7.
+inline int qmf_depth(long stage_bytes) { return stage_bytes >= (4L << 20) ? 1 : 2; }
+
 inline int qmv_depth(int type, int M, int N, int K) {
   return qmv_depth_for(qmv_stage_bytes(type, N, K), M, type == Q6_K || type == Q8_0);
 }

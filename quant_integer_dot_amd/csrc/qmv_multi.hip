@@ -15,9 +15,8 @@ static_assert(QMV_MULTI_MAX == QDOT_MULTI_MAX, "group size of the C ABI");
 template <int TA, int TB, int M, int DEPTH>
 static int launch_multi_k(const QmvMulti& a, int K, const uint8_t* xq, hipStream_t s) {
   const int P = qmv_waves(K / QK);
-  const size_t stage = (size_t)P * 8 * M * (Q8_BLOCK + sizeof(DsEntry));
-  const size_t red = (size_t)P * QMV_SLOTS * M * sizeof(double);
-  const size_t lds = stage > red ? stage : red;
+  const size_t la = qmv_lds_bytes<TA, M, true>(P), lb = qmv_lds_bytes<TB, M, true>(P);
+  const size_t lds = la > lb ? la : lb;
   hipLaunchKernelGGL((qmv_multi_kernel<TA, TB, M, DEPTH>), dim3(a.tile_end[a.n - 1]), dim3(64 * P), lds,
                      s, a, K, xq);
   return hipGetLastError() == hipSuccess ? 0 : -1;
@@ -27,7 +26,7 @@ template <int TA, int TB, int M>
 static int launch_multi_d(const QmvMulti& a, int K, const uint8_t* xq, int depth, hipStream_t s) {
   constexpr bool wide = TA == Q6_K || TA == Q8_0 || TB == Q6_K || TB == Q8_0;
   if (depth == 1) return launch_multi_k<TA, TB, M, 1>(a, K, xq, s);
-  if constexpr (!wide) {
+  if constexpr (!wide && !qmf_ok<TA, M, true>() && !qmf_ok<TB, M, true>()) {
     if (depth == 4) return launch_multi_k<TA, TB, M, 4>(a, K, xq, s);
   }
   return launch_multi_k<TA, TB, M, 2>(a, K, xq, s);
@@ -60,14 +59,16 @@ static int launch_group(const int* idx, int cnt, const void* const* W, const int
     a.y[g] = y[i];
     a.N[g] = N[i];
     a.type[g] = types[i];
-    tiles += (N[i] + QMV_SLOTS - 1) / QMV_SLOTS;
+    const int rows = qmv_rows(types[i], M, true);
+    tiles += (N[i] + rows - 1) / rows;
     if (tiles > 0x7FFFFFFF / 2) return -1;
     a.tile_end[g] = tiles;
     stage += qmv_stage_bytes(types[i], N[i], K);
   }
   a.n = cnt;
   const bool wide = ta == Q6_K || ta == Q8_0 || tb == Q6_K || tb == Q8_0;
-  const int depth = qmv_depth_for(stage, M, wide);
+  const bool mfma_tile = qmv_rows(ta, M, true) == QMF_ROWS || qmv_rows(tb, M, true) == QMF_ROWS;
+  const int depth = mfma_tile ? qmf_depth(stage) : qmv_depth_for(stage, M, wide);
   const uint8_t* x8 = static_cast<const uint8_t*>(xq);
   if (ta == tb) {
     switch (ta) {

@@ -50,7 +50,9 @@ def test_sizes(lib):
 
 
 def test_names_and_status(lib):
-    assert qd.qdot_kernel_name(qd.QDOT_Q4_K, 8) == "qmv_dot4<Q4_K,8>"
+    assert qd.qdot_kernel_name(qd.QDOT_Q4_K, 8) == "qmv_mfma<Q4_K,8>"
+    assert qd.qdot_kernel_name(qd.QDOT_Q4_K, 6) == "qmv_dot4<Q4_K,6>"
+    assert qd.qdot_kernel_name(qd.QDOT_Q6_K, 8) == "qmv_dot4<Q6_K,8>"
     assert qd.qdot_kernel_name(qd.QDOT_IQ4_XS, 1) == "qmv_dot4<IQ4_XS,1>"
     assert qd.qdot_kernel_name(qd.QDOT_Q8_0, 4) == "qmv_dot4<Q8_0,4>"
     assert qd.qdot_kernel_name(qd.QDOT_Q4_0, 100) == "qmm_mfma<Q4_0>"
