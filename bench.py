@@ -77,7 +77,7 @@ def workload_def(name):
     if name == "qwen3-8b-q4_0-q8_0-decode":
         return 5, synth.QWEN3_8B_Q40_Q80, 36, [1, 2, 4, 8]
     if name == "qwen3-8b-mid-batch":
-        return 6, synth.QWEN3_8B, 36, [16, 32, 64]
+        return 6, synth.QWEN3_8B, 36, [16, 32, 64, 96]
     raise ValueError(name)
 
 

@@ -112,9 +112,9 @@ int qdot_quantize_q8_1(const float *x, int64_t M, int64_t K, void *x_q8,
  * scale product is exact and accumulated in fp64; y is rounded once to fp32.
  * M <= 8 runs the decode kernel (v_dot4_i32_i8, M-row tile; for Q4_K at
  * M = 7, 8 the integer dots run on v_mfma_i32_32x32x32_i8 instead, summed in
- * the same order, so the rows are bitwise those of the dot4 tile); 8 < M <= 64 a
+ * the same order, so the rows are bitwise those of the dot4 tile); 8 < M <= 96 a
  * mid-batch MFMA i8 kernel (16-row activation tiles, K split eight ways);
- * M > 64 the MFMA i8 prefill kernel.  Within each of these three ranges a row
+ * M > 96 the MFMA i8 prefill kernel.  Within each of these three ranges a row
  * of y is bitwise the same whatever M it is computed with; across them it may
  * differ in the last fp32 bit (different fp64 summation orders).  K % 256 == 0
  * is required. */

@@ -45,12 +45,13 @@ int check_dims(int type, int64_t N, int64_t K, int64_t M) {
 // prefill kernel (64 or 32 activation rows per tile).  Measured on MI355X at
 // the Qwen3-8B shapes the mid-batch kernel beats running the decode kernel
 // over 8-row chunks at every M from 9 to 32 (4096 x 4096, M = 16: 11.8 vs
-// 15.8 us) and the prefill kernel up to M = 48 on every shape; at M = 64 it
-// is 2x faster on 4096 x 4096, 4096 x 12288 and 1024 x 4096 and 15 % slower
-// on 12288 x 4096 (a whole layer: 270 vs 437 us).  The choice depends on M
-// only, so the kernel a call runs is known from (type, M).
+// 15.8 us) and the prefill kernel up to M = 48 on every shape; over a whole
+// layer it is faster up to M = 96 (M = 64: 270 vs 437 us; M = 96: 391 vs
+// 476 us; M = 128: equal), though 12288 x 4096 alone prefers the prefill
+// kernel from M = 56.  The choice depends on M only, so the kernel a call
+// runs is known from (type, M).
 #ifndef QDOT_SKINNY_MAX_M
-#define QDOT_SKINNY_MAX_M 64
+#define QDOT_SKINNY_MAX_M 96
 #endif
 
 int run_qmatmul(const void* W, int type, int64_t N, int64_t K, const void* x_q8, int64_t M,

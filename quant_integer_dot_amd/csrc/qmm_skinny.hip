@@ -1,4 +1,4 @@
-// qmm_skinny.hip -- mid-batch matmul (9 <= M <= 64 activation rows) on the
+// qmm_skinny.hip -- mid-batch matmul (9 <= M <= 96 activation rows) on the
 // int8 matrix cores: v_mfma_i32_16x16x32_i8, sixteen activation rows per tile.
 //
 // Same arithmetic as the other kernels: exact int32 block dots of the raw

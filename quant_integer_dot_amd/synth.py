@@ -54,7 +54,7 @@ WORKLOADS = {
     3: dict(name="iq4xs-h5120-decode", shapes=IQ4XS_H5120, layers=64, Ms=list(range(1, 9))),
     4: dict(name="qwen3-8b-prefill-512", shapes=QWEN3_8B, layers=36, Ms=[512]),
     5: dict(name="qwen3-8b-q4_0-q8_0-decode", shapes=QWEN3_8B_Q40_Q80, layers=36, Ms=[1, 2, 4, 8]),
-    6: dict(name="qwen3-8b-mid-batch", shapes=QWEN3_8B, layers=36, Ms=[16, 32, 64]),
+    6: dict(name="qwen3-8b-mid-batch", shapes=QWEN3_8B, layers=36, Ms=[16, 32, 64, 96]),
 }
 
 

@@ -59,8 +59,8 @@ def test_names_and_status(lib):
     assert qd.qdot_kernel_name(qd.QDOT_Q8_0, 16) == "qmm_skinny<Q8_0>"
     assert qd.qdot_kernel_name(qd.QDOT_Q6_K, 512) == "qmm_mfma<Q6_K>"
     assert qd.qdot_kernel_name(qd.QDOT_Q4_K, 9) == "qmm_skinny<Q4_K>"
-    assert qd.qdot_kernel_name(qd.QDOT_IQ4_XS, 64) == "qmm_skinny<IQ4_XS>"
-    assert qd.qdot_kernel_name(qd.QDOT_Q4_K, 65) == "qmm_mfma<Q4_K>"
+    assert qd.qdot_kernel_name(qd.QDOT_IQ4_XS, 96) == "qmm_skinny<IQ4_XS>"
+    assert qd.qdot_kernel_name(qd.QDOT_Q4_K, 97) == "qmm_mfma<Q4_K>"
     assert qd.qdot_kernel_name(9, 1) == "invalid"
     assert qd.qdot_status_str(qd.QDOT_E_ALIGN) == "misaligned pointer"
     assert "gfx950" in qd.qdot_build_id()
