@@ -58,6 +58,8 @@ def lib():
         L.oracle_qmatmul.restype = ctypes.c_int
         L.oracle_qmatmul_rows.argtypes = [P, ctypes.c_int, i64, i64, P, i64, P, i64, P, P]
         L.oracle_qmatmul_rows.restype = ctypes.c_int
+        L.oracle_rmsnorm.argtypes = [P, P, ctypes.c_float, i64, i64, P, P]
+        L.oracle_rmsnorm.restype = None
         L.oracle_codebook.argtypes = []
         L.oracle_codebook.restype = ctypes.POINTER(ctypes.c_int)
         _lib = L
@@ -96,6 +98,26 @@ def quantize_q8_1(x):
     out = np.empty((M, K // 32 * 36), dtype=np.uint8)
     lib().oracle_quantize_q8_1(_ptr(x), M, K, _ptr(out))
     return out
+
+
+def rmsnorm(x, w, eps):
+    """RMSNorm of each row of fp32 [M][K] with weight w[K] (oracle.c,
+    oracle_rmsnorm: Kestrel 3.6 numerics, fixed sum-of-squares tree);
+    returns (xn fp32 [M][K], ss fp32 [M])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    M, K = x.shape
+    assert K % 32 == 0 and w.shape == (K,)
+    xn = np.empty((M, K), dtype=np.float32)
+    ss = np.empty(M, dtype=np.float32)
+    lib().oracle_rmsnorm(_ptr(x), _ptr(w), float(eps), M, K, _ptr(xn), _ptr(ss))
+    return xn, ss
+
+
+def rmsnorm_quantize_q8_1(x, w, eps):
+    """The fused producer's output: Q8_1 blocks of RMSNorm(x) * w."""
+    xn, _ = rmsnorm(x, w, eps)
+    return quantize_q8_1(xn)
 
 
 def dequant_q8_1(xq, M, K):

@@ -151,6 +151,60 @@ void oracle_quantize_q8_1(const float *x, int64_t M, int64_t K, uint8_t *out) {
   }
 }
 
+/* RMSNorm of each row (the producer of the Q8_1 activations of the Q/K/V and
+ * gate/up projections: the xLLM engine quantizes the normalized input into
+ * one shared buffer, d_xn_q8, section C.1; Kestrel_VLLM #18 section 3.6
+ * gives the RMSNorm numerics it matches against the CPU).
+ * Numerics as Kestrel 3.6: fp32 throughout, r = 1.0f / sqrtf(ss / K + eps)
+ * (correctly rounded division and square root, not an rsqrt approximation),
+ * out_i = (x_i * r) * w_i.
+ * Reading (the order of the sum of squares): Kestrel sums each group of 8
+ * squares as (lo0 + lo1) + (lo2 + lo3) with lo_k = s_k + s_{k+4}; here every
+ * 8-group is summed that way, the four groups of each 32-element block
+ * pairwise, (t0 + t1) + (t2 + t3), and the block sums of a row in a pairwise
+ * tree (zero-padded to a power of two: level by level u_i = u_2i + u_2i+1).
+ * Every operation is a single fp32 operation; nothing is fused.
+ * xn is [M][K] fp32; ss[m] receives the row's sum of squares. */
+void oracle_rmsnorm(const float *x, const float *w, float eps, int64_t M, int64_t K, float *xn,
+                    float *ss) {
+  int64_t nblk = K / OR_Q8_BLOCK;
+  int64_t p2 = 1;
+  while (p2 < nblk) p2 *= 2;
+  float *u = (float *)calloc((size_t)p2, sizeof(float));
+  for (int64_t m = 0; m < M; ++m) {
+    const float *xr = x + m * K;
+    for (int64_t i = 0; i < p2; ++i) u[i] = 0.0f;
+    for (int64_t b = 0; b < nblk; ++b) {
+      float t[4];
+      for (int g = 0; g < 4; ++g) {
+        const float *e = xr + b * OR_Q8_BLOCK + 8 * g;
+        float lo[4];
+        for (int k = 0; k < 4; ++k) {
+          float s0 = e[k] * e[k];
+          float s1 = e[k + 4] * e[k + 4];
+          lo[k] = s0 + s1;
+        }
+        float s01 = lo[0] + lo[1];
+        float s23 = lo[2] + lo[3];
+        t[g] = s01 + s23;
+      }
+      float t01 = t[0] + t[1];
+      float t23 = t[2] + t[3];
+      u[b] = t01 + t23;
+    }
+    for (int64_t len = p2; len > 1; len /= 2)
+      for (int64_t i = 0; i < len / 2; ++i) u[i] = u[2 * i] + u[2 * i + 1];
+    float mean = u[0] / (float)K;
+    float r = 1.0f / sqrtf(mean + eps);
+    ss[m] = u[0];
+    for (int64_t k = 0; k < K; ++k) {
+      float a = xr[k] * r;
+      xn[m * K + k] = a * w[k];
+    }
+  }
+  free(u);
+}
+
 /* Exact dequantization of Q8_1 blocks: xhat[m][k] = D * q. */
 void oracle_dequant_q8_1(const uint8_t *xq, int64_t M, int64_t K, double *xhat) {
   int64_t nblk = K / OR_Q8_BLOCK;

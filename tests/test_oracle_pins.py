@@ -12,6 +12,10 @@
   one-hot closed form and the special cases.
 - the pages' statistical anchor: about 0.5 % RMS against fp32 SGEMV with the
   argmax kept (golden fixture with its citation).
+- RMSNorm (the fused producer of the Q8_1 activations): a closed form on
+  constant rows, exact power-of-two scale invariances, the fp64 formula within
+  the fp32 error bound, and the stated summation tree on an input where
+  another order gives another fp32 sum.
 """
 import json
 import os
@@ -334,3 +338,78 @@ def test_activation_quantization_noise_matches_pages(oracle_lib, wtype):
         gap = ref[m, top[0]] - ref[m, top[1]]
         if gap > 6 * rel * np.sqrt(np.mean(ref[m] ** 2)):
             assert int(np.argmax(y64[m])) == int(top[0])
+
+
+# ------------------------------------------------ RMSNorm (fused producer)
+# Pins of oracle.rmsnorm: a closed form, exact scale invariances, the fp64
+# textbook formula within the fp32 error bound, and the stated summation
+# tree on an input where a different order gives a different fp32 sum.
+def test_rmsnorm_constant_row_is_exactly_unit(oracle_lib):
+    """x = c (a power of two), w = 1, eps = 0: mean = c^2, r = 1/|c| exactly,
+    so every output is +-1 and the quantized block is the closed form."""
+    K = 512
+    for c in (2.0 ** -3, -4.0, 1.0):
+        x = np.full((1, K), c, np.float32)
+        xn, ss = oracle_lib.rmsnorm(x, np.ones(K, np.float32), 0.0)
+        assert ss[0] == np.float32(K * c * c)
+        assert np.all(xn == np.float32(np.sign(c)))
+        xq = oracle_lib.rmsnorm_quantize_q8_1(x, np.ones(K, np.float32), 0.0).reshape(K // 32, 36)
+        d32 = np.float32(1.0) / np.float32(127.0)
+        assert np.all(xq[:, 4:].view(np.int8) == int(np.sign(c)) * 127)
+        D = np.float16(d32)
+        assert np.all(xq[:, 0:2].copy().view(np.float16) == D)
+
+
+def test_rmsnorm_power_of_two_scale_invariance(oracle_lib):
+    """Scaling x by 4 scales every square and sum by 16 and r by 1/4 exactly
+    (eps = 0), so outputs and bytes are identical; scaling w by 2 doubles
+    every output exactly."""
+    rng = np.random.default_rng(11)
+    M, K = 3, 1536
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    w = (1.0 + 0.1 * rng.standard_normal(K)).astype(np.float32)
+    xn, _ = oracle_lib.rmsnorm(x, w, 0.0)
+    xn4, _ = oracle_lib.rmsnorm(4 * x, w, 0.0)
+    assert np.array_equal(xn.view(np.uint32), xn4.view(np.uint32))
+    xn2, _ = oracle_lib.rmsnorm(x, 2 * w, 0.0)
+    assert np.array_equal((2 * xn).view(np.uint32), xn2.view(np.uint32))
+    assert np.array_equal(oracle_lib.rmsnorm_quantize_q8_1(x, w, 0.0),
+                          oracle_lib.rmsnorm_quantize_q8_1(4 * x, w, 0.0))
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-6, 0.5])
+def test_rmsnorm_matches_fp64_formula(oracle_lib, eps):
+    """Against x / sqrt(mean(x^2) + eps) * w in fp64: a handful of fp32
+    roundings, so within 8 units of 2^-24 relative (catches a missing 1/K,
+    eps outside the root, an rsqrt-style approximation, a dropped weight)."""
+    rng = np.random.default_rng(12)
+    M, K = 4, 4096
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    w = rng.uniform(0.5, 1.5, K).astype(np.float32)
+    xn, ss = oracle_lib.rmsnorm(x, w, eps)
+    x64 = x.astype(np.float64)
+    ref = x64 / np.sqrt((x64 ** 2).mean(axis=1, keepdims=True) + eps) * w.astype(np.float64)
+    assert np.all(np.abs(xn - ref) <= 8 * 2.0 ** -24 * np.abs(ref) + 1e-30)
+    assert np.allclose(ss, (x64 ** 2).sum(axis=1), rtol=1e-6)
+
+
+def test_rmsnorm_sum_of_squares_order(oracle_lib):
+    """x = [2^12, 1, 1, ...] over K = 64: the 8-group sums give
+    (2^24 + 2) + 4 = 2^24 + 6 for the first group and 8 for the others, the
+    blocks (2^24 + 6 + 8) + 16 = 2^24 + 30 and 32, the tree 2^24 + 62; a
+    left-to-right fp32 sum stays at 2^24 (each +1 on 2^24 rounds back)."""
+    K = 64
+    x = np.ones((1, K), np.float32)
+    x[0, 0] = 2.0 ** 12
+    _, ss = oracle_lib.rmsnorm(x, np.ones(K, np.float32), 0.0)
+    assert ss[0] == np.float32(2.0 ** 24 + 62)
+    seq = np.float32(0)
+    for v in (x[0].astype(np.float32) ** 2):
+        seq = np.float32(seq + v)
+    assert seq != ss[0]
+
+
+def test_rmsnorm_zero_row_quantizes_to_zero(oracle_lib):
+    K = 256
+    xq = oracle_lib.rmsnorm_quantize_q8_1(np.zeros((2, K), np.float32), np.ones(K, np.float32), 1e-6)
+    assert not xq.any()
