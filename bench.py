@@ -47,7 +47,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="qwen3-8b-decode",
                    choices=["qwen3-8b-decode", "qwen3-8b-prefill-512", "iq4xs-h5120-decode",
-                            "qwen2.5-1.5b-decode", "qwen3-8b-q4_0-q8_0-decode", "qwen3-8b-mid-batch"])
+                            "qwen2.5-1.5b-decode", "qwen3-8b-q4_0-q8_0-decode", "qwen3-8b-mid-batch",
+                            "qwen3-8b-rmsnorm-q8_1"])
     p.add_argument("--ms", default=None, help="comma-separated M values (default per workload)")
     p.add_argument("--layers", type=int, default=None, help="override the layer count")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -180,6 +181,112 @@ def cpu_baseline(shapes, cfg_idx, Ms, budget_s=20.0, prefill=False):
                       f"quantize + qmatmul per projection; CPU: {cpu})"}
 
 
+def producer_bench(args):
+    """The fused RMSNorm + Q8_1 producer at the Qwen3-8B hidden size (K = 4096):
+    one step = 36 layers x 2 norms (attention and FFN input) for each M in
+    1, 2, 4, 8, captured in HIP graphs like the matmul step; the standalone
+    quantizer on the same rows is timed beside it.  Bytes per launch: x read
+    (4MK), w read (4K), Q8_1 written (36MK/32)."""
+    import numpy as np
+    import torch
+    from quant_integer_dot_amd import binding as qd
+    from quant_integer_dot_amd import synth
+    L = qd.load()
+    dev = torch.device("cuda:0")
+    K, layers, Ms = 4096, 36, [int(v) for v in args.ms.split(",")] if args.ms else [1, 2, 4, 8]
+    if args.layers:
+        layers = args.layers
+    n = 2 * layers
+    bufs = {}
+    for M in Ms:
+        xs = [torch.from_numpy(synth.activations(M, K, (2026, 90, M, i))).to(dev) for i in range(n)]
+        ws = [torch.from_numpy((1.0 + 0.1 * synth.activations(1, K, (2026, 91, i))[0]).astype(np.float32)).to(dev)
+              for i in range(n)]
+        qs = [torch.empty(qd.qdot_q8_1_bytes(M, K), dtype=torch.uint8, device=dev) for _ in range(n)]
+        bufs[M] = (xs, ws, qs)
+
+    def sweep(M, fused):
+        s = torch.cuda.current_stream(dev).cuda_stream
+        xs, ws, qs = bufs[M]
+        for i in range(n):
+            if fused:
+                rc = L.qdot_rmsnorm_quantize_q8_1(xs[i].data_ptr(), ws[i].data_ptr(), ctypes.c_float(1e-6), M, K,
+                                                  qs[i].data_ptr(), s)
+            else:
+                rc = L.qdot_quantize_q8_1(xs[i].data_ptr(), M, K, qs[i].data_ptr(), s)
+            assert rc == 0, rc
+
+    def timed(fused):
+        graphs = {}
+        for M in Ms:
+            sweep(M, fused)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                sweep(M, fused)
+            graphs[M] = g
+        for _ in range(args.warmup):
+            for M in Ms:
+                graphs[M].replay()
+        torch.cuda.synchronize()
+        per = {}
+        for M in Ms:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(args.steps):
+                graphs[M].replay()
+            b.record()
+            torch.cuda.synchronize()
+            per[M] = a.elapsed_time(b) / args.steps
+        return per
+
+    fused = timed(True)
+    quant = timed(False)
+    # sampled check: last launch of each M against the oracle
+    check = None
+    if not args.no_check:
+        import oracle
+        bad = 0
+        for M in Ms:
+            xs, ws, qs = bufs[M]
+            sweep(M, True)
+            torch.cuda.synchronize()
+            exp = oracle.rmsnorm_quantize_q8_1(xs[-1].cpu().numpy(), ws[-1].cpu().numpy(), np.float32(1e-6))
+            bad += int((qs[-1].cpu().numpy() != exp.reshape(-1)).sum())
+        check = {"bytes_differing": bad}
+    ms_step = sum(fused.values())
+    byt = {M: 4 * M * K + 4 * K + qd.qdot_q8_1_bytes(M, K) for M in Ms}
+    total = sum(byt[M] * n for M in Ms)
+    per_launch_us = ms_step * 1e3 / (n * len(Ms))
+    achieved = total / (ms_step * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 10.0:
+            for M in Ms:
+                xs, ws, _ = bufs[M]
+                oracle.rmsnorm_quantize_q8_1(xs[0].cpu().numpy(), ws[0].cpu().numpy(), np.float32(1e-6))
+            reps += 1
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(reps * sum(byt.values()) / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle", "sample": f"{reps} passes over one launch per M ({dt:.1f} s, single thread)"}
+    print(json.dumps({
+        "metric": "GB/s (x and w read, Q8_1 written) of the fused RMSNorm + Q8_1 producer, Qwen3-8B hidden 4096",
+        "value": round(achieved, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "K": K, "layers": layers, "M": Ms, "launches_per_step": n * len(Ms)},
+        "roofline": {"bound": "hbm", "kernel": "rmsnorm_q8_1_kernel", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
+                     "traffic": recorded_traffic("rmsnorm_q8_1_kernel", args.workload),
+                     "launches": n * len(Ms), "avg_launch_us": round(per_launch_us, 3),
+                     "algorithmic_bytes_per_launch": round(total / (n * len(Ms)))},
+        "per_M_us": {str(M): {"fused_rmsnorm_q8_1": round(fused[M] * 1e3 / n, 3),
+                              "quantize_q8_1_alone": round(quant[M] * 1e3 / n, 3)} for M in Ms},
+        "cpu_baseline": cpu, "sampled_check": check}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -188,6 +295,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
+        return
+    if args.workload == "qwen3-8b-rmsnorm-q8_1":
+        producer_bench(args)
         return
 
     import numpy as np

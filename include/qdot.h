@@ -149,6 +149,23 @@ int qdot_qmatmul_multi(int n, const void *const *W, const int *types,
                        const int64_t *N, int64_t K, const void *x_q8,
                        int64_t M, float *const *y, void *stream);
 
+/* RMSNorm fused with the Q8_1 quantizer: x_q8 = quantize_q8_1(RMSNorm(x) * w)
+ * in one launch, for the producer of the Q/K/V and gate/up activations (the
+ * xLLM v0.7 log, section C.1, quantizes the normalized input into one shared
+ * buffer).  Per row of x [M][K] (fp32, device): ss = sum of x_k^2, r =
+ * 1.0f / sqrtf(ss / K + eps), xn_k = (x_k * r) * w_k, all in fp32 with
+ * correctly rounded division and square root as on the Kestrel_VLLM #18
+ * page (section 3.6); ss is summed in a fixed order (each group of 8 squares
+ * as on that page, the four groups of a 32-element block pairwise, the blocks
+ * in a pairwise tree), so the output bytes are reproducible bit for bit.  xn
+ * is then quantized exactly as qdot_quantize_q8_1 does.  w is fp32 [K]
+ * (device); x_q8 receives qdot_q8_1_bytes(M, K) bytes.  32 <= K <=
+ * QDOT_RMSNORM_MAX_K, K % 32 == 0, eps finite and >= 0, else E_ARG; x, w,
+ * x_q8 4-byte aligned, else E_ALIGN. */
+#define QDOT_RMSNORM_MAX_K 32768
+int qdot_rmsnorm_quantize_q8_1(const float *x, const float *w, float eps,
+                               int64_t M, int64_t K, void *x_q8, void *stream);
+
 /* Static text for a status code. */
 const char *qdot_status_str(int status);
 

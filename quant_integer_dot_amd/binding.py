@@ -56,6 +56,8 @@ def load():
     L.qdot_qmatmul_multi.argtypes = [i32, ctypes.POINTER(P), ctypes.POINTER(i32), ctypes.POINTER(i64),
                                      i64, P, i64, ctypes.POINTER(P), P]
     L.qdot_qmatmul_multi.restype = i32
+    L.qdot_rmsnorm_quantize_q8_1.argtypes = [P, P, ctypes.c_float, i64, i64, P, P]
+    L.qdot_rmsnorm_quantize_q8_1.restype = i32
     L.qdot_status_str.argtypes = [i32]
     L.qdot_status_str.restype = ctypes.c_char_p
     L.qdot_kernel_name.argtypes = [i32, i64]
@@ -111,6 +113,12 @@ def qdot_isum_count(wtype, N, K, M):
 def qdot_quantize_q8_1(x, M, K, x_q8, stream=None):
     s = _stream(stream, x, x_q8)
     _check(load().qdot_quantize_q8_1(_addr(x), M, K, _addr(x_q8), s), "qdot_quantize_q8_1")
+
+
+def qdot_rmsnorm_quantize_q8_1(x, w, eps, M, K, x_q8, stream=None):
+    s = _stream(stream, x, w, x_q8)
+    _check(load().qdot_rmsnorm_quantize_q8_1(_addr(x), _addr(w), float(eps), M, K, _addr(x_q8), s),
+           "qdot_rmsnorm_quantize_q8_1")
 
 
 def qdot_qmatmul(W, wtype, N, K, x_q8, M, y, stream=None):

@@ -11,6 +11,8 @@
 
 namespace qdot {
 int launch_quantize_q8_1(const float* x, int64_t M, int64_t K, void* xq, hipStream_t s);
+int launch_rmsnorm_q8_1(const float* x, const float* w, float eps, int64_t M, int64_t K, void* xq,
+                        hipStream_t s);
 int launch_qmv(const void* W, int type, int N, int K, const void* xq, int M, float* y,
                int32_t* isums, hipStream_t s);
 int launch_qmm(const void* W, int type, int N, int K, const void* xq, int M, float* y,
@@ -108,6 +110,16 @@ int qdot_quantize_q8_1(const float* x, int64_t M, int64_t K, void* x_q8, void* s
   if ((double)M * (double)K > 4.0e18) return QDOT_E_ARG;
   if (!aligned4(x) || !aligned4(x_q8)) return QDOT_E_ALIGN;
   int rc = qdot::launch_quantize_q8_1(x, M, K, x_q8, static_cast<hipStream_t>(stream));
+  return rc == 0 ? QDOT_OK : QDOT_E_HIP;
+}
+
+int qdot_rmsnorm_quantize_q8_1(const float* x, const float* w, float eps, int64_t M, int64_t K,
+                               void* x_q8, void* stream) {
+  if (!x || !w || !x_q8) return QDOT_E_ARG;
+  if (M < 1 || M > kMaxDim || K < 32 || K % 32 != 0 || K > QDOT_RMSNORM_MAX_K) return QDOT_E_ARG;
+  if (!(eps >= 0.0f) || eps > 3.4e38f) return QDOT_E_ARG;  // also rejects NaN
+  if (!aligned4(x) || !aligned4(w) || !aligned4(x_q8)) return QDOT_E_ALIGN;
+  int rc = qdot::launch_rmsnorm_q8_1(x, w, eps, M, K, x_q8, static_cast<hipStream_t>(stream));
   return rc == 0 ? QDOT_OK : QDOT_E_HIP;
 }
 

@@ -55,6 +55,17 @@ __device__ __forceinline__ float h2f(uint32_t bits16) {
   return __half2float(__ushort_as_half((unsigned short)(bits16 & 0xFFFFu)));
 }
 
+// binary16 bits of S = D * sumq for a Q8_1 block.  The product is exact in
+// fp32 (11 + 12 significant bits), so S takes one rounding.  A zero product
+// keeps its IEEE sign (D = +0 with a negative sum gives -0): the compiler
+// would otherwise fold the multiply and the conversion into a mixed-precision
+// FMA with a +0 addend, which turns -0 into +0.
+__device__ __forceinline__ uint32_t q8_1_s_bits(__half dh, int sumq) {
+  const float p = __half2float(dh) * (float)sumq;
+  if (p == 0.0f) return (__float_as_uint(p) >> 16) & 0x8000u;
+  return __half_as_ushort(__float2half_rn(p));
+}
+
 // Integer dot of four int8 pairs, accumulated (v_dot4_i32_i8).
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
   return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);

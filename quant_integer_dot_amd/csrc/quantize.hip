@@ -56,10 +56,8 @@ __global__ __launch_bounds__(256) void quantize_q8_1_kernel(
   uint8_t* ob = out + blk * Q8_BYTES;
   *reinterpret_cast<uint32_t*>(ob + 4 + 4 * part) = packed;
   if (part == 0) {
-    __half dh = __float2half_rn(d32);
-    // D * sum(q) is exact in fp32 (11 + 12 significant bits): one rounding.
-    __half sh = __float2half_rn(__half2float(dh) * (float)sumq);
-    uint32_t ds = (uint32_t)__half_as_ushort(dh) | ((uint32_t)__half_as_ushort(sh) << 16);
+    const __half dh = __float2half_rn(d32);
+    const uint32_t ds = (uint32_t)__half_as_ushort(dh) | (q8_1_s_bits(dh, sumq) << 16);
     *reinterpret_cast<uint32_t*>(ob) = ds;
   }
 }

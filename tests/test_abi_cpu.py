@@ -151,3 +151,20 @@ def test_qmatmul_multi_validation(lib, case, status):
 def test_binding_multi_lengths(lib):
     with pytest.raises(ValueError):
         qd.qdot_qmatmul_multi([16, 16], [1], [16, 16], 256, 16, 1, [16, 16], stream=0)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 16, 1e-6, 1, 256, 16), qd.QDOT_E_ARG),
+    ((16, 0, 1e-6, 1, 256, 16), qd.QDOT_E_ARG),
+    ((16, 16, 1e-6, 1, 256, 0), qd.QDOT_E_ARG),
+    ((16, 16, 1e-6, 0, 256, 16), qd.QDOT_E_ARG),
+    ((16, 16, 1e-6, 1, 100, 16), qd.QDOT_E_ARG),
+    ((16, 16, 1e-6, 1, 65536, 16), qd.QDOT_E_ARG),
+    ((16, 16, -1.0, 1, 256, 16), qd.QDOT_E_ARG),
+    ((16, 16, float("nan"), 1, 256, 16), qd.QDOT_E_ARG),
+    ((18, 16, 1e-6, 1, 256, 16), qd.QDOT_E_ALIGN),
+    ((16, 16, 1e-6, 1, 256, 18), qd.QDOT_E_ALIGN),
+])
+def test_rmsnorm_quantize_validation(lib, args, status):
+    x, w, eps, M, K, xq = args
+    assert lib.qdot_rmsnorm_quantize_q8_1(x, w, eps, M, K, xq, None) == status

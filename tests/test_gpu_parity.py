@@ -47,6 +47,8 @@ def test_quantizer_edge_values():
     x[3, 96:128] = -np.abs(x[3, 96:128])                  # all negative
     x[3, 128:160] = np.float32(1e-38)                     # fp32-subnormal-ish inputs
     x[3, 160:192] = np.float32(200.0) * np.sign(x[3, 160:192])
+    x[3, 192:224] = -np.abs(x[3, 192:224]) * np.float32(1e-12)  # D = +0, sum(q) < 0: S = -0
+    x[3, 224:256] = np.abs(x[3, 224:256]) * np.float32(1e-12)   # D = +0, sum(q) > 0: S = +0
     _, got = quantize(x)
     assert np.array_equal(got, oracle.quantize_q8_1(x).reshape(-1))
 
