@@ -432,16 +432,11 @@ __global__ __launch_bounds__(64 * QMM_WAVES) void qmm_mfma_kernel(
 // beat one and four for N > 2048; four slices win for N <= 2048, where the
 // grid is otherwise too small to fill 256 CUs.
 inline int qmm_ksplit(int N, int K) {
-#ifdef QMM_FORCE_KP
-  (void)N; (void)K;
-  return QMM_FORCE_KP;
-#else
   const int n_tiles = (N + QMM_BN - 1) / QMM_BN;
   const int nsb = K / QK;
   int kp = n_tiles <= 32 ? 4 : 2;
   while (kp > nsb) kp >>= 1;
   return kp;
-#endif
 }
 
 template <int T, int KP, bool DUMP>

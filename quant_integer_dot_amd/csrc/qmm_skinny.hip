@@ -410,14 +410,11 @@ static int launch_skinny_t(const uint8_t* W, int N, int K, const uint8_t* xq, in
 // 7168 x 5120 and 5120 x 17408 at M = 16 (224 and 160) run 1.1-1.2x faster
 // with two, as does every shape with 256 or more.  The choice changes no
 // summation order.
-#ifndef QDOT_SKINNY_NT
-#define QDOT_SKINNY_NT 0
-#endif
 template <int T, bool DUMP>
 static int launch_skinny_n(const uint8_t* W, int N, int K, const uint8_t* xq, int M, float* y,
                            int32_t* isums, hipStream_t s) {
   const long m_tiles = (M + SK_BM - 1) / SK_BM;
-  const bool two = QDOT_SKINNY_NT ? QDOT_SKINNY_NT == 2 : m_tiles * ((N + 31) / 32) >= 144;
+  const bool two = m_tiles * ((N + 31) / 32) >= 144;
   if (two) return launch_skinny_t<T, 2, DUMP>(W, N, K, xq, M, y, isums, s);
   return launch_skinny_t<T, 1, DUMP>(W, N, K, xq, M, y, isums, s);
 }

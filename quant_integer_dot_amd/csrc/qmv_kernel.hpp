@@ -496,18 +496,17 @@ typedef int qmf_v4i __attribute__((ext_vector_type(4)));
 typedef int qmf_v16i __attribute__((ext_vector_type(16)));
 
 constexpr int QMF_ROWS = 32;  // weight rows per workgroup
-// Smallest M that runs the MFMA tile, measured on MI355X (Qwen3-8B shapes):
-// alone, a 4096 x 4096 launch is faster on the dot4 tile up to M = 6 (its
-// 128 MFMA workgroups are too few), while the grouped launches (q+k+v,
-// gate+up: 2-3x the workgroups) gain 7-12 % per sweep already at M = 5, 6.
+// Which Q4_K launches take the MFMA tile (measured on MI355X, Qwen3-8B
+// shapes).  Alone (qdot_qmatmul): M >= 7 -- a 4096 x 4096 launch is faster
+// on the dot4 tile up to M = 6, its 128 MFMA workgroups being too few.  In a
+// grouped launch (qdot_qmatmul_multi) the launcher decides per launch (MF):
+// q+k+v (K = 4096) is faster on MFMA tiles at every M (M = 1: 7.2 vs 7.9 us,
+// M = 4: 8.1 vs 9.9), gate+up from M = 3; at K = 1536 (Qwen2.5-1.5B) the dot4
+// tile stays faster.  Either tile gives bitwise the same rows.
 constexpr int QMF_MIN_M = 7;
-constexpr int QMF_MIN_M_GROUPED = 5;
-template <int T, int M, bool GROUPED = false> constexpr bool qmf_ok() {
-  return M >= (GROUPED ? QMF_MIN_M_GROUPED : QMF_MIN_M) && T == Q4_K;
-}
-template <int T, int M, bool GROUPED = false> constexpr int qmv_tile_rows() {
-  return qmf_ok<T, M, GROUPED>() ? QMF_ROWS : QMV_SLOTS;
-}
+template <int T, int M> constexpr bool qmf_ok() { return M >= QMF_MIN_M && T == Q4_K; }
+template <int T, int M, bool MF> constexpr bool qmf_group_ok() { return MF && T == Q4_K; }
+template <int T, int M> constexpr int qmv_tile_rows() { return qmf_ok<T, M>() ? QMF_ROWS : QMV_SLOTS; }
 
 struct __attribute__((aligned(16))) QmfDs { double d, s; };  // fp64 D and S of one Q8_1 block
 
@@ -641,13 +640,15 @@ __device__ __forceinline__ void qmf_tile(const uint8_t* __restrict__ W, int N, i
 }
 
 // LDS bytes a decode workgroup of P waves needs (either tile).
-template <int T, int M, bool GROUPED = false> constexpr size_t qmv_lds_bytes_per_wave_stage() {
-  return qmf_ok<T, M, GROUPED>() ? 64 * sizeof(QmfDs) : (size_t)8 * M * (Q8_BLOCK + sizeof(DsEntry));
-}
-template <int T, int M, bool GROUPED = false> inline size_t qmv_lds_bytes(int waves) {
-  const size_t stage = (size_t)waves * qmv_lds_bytes_per_wave_stage<T, M, GROUPED>();
-  const size_t red = (size_t)waves * qmv_tile_rows<T, M, GROUPED>() * M * sizeof(double);
+// LDS bytes of a workgroup of `waves` waves running the MFMA tile (mfma) or
+// the dot4 tile.
+template <int M> inline size_t qmv_lds_bytes_tile(bool mfma, int waves) {
+  const size_t stage = (size_t)waves * (mfma ? 64 * sizeof(QmfDs) : (size_t)8 * M * (Q8_BLOCK + sizeof(DsEntry)));
+  const size_t red = (size_t)waves * (mfma ? QMF_ROWS : QMV_SLOTS) * M * sizeof(double);
   return stage > red ? stage : red;
+}
+template <int T, int M> inline size_t qmv_lds_bytes(int waves) {
+  return qmv_lds_bytes_tile<M>(qmf_ok<T, M>(), waves);
 }
 
 template <int T, int M, int DEPTH, bool DUMP>
@@ -676,7 +677,7 @@ struct QmvMulti {
   int n;
 };
 
-template <int TA, int TB, int M, int DEPTH>
+template <int TA, int TB, int M, int DEPTH, bool MF>
 __global__ __launch_bounds__(QMV_MAX_THREADS) void qmv_multi_kernel(QmvMulti a, int K,
                                                                     const uint8_t* __restrict__ xq) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -687,12 +688,12 @@ __global__ __launch_bounds__(QMV_MAX_THREADS) void qmv_multi_kernel(QmvMulti a, 
     if (j < a.n - 1 && g >= a.tile_end[j]) i = j + 1;
   const int tile = g - (i > 0 ? a.tile_end[i - 1] : 0);
   if (TA == TB || a.type[i] == TA) {
-    if constexpr (qmf_ok<TA, M, true>())
+    if constexpr (qmf_group_ok<TA, M, MF>())
       qmf_tile<TA, M, DEPTH, false>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
     else
       qmv_tile<TA, M, DEPTH, false>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
   } else {
-    if constexpr (qmf_ok<TB, M, true>())
+    if constexpr (qmf_group_ok<TB, M, MF>())
       qmf_tile<TB, M, DEPTH, false>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
     else
       qmv_tile<TB, M, DEPTH, false>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
@@ -718,9 +719,7 @@ inline int qmv_waves(int nsb) {
 // stage at M <= 4; the 9 MB matrices want all four superblocks of a wave in
 // flight; Q6_K's larger register stage is kept to two.
 // Weight rows per workgroup of the decode kernels for (type, M).
-inline int qmv_rows(int type, int M, bool grouped) {
-  return (M >= (grouped ? QMF_MIN_M_GROUPED : QMF_MIN_M) && type == Q4_K) ? QMF_ROWS : QMV_SLOTS;
-}
+inline int qmv_rows(int type, bool mfma_q4k) { return (mfma_q4k && type == Q4_K) ? QMF_ROWS : QMV_SLOTS; }
 
 inline long qmv_stage_bytes(int type, int N, int K) {
   const long waves = (long)((N + QMV_SLOTS - 1) / QMV_SLOTS) * qmv_waves(K / QK);

@@ -12,37 +12,47 @@ namespace qdot {
 
 static_assert(QMV_MULTI_MAX == QDOT_MULTI_MAX, "group size of the C ABI");
 
-template <int TA, int TB, int M, int DEPTH>
+template <int TA, int TB, int M, int DEPTH, bool MF>
 static int launch_multi_k(const QmvMulti& a, int K, const uint8_t* xq, hipStream_t s) {
   const int P = qmv_waves(K / QK);
-  const size_t la = qmv_lds_bytes<TA, M, true>(P), lb = qmv_lds_bytes<TB, M, true>(P);
+  const size_t la = qmv_lds_bytes_tile<M>(qmf_group_ok<TA, M, MF>(), P);
+  const size_t lb = qmv_lds_bytes_tile<M>(qmf_group_ok<TB, M, MF>(), P);
   const size_t lds = la > lb ? la : lb;
-  hipLaunchKernelGGL((qmv_multi_kernel<TA, TB, M, DEPTH>), dim3(a.tile_end[a.n - 1]), dim3(64 * P), lds,
-                     s, a, K, xq);
+  hipLaunchKernelGGL((qmv_multi_kernel<TA, TB, M, DEPTH, MF>), dim3(a.tile_end[a.n - 1]), dim3(64 * P),
+                     lds, s, a, K, xq);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-template <int TA, int TB, int M>
+template <int TA, int TB, int M, bool MF>
 static int launch_multi_d(const QmvMulti& a, int K, const uint8_t* xq, int depth, hipStream_t s) {
   constexpr bool wide = TA == Q6_K || TA == Q8_0 || TB == Q6_K || TB == Q8_0;
-  if (depth == 1) return launch_multi_k<TA, TB, M, 1>(a, K, xq, s);
-  if constexpr (!wide && !qmf_ok<TA, M, true>() && !qmf_ok<TB, M, true>()) {
-    if (depth == 4) return launch_multi_k<TA, TB, M, 4>(a, K, xq, s);
+  if (depth == 1) return launch_multi_k<TA, TB, M, 1, MF>(a, K, xq, s);
+  if constexpr (!wide && !qmf_group_ok<TA, M, MF>() && !qmf_group_ok<TB, M, MF>()) {
+    if (depth == 4) return launch_multi_k<TA, TB, M, 4, MF>(a, K, xq, s);
   }
-  return launch_multi_k<TA, TB, M, 2>(a, K, xq, s);
+  return launch_multi_k<TA, TB, M, 2, MF>(a, K, xq, s);
+}
+
+template <int TA, int TB, int M>
+static int launch_multi_f(const QmvMulti& a, int K, const uint8_t* xq, int depth, bool mf, hipStream_t s) {
+  if constexpr (TA == Q4_K || TB == Q4_K) {
+    if (mf) return launch_multi_d<TA, TB, M, true>(a, K, xq, depth, s);
+  }
+  return launch_multi_d<TA, TB, M, false>(a, K, xq, depth, s);
 }
 
 template <int TA, int TB>
-static int launch_multi_m(const QmvMulti& a, int K, const uint8_t* xq, int M, int depth, hipStream_t s) {
+static int launch_multi_m(const QmvMulti& a, int K, const uint8_t* xq, int M, int depth, bool mf,
+                          hipStream_t s) {
   switch (M) {
-    case 1: return launch_multi_d<TA, TB, 1>(a, K, xq, depth, s);
-    case 2: return launch_multi_d<TA, TB, 2>(a, K, xq, depth, s);
-    case 3: return launch_multi_d<TA, TB, 3>(a, K, xq, depth, s);
-    case 4: return launch_multi_d<TA, TB, 4>(a, K, xq, depth, s);
-    case 5: return launch_multi_d<TA, TB, 5>(a, K, xq, depth, s);
-    case 6: return launch_multi_d<TA, TB, 6>(a, K, xq, depth, s);
-    case 7: return launch_multi_d<TA, TB, 7>(a, K, xq, depth, s);
-    case 8: return launch_multi_d<TA, TB, 8>(a, K, xq, depth, s);
+    case 1: return launch_multi_f<TA, TB, 1>(a, K, xq, depth, mf, s);
+    case 2: return launch_multi_f<TA, TB, 2>(a, K, xq, depth, mf, s);
+    case 3: return launch_multi_f<TA, TB, 3>(a, K, xq, depth, mf, s);
+    case 4: return launch_multi_f<TA, TB, 4>(a, K, xq, depth, mf, s);
+    case 5: return launch_multi_f<TA, TB, 5>(a, K, xq, depth, mf, s);
+    case 6: return launch_multi_f<TA, TB, 6>(a, K, xq, depth, mf, s);
+    case 7: return launch_multi_f<TA, TB, 7>(a, K, xq, depth, mf, s);
+    case 8: return launch_multi_f<TA, TB, 8>(a, K, xq, depth, mf, s);
     default: return -2;
   }
 }
@@ -52,6 +62,11 @@ static int launch_group(const int* idx, int cnt, const void* const* W, const int
                         int K, const void* xq, int M, float* const* y, int ta, int tb, hipStream_t s) {
   QmvMulti a{};
   long stage = 0;
+  for (int g = 0; g < cnt; ++g) stage += qmv_stage_bytes(types[idx[g]], N[idx[g]], K);
+  // MFMA tiles for the Q4_K matrices of the group (measured, see qmv_kernel.hpp):
+  // with K >= 4096, from M = 3, and at any M for groups under 4 MB per stage
+  // (q+k+v).  At K = 1536 (six superblocks a row) the dot4 tile stays faster.
+  const bool mf = (ta == Q4_K || tb == Q4_K) && K >= 4096 && (M >= 3 || stage < (4L << 20));
   int tiles = 0;
   for (int g = 0; g < cnt; ++g) {
     const int i = idx[g];
@@ -59,29 +74,27 @@ static int launch_group(const int* idx, int cnt, const void* const* W, const int
     a.y[g] = y[i];
     a.N[g] = N[i];
     a.type[g] = types[i];
-    const int rows = qmv_rows(types[i], M, true);
+    const int rows = qmv_rows(types[i], mf);
     tiles += (N[i] + rows - 1) / rows;
     if (tiles > 0x7FFFFFFF / 2) return -1;
     a.tile_end[g] = tiles;
-    stage += qmv_stage_bytes(types[i], N[i], K);
   }
   a.n = cnt;
   const bool wide = ta == Q6_K || ta == Q8_0 || tb == Q6_K || tb == Q8_0;
-  const bool mfma_tile = qmv_rows(ta, M, true) == QMF_ROWS || qmv_rows(tb, M, true) == QMF_ROWS;
-  const int depth = mfma_tile ? qmf_depth(stage) : qmv_depth_for(stage, M, wide);
+  const int depth = mf ? qmf_depth(stage) : qmv_depth_for(stage, M, wide);
   const uint8_t* x8 = static_cast<const uint8_t*>(xq);
   if (ta == tb) {
     switch (ta) {
-      case Q4_K: return launch_multi_m<Q4_K, Q4_K>(a, K, x8, M, depth, s);
-      case Q6_K: return launch_multi_m<Q6_K, Q6_K>(a, K, x8, M, depth, s);
-      case IQ4_XS: return launch_multi_m<IQ4_XS, IQ4_XS>(a, K, x8, M, depth, s);
-      case Q4_0: return launch_multi_m<Q4_0, Q4_0>(a, K, x8, M, depth, s);
-      case Q8_0: return launch_multi_m<Q8_0, Q8_0>(a, K, x8, M, depth, s);
+      case Q4_K: return launch_multi_m<Q4_K, Q4_K>(a, K, x8, M, depth, mf, s);
+      case Q6_K: return launch_multi_m<Q6_K, Q6_K>(a, K, x8, M, depth, mf, s);
+      case IQ4_XS: return launch_multi_m<IQ4_XS, IQ4_XS>(a, K, x8, M, depth, mf, s);
+      case Q4_0: return launch_multi_m<Q4_0, Q4_0>(a, K, x8, M, depth, mf, s);
+      case Q8_0: return launch_multi_m<Q8_0, Q8_0>(a, K, x8, M, depth, mf, s);
       default: return -2;
     }
   }
-  if (ta == Q4_K && tb == Q6_K) return launch_multi_m<Q4_K, Q6_K>(a, K, x8, M, depth, s);
-  if (ta == Q4_0 && tb == Q8_0) return launch_multi_m<Q4_0, Q8_0>(a, K, x8, M, depth, s);
+  if (ta == Q4_K && tb == Q6_K) return launch_multi_m<Q4_K, Q6_K>(a, K, x8, M, depth, mf, s);
+  if (ta == Q4_0 && tb == Q8_0) return launch_multi_m<Q4_0, Q8_0>(a, K, x8, M, depth, mf, s);
   return -2;
 }
 
