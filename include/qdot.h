@@ -111,8 +111,9 @@ int qdot_quantize_q8_1(const float *x, int64_t M, int64_t K, void *x_q8,
  * int8 activations and D, S are the activation block's fp16 d and s.  Every
  * scale product is exact and accumulated in fp64; y is rounded once to fp32.
  * M <= 8 runs the decode kernel (v_dot4_i32_i8, M-row tile; for Q4_K at
- * M = 7, 8 the integer dots run on v_mfma_i32_32x32x32_i8 instead, summed in
- * the same order, so the rows are bitwise those of the dot4 tile); 8 < M <= 96 a
+ * M = 7, 8 and IQ4_XS at M = 5..8 the integer dots run on
+ * v_mfma_i32_32x32x32_i8 instead, summed in the same order, so the rows are
+ * bitwise those of the dot4 tile); 8 < M <= 96 a
  * mid-batch MFMA i8 kernel (16-row activation tiles, K split eight ways);
  * M > 96 the MFMA i8 prefill kernel.  Within each of these three ranges a row
  * of y is bitwise the same whatever M it is computed with; across them it may
@@ -139,9 +140,9 @@ int qdot_qmatmul_dump_isums(const void *W, int type, int64_t N, int64_t K,
  * W, types, N and y are host arrays of n entries; W[i] and y[i] are device
  * pointers with the alignment qdot_qmatmul requires.  For M <= 8 the decode
  * tiles of all matrices run in one launch (Q4_K with Q6_K, Q4_0 with Q8_0, or
- * a single type; other mixes take one launch per type), Q4_K tiles on the
- * MFMA units from M = 5; for M > 8 the matrices are launched one after
- * another.  The saving is the fixed cost of
+ * a single type; other mixes take one launch per type), Q4_K and IQ4_XS
+ * tiles on the MFMA units where that measured faster (K >= 4096); for M > 8
+ * the matrices are launched one after another.  The saving is the fixed cost of
  * the launches replaced.  Errors as qdot_qmatmul; n outside 1..QDOT_MULTI_MAX
  * is E_ARG.  Every argument is checked before anything is launched. */
 #define QDOT_MULTI_MAX 4

@@ -473,7 +473,8 @@ __device__ __forceinline__ void qmv_tile(const uint8_t* __restrict__ W, int N, i
 // ------------------------------------------ the MFMA tile for M = 7, 8
 //
 // The same sums as qmv_tile, in the same fp64 order, with the integer dots
-// on v_mfma_i32_32x32x32_i8 (Q4_K weights).  At M = 8 each of qmv_tile's 16
+// on v_mfma_i32_32x32x32_i8 (Q4_K and IQ4_XS weights: 32-element sub-blocks,
+// two per quarter, like the dot4 tile's).  At M = 8 each of qmv_tile's 16
 // row slots reads all 8*M activation blocks of a superblock from LDS (48 KB
 // per wave and superblock); here the matrix unit reuses every activation byte
 // across 32 weight rows, and only the fp64 scales go through LDS.
@@ -503,9 +504,13 @@ constexpr int QMF_ROWS = 32;  // weight rows per workgroup
 // q+k+v (K = 4096) is faster on MFMA tiles at every M (M = 1: 7.2 vs 7.9 us,
 // M = 4: 8.1 vs 9.9), gate+up from M = 3; at K = 1536 (Qwen2.5-1.5B) the dot4
 // tile stays faster.  Either tile gives bitwise the same rows.
-constexpr int QMF_MIN_M = 7;
-template <int T, int M> constexpr bool qmf_ok() { return M >= QMF_MIN_M && T == Q4_K; }
-template <int T, int M, bool MF> constexpr bool qmf_group_ok() { return MF && T == Q4_K; }
+// IQ4_XS (hidden-5120 shapes): its dot4 tile looks the codebook up for every
+// weight, so the MFMA tile wins from M = 5 (5120 x 7168 at M = 7: 10.9 vs
+// 14.5 us; at M = 4 the dot4 tile: 10.2 vs 10.8).
+template <int T> constexpr bool qmf_type() { return T == Q4_K || T == IQ4_XS; }
+template <int T> constexpr int qmf_min_m() { return T == IQ4_XS ? 5 : 7; }
+template <int T, int M> constexpr bool qmf_ok() { return qmf_type<T>() && M >= qmf_min_m<T>(); }
+template <int T, int M, bool MF> constexpr bool qmf_group_ok() { return MF && qmf_type<T>(); }
 template <int T, int M> constexpr int qmv_tile_rows() { return qmf_ok<T, M>() ? QMF_ROWS : QMV_SLOTS; }
 
 struct __attribute__((aligned(16))) QmfDs { double d, s; };  // fp64 D and S of one Q8_1 block
@@ -514,7 +519,8 @@ template <int T, int M, int DEPTH, bool DUMP>
 __device__ __forceinline__ void qmf_tile(const uint8_t* __restrict__ W, int N, int K,
                                          const uint8_t* __restrict__ xq, float* __restrict__ y,
                                          int32_t* __restrict__ isums, int tile, uint8_t* smem) {
-  static_assert(T == Q4_K, "the MFMA decode tile takes Q4_K weights");
+  static_assert(qmf_type<T>(), "the MFMA decode tile takes Q4_K or IQ4_XS weights");
+  constexpr int NQ = T == Q4_K ? 4 : 8;  // 16-byte code loads per superblock and lane
   constexpr int BYTES = Geom<T>::BYTES;
   constexpr int SUB = Geom<T>::SUB;
   const int P = blockDim.x >> 6;
@@ -540,8 +546,12 @@ __device__ __forceinline__ void qmf_tile(const uint8_t* __restrict__ W, int N, i
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) acc[q][mm] = 0.0;
 
+  // Q4_K: header (d, dmin, scales) and the code bytes of K-slice s of each
+  // quarter (low nibbles sub-block 2q, high 2q+1).  IQ4_XS: header (d,
+  // scales_h, scales_l) and the 16 code bytes of each sub-block (low nibbles
+  // its elements 0-15 = K-slice 0, high nibbles 16-31 = K-slice 1).
   struct Stage {
-    u32x4 h, q[4];  // header (d, dmin, scales); K-slice s code bytes of each quarter
+    u32x4 h, q[NQ];
     u32x4 a[2];     // this lane's A data in groups 0 and 1
     uint32_t ds;    // d, s of the published scale entry
   };
@@ -551,7 +561,8 @@ __device__ __forceinline__ void qmf_tile(const uint8_t* __restrict__ W, int N, i
     const uint8_t* sb = wrow + (size_t)bc * BYTES;
     st.h = ld16(sb);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) st.q[q] = ld16(sb + 16 + 32 * q + 16 * s);
+    for (int q = 0; q < NQ; ++q)
+      st.q[q] = T == Q4_K ? ld16(sb + 16 + 32 * q + 16 * s) : ld16(sb + 8 + 16 * q);
 #pragma unroll
     for (int g = 0; g < 2; ++g) st.a[g] = ld16(xa_row + (size_t)(8 * bc + 4 * g) * Q8_BYTES);
     st.ds = ld4(xd_src + (size_t)8 * bc * Q8_BYTES);
@@ -573,23 +584,41 @@ __device__ __forceinline__ void qmf_tile(const uint8_t* __restrict__ W, int N, i
       qmf_v16i C = {0};
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        // sub-block 4g + jj: quarter 2g + jj/2, low (jj even) or high nibbles
-        const u32x4 v = st.q[2 * g + (jj >> 1)];
-        const int sh = 4 * (jj & 1);
-        const qmf_v4i bq = qmf_v4i{(int)((v.x >> sh) & 0x0F0F0F0Fu), (int)((v.y >> sh) & 0x0F0F0F0Fu),
-                                   (int)((v.z >> sh) & 0x0F0F0F0Fu), (int)((v.w >> sh) & 0x0F0F0F0Fu)};
+        qmf_v4i bq;
+        if constexpr (T == Q4_K) {
+          // sub-block 4g + jj: quarter 2g + jj/2, low (jj even) or high nibbles
+          const u32x4 v = st.q[2 * g + (jj >> 1)];
+          const int sh = 4 * (jj & 1);
+          bq = qmf_v4i{(int)((v.x >> sh) & 0x0F0F0F0Fu), (int)((v.y >> sh) & 0x0F0F0F0Fu),
+                       (int)((v.z >> sh) & 0x0F0F0F0Fu), (int)((v.w >> sh) & 0x0F0F0F0Fu)};
+        } else {
+          // sub-block 4g + jj: this lane's K-slice is the low (s = 0) or high
+          // nibbles of its 16 bytes, looked up in the codebook
+          const u32x4 v = st.q[4 * g + jj];
+          const int sh = 4 * s;
+          bq = qmf_v4i{(int)cb_lookup(v.x >> sh, CB0, CB1, CB2, CB3), (int)cb_lookup(v.y >> sh, CB0, CB1, CB2, CB3),
+                       (int)cb_lookup(v.z >> sh, CB0, CB1, CB2, CB3), (int)cb_lookup(v.w >> sh, CB0, CB1, CB2, CB3)};
+        }
         C = __builtin_amdgcn_mfma_i32_32x32x32_i8(slot == jj ? a : z4, bq, C, 0, 0, 0);
       }
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int j = 4 * g + jj;
-        // 6-bit scale and min of sub-block j, as qmv_tile's decode_sub computes them
-        const int sh = 8 * jj;
-        const uint32_t Ys = st.h.y >> sh, Zs = st.h.z >> sh, Ws = st.h.w >> sh;
-        const uint32_t sc = g == 0 ? (Ys & 63u) : ((Ws & 15u) | ((Ys >> 2) & 0x30u));
-        const uint32_t mn = g == 0 ? (Zs & 63u) : (((Ws >> 4) & 15u) | ((Zs >> 2) & 0x30u));
-        const double wsc = (double)(h2f(st.h.x) * (float)sc);
-        const double wmn = -(double)(h2f(st.h.x >> 16) * (float)mn);
+        // scale (and Q4_K min) of sub-block j, as qmv_tile's decode_sub computes them
+        double wsc, wmn = 0.0;
+        if constexpr (T == Q4_K) {
+          const int sh = 8 * jj;
+          const uint32_t Ys = st.h.y >> sh, Zs = st.h.z >> sh, Ws = st.h.w >> sh;
+          const uint32_t sc = g == 0 ? (Ys & 63u) : ((Ws & 15u) | ((Ys >> 2) & 0x30u));
+          const uint32_t mn = g == 0 ? (Zs & 63u) : (((Ws >> 4) & 15u) | ((Zs >> 2) & 0x30u));
+          wsc = (double)(h2f(st.h.x) * (float)sc);
+          wmn = -(double)(h2f(st.h.x >> 16) * (float)mn);
+        } else {
+          const uint32_t sl = (st.h.y >> (4 * j)) & 15u;
+          const uint32_t shb = ((st.h.x >> 16) >> (2 * j)) & 3u;
+          const int ls = (int)(sl | (shb << 4));
+          wsc = (double)(h2f(st.h.x) * (float)(ls - 32));  // d*(ls-32), exact in fp32
+        }
         // rows m >= M (upper-half lanes at M = 7) drain zero dots against
         // row 0's scales and are never stored
 #pragma unroll
@@ -598,7 +627,7 @@ __device__ __forceinline__ void qmf_tile(const uint8_t* __restrict__ W, int N, i
           const QmfDs e = lds_ds[(m < M ? m : 0) * 8 + j];
           const int I = C[4 * jj + mm];
           acc[j >> 1][mm] = fma(wsc * e.d, (double)I, acc[j >> 1][mm]);
-          acc[j >> 1][mm] = fma(wmn, e.s, acc[j >> 1][mm]);
+          if constexpr (T == Q4_K) acc[j >> 1][mm] = fma(wmn, e.s, acc[j >> 1][mm]);
           if (DUMP && m < M && nrow < N)
             isums[((size_t)m * N + nrow) * (K / SUB) + (size_t)b * (QK / SUB) + j] = I;
         }
@@ -639,7 +668,6 @@ __device__ __forceinline__ void qmf_tile(const uint8_t* __restrict__ W, int N, i
   }
 }
 
-// LDS bytes a decode workgroup of P waves needs (either tile).
 // LDS bytes of a workgroup of `waves` waves running the MFMA tile (mfma) or
 // the dot4 tile.
 template <int M> inline size_t qmv_lds_bytes_tile(bool mfma, int waves) {
@@ -719,7 +747,7 @@ inline int qmv_waves(int nsb) {
 // stage at M <= 4; the 9 MB matrices want all four superblocks of a wave in
 // flight; Q6_K's larger register stage is kept to two.
 // Weight rows per workgroup of the decode kernels for (type, M).
-inline int qmv_rows(int type, bool mfma_q4k) { return (mfma_q4k && type == Q4_K) ? QMF_ROWS : QMV_SLOTS; }
+inline int qmv_rows(int type, bool mfma) { return (mfma && (type == Q4_K || type == IQ4_XS)) ? QMF_ROWS : QMV_SLOTS; }
 
 inline long qmv_stage_bytes(int type, int N, int K) {
   const long waves = (long)((N + QMV_SLOTS - 1) / QMV_SLOTS) * qmv_waves(K / QK);

@@ -35,7 +35,7 @@ static int launch_multi_d(const QmvMulti& a, int K, const uint8_t* xq, int depth
 
 template <int TA, int TB, int M>
 static int launch_multi_f(const QmvMulti& a, int K, const uint8_t* xq, int depth, bool mf, hipStream_t s) {
-  if constexpr (TA == Q4_K || TB == Q4_K) {
+  if constexpr (qmf_type<TA>() || qmf_type<TB>()) {
     if (mf) return launch_multi_d<TA, TB, M, true>(a, K, xq, depth, s);
   }
   return launch_multi_d<TA, TB, M, false>(a, K, xq, depth, s);
@@ -66,7 +66,8 @@ static int launch_group(const int* idx, int cnt, const void* const* W, const int
   // MFMA tiles for the Q4_K matrices of the group (measured, see qmv_kernel.hpp):
   // with K >= 4096, from M = 3, and at any M for groups under 4 MB per stage
   // (q+k+v).  At K = 1536 (six superblocks a row) the dot4 tile stays faster.
-  const bool mf = (ta == Q4_K || tb == Q4_K) && K >= 4096 && (M >= 3 || stage < (4L << 20));
+  const bool mf = (ta == Q4_K || tb == Q4_K || ta == IQ4_XS || tb == IQ4_XS) && K >= 4096 &&
+                  (M >= 3 || stage < (4L << 20));
   int tiles = 0;
   for (int g = 0; g < cnt; ++g) {
     const int i = idx[g];
