@@ -24,7 +24,10 @@
 // activation rows by QMM_BN weight rows (QMM_NT MFMA tiles per wave).  Wave
 // w takes the 32 rows (w / KP) and the superblocks b = w % KP (mod KP) of K;
 // the KP partial sums of an output are added in fixed order at the end.  KP
-// depends on N and K only, so an output's value does not depend on M.
+// depends on N and K only, so an output's value does not depend on M.  The
+// weight superblocks of each step are staged in LDS for the whole workgroup
+// (coalesced copies, one copy for the waves that share a K slice); the
+// activation codes go from HBM/L2 straight into VGPRs through a small ring.
 #pragma once
 #include <type_traits>
 
@@ -194,39 +197,54 @@ template <> struct QmmFmt<Q6_K> {
 };
 
 // --------------------------------------------------------------- kernel
-// Operands of one 32-element block for this lane: activation codes (A) and
-// the weight codes of the QMM_NT weight tiles (B, raw; decoded at use).
-template <int T> struct QmmOps {
-  u32x4 a;                               // Q6_K: .xy = K-slice of the first 16, .zw of the second
-  typename QmmFmt<T>::Blk w[QMM_NT];
-};
+// Weight staging.  Each iteration the workgroup copies the superblocks it
+// works on next -- superblock kp + KP*it of each of its QMM_BN weight rows,
+// for every K slice kp -- into LDS with 16-byte chunk copies in which
+// consecutive lanes take consecutive bytes of a row, so one copy instruction
+// of a wave touches a few cache lines, where the MFMA operand layout (lane l
+// <-> row l%32) would touch 32; the waves that share a K slice read the one
+// copy.  A row's superblock keeps its own byte order at a pitch of its size
+// rounded up to 16 bytes, so the format decoders read it as they read HBM.
+template <int T> constexpr int qmm_pitch() { return (Geom<T>::BYTES + 15) / 16 * 16; }
+template <int T, int KP> constexpr int qmm_stage_chunks() { return KP * QMM_BN * qmm_pitch<T>() / 16; }
+template <int T, int KP> constexpr int qmm_stage_regs() {  // 16-byte chunks each thread copies
+  return (qmm_stage_chunks<T, KP>() + 64 * QMM_WAVES - 1) / (64 * QMM_WAVES);
+}
+// LDS: the per-wave fp64 activation scales of one superblock, then the
+// weight stage; after the main loop the K-split partial sums reuse it.
+constexpr int QMM_SCALE_BYTES = QMM_WAVES * 8 * 32 * 16;
+template <int KP> constexpr int qmm_red_bytes() { return (QMM_WAVES - QMM_WAVES / KP) * QMM_NT * 16 * 64 * 8; }
+template <int T, int KP> constexpr int qmm_lds_bytes() {
+  return QMM_SCALE_BYTES + 16 * qmm_stage_chunks<T, KP>() > qmm_red_bytes<KP>()
+             ? QMM_SCALE_BYTES + 16 * qmm_stage_chunks<T, KP>()
+             : qmm_red_bytes<KP>();
+}
 
-template <int T> constexpr int qmm_ring() { return T == Q6_K ? 2 : 4; }  // operand ring: loads run ring-1 blocks ahead
+template <int T> constexpr int qmm_ring() { return T == Q6_K ? 2 : 4; }  // A-operand ring: loads run ring-1 blocks ahead
 
 
 template <int KP> constexpr int qmm_bm() { return 32 * QMM_WAVES / KP; }  // activation rows per workgroup
-template <int KP> constexpr int qmm_lds_bytes() {
-  // scale staging, or the partial sums of the KP-1 later K slices (same memory)
-  return (QMM_WAVES * 2 * 8 * 32 * 16) > ((QMM_WAVES - QMM_WAVES / KP) * QMM_NT * 16 * 64 * 8)
-             ? (QMM_WAVES * 2 * 8 * 32 * 16)
-             : ((QMM_WAVES - QMM_WAVES / KP) * QMM_NT * 16 * 64 * 8);
-}
 
 template <int T, int KP, bool DUMP>
-__global__ __launch_bounds__(64 * QMM_WAVES) void qmm_mfma_kernel(
+__global__ __launch_bounds__(64 * QMM_WAVES, 2) void qmm_mfma_kernel(
     const uint8_t* __restrict__ W, int N, int K, const uint8_t* __restrict__ xq, int M,
     float* __restrict__ y, int32_t* __restrict__ isums, int m_tiles, int n_tiles) {
   using F = QmmFmt<T>;
   constexpr int SUB = Geom<T>::SUB;
+  constexpr int BYTES = Geom<T>::BYTES;
+  constexpr int PITCH = qmm_pitch<T>();
+  constexpr int CPR = PITCH / 16;                      // chunks per staged row
+  constexpr int CHUNKS = qmm_stage_chunks<T, KP>();
+  constexpr int NCH = qmm_stage_regs<T, KP>();
   constexpr int QMM_RING = qmm_ring<T>();
   static_assert(8 % QMM_RING == 0, "ring slot of block j must not depend on the superblock");
   static_assert(QMM_WAVES % KP == 0, "K split must divide the waves");
-  // Activation scales of this wave's 32 rows for one superblock, fp64, two
-  // superblocks in flight: [wave][parity][block][row].  Each wave reads only
-  // its own slice, so a wave-level barrier orders the staging.  After the
-  // main loop the same memory holds the K-split partial sums.
-  __shared__ __align__(16) double lds_raw[qmm_lds_bytes<KP>() / 8];
-  QmmDs(*const lds_ds)[2][8][32] = reinterpret_cast<QmmDs(*)[2][8][32]>(lds_raw);
+  // Activation scales of this wave's 32 rows for its current superblock,
+  // fp64: [wave][block][row].  Each wave reads only its own slice, so a
+  // wave-level barrier orders the staging.
+  __shared__ __align__(16) double lds_raw[qmm_lds_bytes<T, KP>() / 8];
+  QmmDs(*const lds_ds)[8][32] = reinterpret_cast<QmmDs(*)[8][32]>(lds_raw);
+  uint8_t* const lds_w = reinterpret_cast<uint8_t*>(lds_raw) + QMM_SCALE_BYTES;
 
   // XCD-aware tile order: workgroup id i runs on XCD i % 8; the m_tiles
   // workgroups that share a weight tile get ids with the same residue, so
@@ -241,38 +259,69 @@ __global__ __launch_bounds__(64 * QMM_WAVES) void qmm_mfma_kernel(
   const int g = lane >> 5, c32 = lane & 31;
   const int kp = wave % KP, wq = wave / KP;
   const int nsb = K / QK, nq8 = K / Q8_BLOCK;
-  const size_t row_bytes = (size_t)nsb * F::BYTES;
+  const size_t row_bytes = (size_t)nsb * BYTES;
   const int m0 = m_tile * qmm_bm<KP>() + 32 * wq;
   const int n0 = n_tile * QMM_BN;
 
-  // This lane's activation row (A operand and scale staging) and weight rows
-  // (B); rows past the edge are clamped to the last one and never stored.
+  // This lane's activation row (A operand and scale staging); rows past the
+  // edge are clamped to the last one and never stored.
   const int ma = m0 + c32 < M ? m0 + c32 : M - 1;
   const uint8_t* xrow = xq + (size_t)ma * nq8 * Q8_BYTES;
-  const uint8_t* wrow[QMM_NT];
+  // This lane's staged weight rows (B operand) in K slice kp.
+  const uint8_t* wl[QMM_NT];
 #pragma unroll
-  for (int t = 0; t < QMM_NT; ++t) {
-    const int n = n0 + 32 * t + c32;
-    wrow[t] = W + (size_t)(n < N ? n : N - 1) * row_bytes;
-  }
-  QmmDs(*const stage)[8][32] = lds_ds[wave];
+  for (int t = 0; t < QMM_NT; ++t) wl[t] = lds_w + (size_t)(kp * QMM_BN + 32 * t + c32) * PITCH;
+  QmmDs(*const stage)[32] = lds_ds[wave];
 
-  auto load_ops = [&](int b, int j) {
-    QmmOps<T> o;
+  // Stage copy: chunk i = (K slice s, row r, 16-byte piece c); rows past N
+  // are clamped to the last row, superblocks past the row to the last one
+  // (in bounds, never used).  The loads are unconditional (threads past the
+  // last chunk repeat it; only the LDS store is skipped), so no branch makes
+  // the compiler wait for them before the compute.  The last piece of a 210-
+  // or 136-byte superblock is read as the 16 bytes that end the superblock
+  // and shifted down.
+  auto stage_load = [&](int it, u32x4 (&breg)[NCH]) {
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int iu = tid + 64 * QMM_WAVES * u;
+      const int i = iu < CHUNKS ? iu : CHUNKS - 1;
+      const int s = i / (QMM_BN * CPR), rem = i % (QMM_BN * CPR);
+      const int r = rem / CPR, c = rem % CPR;
+      const int n = n0 + r < N ? n0 + r : N - 1;
+      int bb = s + KP * it;
+      bb = bb < nsb ? bb : nsb - 1;
+      const uint8_t* sb = W + (size_t)n * row_bytes + (size_t)bb * BYTES;
+      if constexpr (BYTES % 16 == 0) {
+        breg[u] = ld16(sb + 16 * c);
+      } else {
+        constexpr int TAIL = BYTES % 16;
+        const bool tail = c == CPR - 1;
+        const u32x4 v = ld16(sb + (tail ? BYTES - 16 : 16 * c));
+        if constexpr (TAIL == 8) {
+          breg[u] = tail ? u32x4{v.z, v.w, 0u, 0u} : v;
+        } else {
+          static_assert(TAIL == 2, "tail piece of 2 or 8 bytes");
+          breg[u] = tail ? u32x4{v.w >> 16, 0u, 0u, 0u} : v;
+        }
+      }
+    }
+  };
+  auto stage_store = [&](const u32x4 (&breg)[NCH]) {
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int i = tid + 64 * QMM_WAVES * u;
+      if (i < CHUNKS) *reinterpret_cast<u32x4*>(lds_w + 16 * i) = breg[u];
+    }
+  };
+  // A operand of block j of superblock b (this lane's row and K-slice g).
+  auto load_a = [&](int b, int j) {
     const uint8_t* xb = xrow + (size_t)(b * 8 + j) * Q8_BYTES + 4;
     if constexpr (T == Q6_K) {
       const u32x2 lo = ld8(xb + 8 * g), hi = ld8(xb + 16 + 8 * g);
-      o.a = u32x4{lo.x, lo.y, hi.x, hi.y};
+      return u32x4{lo.x, lo.y, hi.x, hi.y};
     } else {
-      o.a = ld16(xb + 16 * g);
+      return ld16(xb + 16 * g);
     }
-#pragma unroll
-    for (int t = 0; t < QMM_NT; ++t) o.w[t] = F::blk(wrow[t] + (size_t)b * F::BYTES, j, g);
-    return o;
-  };
-  auto load_hdr = [&](int b, typename F::Hdr* h) {
-#pragma unroll
-    for (int t = 0; t < QMM_NT; ++t) h[t] = F::hdr(wrow[t] + (size_t)b * F::BYTES);
   };
   // Scales of row c32, blocks 4g..4g+3 of superblock b (raw fp16 pairs).
   auto load_ds = [&](int b, uint32_t* ds) {
@@ -291,110 +340,130 @@ __global__ __launch_bounds__(64 * QMM_WAVES) void qmm_mfma_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.0;
 
-  // Prologue: scales and headers of this wave's first superblock, operands
-  // of its first QMM_RING-1 blocks (clamped in bounds when K has fewer
-  // superblocks than the split).
+  // Every wave runs the same number of iterations (the workgroup barriers
+  // need it); a wave whose K slice has run out skips the compute (with
+  // K = 256 the second slice has no superblock at all, and its prologue
+  // loads are clamped in bounds).
+  const int nit = (nsb + KP - 1) / KP;
   const int b0 = kp < nsb ? kp : nsb - 1;
+  u32x4 breg[NCH];
+  stage_load(0, breg);
   uint32_t ds_next[4];
-  typename F::Hdr hd_next[QMM_NT];
   load_ds(b0, ds_next);
-  load_hdr(b0, hd_next);
-  QmmOps<T> ring[QMM_RING];
+  u32x4 ring[QMM_RING];
 #pragma unroll
-  for (int j = 0; j < QMM_RING - 1; ++j) ring[j] = load_ops(b0, j);
+  for (int j = 0; j < QMM_RING - 1; ++j) ring[j] = load_a(b0, j);
+  stage_store(breg);
+  __syncthreads();
 
-  for (int b = kp, it = 0; b < nsb; b += KP, ++it) {
-    const int par = it & 1;
-    const int bn = b + KP < nsb ? b + KP : b;  // clamped: the last prefetch is redundant, in bounds
+#pragma unroll 1
+  for (int it = 0; it < nit; ++it) {
+    const int b = kp + KP * it;
+    const int bn = b + KP < nsb ? b + KP : nsb - 1;  // clamped: the last prefetch is redundant, in bounds
+    const bool more = it + 1 < nit;                  // uniform over the workgroup
+    stage_load(it + 1, breg);                        // lands while this superblock is computed
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      stage[par][4 * g + u][c32] = QmmDs{(double)h2f(ds_next[u] & 0xFFFFu), (double)h2f(ds_next[u] >> 16)};
-    typename F::Hdr hd[QMM_NT];
-#pragma unroll
-    for (int t = 0; t < QMM_NT; ++t) hd[t] = hd_next[t];
+      stage[4 * g + u][c32] = QmmDs{(double)h2f(ds_next[u] & 0xFFFFu), (double)h2f(ds_next[u] >> 16)};
     load_ds(bn, ds_next);
-    load_hdr(bn, hd_next);
     wave_sync();
 
-    auto do_block = [&](auto JC) {
-      constexpr int J = decltype(JC)::value;
-      constexpr int JN = J + QMM_RING - 1;  // block whose operands are fetched now
-      ring[JN % QMM_RING] = JN < 8 ? load_ops(b, JN) : load_ops(bn, JN - 8);
-      const QmmOps<T>& o = ring[J % QMM_RING];
-      if constexpr (T == Q6_K) {
-        const long a0 = (long)((uint64_t)o.a.x | ((uint64_t)o.a.y << 32));
-        const long a1 = (long)((uint64_t)o.a.z | ((uint64_t)o.a.w << 32));
-        v16i I0[QMM_NT], I1[QMM_NT];
-        int s0[QMM_NT], s1[QMM_NT];
-        double d[QMM_NT];
+    if (b < nsb) {
+      typename F::Hdr hd[QMM_NT];
 #pragma unroll
-        for (int t = 0; t < QMM_NT; ++t) {
-          const v16i z = {0};
-          I0[t] = __builtin_amdgcn_mfma_i32_32x32x16_i8(a0, F::template codes<J>(o.w[t], 0), z, 0, 0, 0);
-          I1[t] = __builtin_amdgcn_mfma_i32_32x32x16_i8(a1, F::template codes<J>(o.w[t], 1), z, 0, 0, 0);
-          F::template scales<J>(hd[t], s0[t], s1[t]);
-          d[t] = (double)h2f(hd[t].d);
-        }
+      for (int t = 0; t < QMM_NT; ++t) hd[t] = F::hdr(wl[t]);
+
+      auto do_block = [&](auto JC) {
+        constexpr int J = decltype(JC)::value;
+        constexpr int JN = J + QMM_RING - 1;  // block whose A operand is fetched now
+        // one block at a time: keeps the scheduler from hoisting the staged
+        // operand reads of all eight blocks into registers at once
+        __builtin_amdgcn_sched_barrier(0);
+        ring[JN % QMM_RING] = JN < 8 ? load_a(b, JN) : load_a(bn, JN - 8);
+        const u32x4 oa = ring[J % QMM_RING];
+        typename F::Blk wb[QMM_NT];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = mfma_row(r, g);
-          const double D = stage[par][J][i].d;
+        for (int t = 0; t < QMM_NT; ++t) wb[t] = F::blk(wl[t], J, g);
+        if constexpr (T == Q6_K) {
+          const long a0 = (long)((uint64_t)oa.x | ((uint64_t)oa.y << 32));
+          const long a1 = (long)((uint64_t)oa.z | ((uint64_t)oa.w << 32));
+          v16i I0[QMM_NT], I1[QMM_NT];
+          int s0[QMM_NT], s1[QMM_NT];
+          double d[QMM_NT];
 #pragma unroll
           for (int t = 0; t < QMM_NT; ++t) {
-            const int P = s0[t] * I0[t][r] + s1[t] * I1[t][r];   // exact int
-            acc[t][r] = fma(d[t] * D, (double)P, acc[t][r]);     // exact product
-            if (DUMP) {
-              const int m = m0 + i, n = n0 + 32 * t + c32;
-              if (m < M && n < N) {
-                int32_t* p = isums + ((size_t)m * N + n) * (K / SUB) + (size_t)b * (QK / SUB) + 2 * J;
-                p[0] = I0[t][r];
-                p[1] = I1[t][r];
+            const v16i z = {0};
+            I0[t] = __builtin_amdgcn_mfma_i32_32x32x16_i8(a0, F::template codes<J>(wb[t], 0), z, 0, 0, 0);
+            I1[t] = __builtin_amdgcn_mfma_i32_32x32x16_i8(a1, F::template codes<J>(wb[t], 1), z, 0, 0, 0);
+            F::template scales<J>(hd[t], s0[t], s1[t]);
+            d[t] = (double)h2f(hd[t].d);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = mfma_row(r, g);
+            const double D = stage[J][i].d;
+#pragma unroll
+            for (int t = 0; t < QMM_NT; ++t) {
+              const int P = s0[t] * I0[t][r] + s1[t] * I1[t][r];   // exact int
+              acc[t][r] = fma(d[t] * D, (double)P, acc[t][r]);     // exact product
+              if (DUMP) {
+                const int m = m0 + i, n = n0 + 32 * t + c32;
+                if (m < M && n < N) {
+                  int32_t* p = isums + ((size_t)m * N + n) * (K / SUB) + (size_t)b * (QK / SUB) + 2 * J;
+                  p[0] = I0[t][r];
+                  p[1] = I1[t][r];
+                }
+              }
+            }
+          }
+        } else {
+          const v4i a = v4i{(int)oa.x, (int)oa.y, (int)oa.z, (int)oa.w};
+          v16i I[QMM_NT];
+          double w[QMM_NT], mn[QMM_NT];
+#pragma unroll
+          for (int t = 0; t < QMM_NT; ++t) {
+            const v16i z = {0};
+            I[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, F::template codes<J>(wb[t], g), z, 0, 0, 0);
+            if constexpr (T == Q4_K) F::template scales<J>(hd[t], w[t], mn[t]);
+            else { w[t] = F::template scale<J>(hd[t], wb[t]); mn[t] = 0.0; }
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = mfma_row(r, g);
+            const QmmDs e = stage[J][i];
+#pragma unroll
+            for (int t = 0; t < QMM_NT; ++t) {
+              acc[t][r] = fma(w[t] * e.d, (double)I[t][r], acc[t][r]);  // exact product
+              if constexpr (T == Q4_K) acc[t][r] = fma(mn[t], e.s, acc[t][r]);
+              if (DUMP) {
+                const int m = m0 + i, n = n0 + 32 * t + c32;
+                if (m < M && n < N)
+                  isums[((size_t)m * N + n) * (K / SUB) + (size_t)b * (QK / SUB) + J] = I[t][r];
               }
             }
           }
         }
-      } else {
-        const v4i a = v4i{(int)o.a.x, (int)o.a.y, (int)o.a.z, (int)o.a.w};
-        v16i I[QMM_NT];
-        double w[QMM_NT], mn[QMM_NT];
-#pragma unroll
-        for (int t = 0; t < QMM_NT; ++t) {
-          const v16i z = {0};
-          I[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, F::template codes<J>(o.w[t], g), z, 0, 0, 0);
-          if constexpr (T == Q4_K) F::template scales<J>(hd[t], w[t], mn[t]);
-          else { w[t] = F::template scale<J>(hd[t], o.w[t]); mn[t] = 0.0; }
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = mfma_row(r, g);
-          const QmmDs e = stage[par][J][i];
-#pragma unroll
-          for (int t = 0; t < QMM_NT; ++t) {
-            acc[t][r] = fma(w[t] * e.d, (double)I[t][r], acc[t][r]);  // exact product
-            if constexpr (T == Q4_K) acc[t][r] = fma(mn[t], e.s, acc[t][r]);
-            if (DUMP) {
-              const int m = m0 + i, n = n0 + 32 * t + c32;
-              if (m < M && n < N)
-                isums[((size_t)m * N + n) * (K / SUB) + (size_t)b * (QK / SUB) + J] = I[t][r];
-            }
-          }
-        }
-      }
-    };
-    do_block(std::integral_constant<int, 0>{});
-    do_block(std::integral_constant<int, 1>{});
-    do_block(std::integral_constant<int, 2>{});
-    do_block(std::integral_constant<int, 3>{});
-    do_block(std::integral_constant<int, 4>{});
-    do_block(std::integral_constant<int, 5>{});
-    do_block(std::integral_constant<int, 6>{});
-    do_block(std::integral_constant<int, 7>{});
+      };
+      do_block(std::integral_constant<int, 0>{});
+      do_block(std::integral_constant<int, 1>{});
+      do_block(std::integral_constant<int, 2>{});
+      do_block(std::integral_constant<int, 3>{});
+      do_block(std::integral_constant<int, 4>{});
+      do_block(std::integral_constant<int, 5>{});
+      do_block(std::integral_constant<int, 6>{});
+      do_block(std::integral_constant<int, 7>{});
+    }
+    if (more) {
+      __syncthreads();  // every wave has read this iteration's staged weights
+      stage_store(breg);
+      __syncthreads();
+    }
   }
 
   if constexpr (KP > 1) {
     // Partial sums of K slices 1..KP-1 go through LDS; slice 0 adds them in
     // slice order and stores.
-    __syncthreads();  // every wave is done with its scale staging
+    __syncthreads();  // every wave is done with its scale and weight staging
     double* red = lds_raw;
     auto slot = [&](int q, int k, int t, int r) {
       return ((((q * (KP - 1) + (k - 1)) * QMM_NT + t) * 16 + r) * 64) + lane;
@@ -426,16 +495,17 @@ __global__ __launch_bounds__(64 * QMM_WAVES) void qmm_mfma_kernel(
   }
 }
 
-// K split: 1, 2 or 4 waves per output tile, from N and K only (never M), so
+// K split: 2 or 4 waves per output tile, from N and K only (never M), so
 // that an output's value does not depend on M.  Measured on MI355X at M = 512
 // (Qwen3-8B and hidden-5120 shapes, occupancy two waves per SIMD): two slices
 // beat one and four for N > 2048; four slices win for N <= 2048, where the
-// grid is otherwise too small to fill 256 CUs.
+// grid is otherwise too small to fill 256 CUs.  With fewer superblocks than
+// slices the extra waves idle (K = 256: one superblock, two slices).
 inline int qmm_ksplit(int N, int K) {
   const int n_tiles = (N + QMM_BN - 1) / QMM_BN;
   const int nsb = K / QK;
   int kp = n_tiles <= 32 ? 4 : 2;
-  while (kp > nsb) kp >>= 1;
+  if (kp > nsb) kp = 2;
   return kp;
 }
 
@@ -455,11 +525,8 @@ inline int launch_qmm_kp(const uint8_t* W, int N, int K, const uint8_t* xq, int 
 template <int T, bool DUMP>
 inline int launch_qmm_t(const uint8_t* W, int N, int K, const uint8_t* xq, int M, float* y,
                         int32_t* isums, hipStream_t s) {
-  switch (qmm_ksplit(N, K)) {
-    case 1: return launch_qmm_kp<T, 1, DUMP>(W, N, K, xq, M, y, isums, s);
-    case 2: return launch_qmm_kp<T, 2, DUMP>(W, N, K, xq, M, y, isums, s);
-    default: return launch_qmm_kp<T, 4, DUMP>(W, N, K, xq, M, y, isums, s);
-  }
+  if (qmm_ksplit(N, K) == 2) return launch_qmm_kp<T, 2, DUMP>(W, N, K, xq, M, y, isums, s);
+  return launch_qmm_kp<T, 4, DUMP>(W, N, K, xq, M, y, isums, s);
 }
 
 }  // namespace qdot
