@@ -205,8 +205,12 @@ template <> struct QmmFmt<Q6_K> {
 // <-> row l%32) would touch 32; the waves that share a K slice read the one
 // copy.  A row's superblock keeps its own byte order at a pitch of its size
 // rounded up to 16 bytes, so the format decoders read it as they read HBM.
-template <int T> constexpr int qmm_pitch() { return (Geom<T>::BYTES + 15) / 16 * 16; }
-template <int T, int KP> constexpr int qmm_stage_chunks() { return KP * QMM_BN * qmm_pitch<T>() / 16; }
+// Q6_K rows are read 8 bytes per lane, 32 rows at once: a pitch of 58
+// dwords (232 bytes) puts those 32 reads on 64 distinct banks, where the
+// 16-byte multiple (224) would put rows r, r+8, r+16, r+24 on the same ones.
+template <int T> constexpr int qmm_cpr() { return (Geom<T>::BYTES + 15) / 16; }  // 16-byte pieces per row
+template <int T> constexpr int qmm_pitch() { return T == Q6_K ? 232 : 16 * qmm_cpr<T>(); }
+template <int T, int KP> constexpr int qmm_stage_chunks() { return KP * QMM_BN * qmm_cpr<T>(); }
 template <int T, int KP> constexpr int qmm_stage_regs() {  // 16-byte chunks each thread copies
   return (qmm_stage_chunks<T, KP>() + 64 * QMM_WAVES - 1) / (64 * QMM_WAVES);
 }
@@ -214,9 +218,10 @@ template <int T, int KP> constexpr int qmm_stage_regs() {  // 16-byte chunks eac
 // weight stage; after the main loop the K-split partial sums reuse it.
 constexpr int QMM_SCALE_BYTES = QMM_WAVES * 8 * 32 * 16;
 template <int KP> constexpr int qmm_red_bytes() { return (QMM_WAVES - QMM_WAVES / KP) * QMM_NT * 16 * 64 * 8; }
+template <int T, int KP> constexpr int qmm_stage_bytes() { return KP * QMM_BN * qmm_pitch<T>(); }
 template <int T, int KP> constexpr int qmm_lds_bytes() {
-  return QMM_SCALE_BYTES + 16 * qmm_stage_chunks<T, KP>() > qmm_red_bytes<KP>()
-             ? QMM_SCALE_BYTES + 16 * qmm_stage_chunks<T, KP>()
+  return QMM_SCALE_BYTES + qmm_stage_bytes<T, KP>() > qmm_red_bytes<KP>()
+             ? QMM_SCALE_BYTES + qmm_stage_bytes<T, KP>()
              : qmm_red_bytes<KP>();
 }
 
@@ -233,7 +238,7 @@ __global__ __launch_bounds__(64 * QMM_WAVES, 2) void qmm_mfma_kernel(
   constexpr int SUB = Geom<T>::SUB;
   constexpr int BYTES = Geom<T>::BYTES;
   constexpr int PITCH = qmm_pitch<T>();
-  constexpr int CPR = PITCH / 16;                      // chunks per staged row
+  constexpr int CPR = qmm_cpr<T>();                    // chunks per staged row
   constexpr int CHUNKS = qmm_stage_chunks<T, KP>();
   constexpr int NCH = qmm_stage_regs<T, KP>();
   constexpr int QMM_RING = qmm_ring<T>();
@@ -310,7 +315,16 @@ __global__ __launch_bounds__(64 * QMM_WAVES, 2) void qmm_mfma_kernel(
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const int i = tid + 64 * QMM_WAVES * u;
-      if (i < CHUNKS) *reinterpret_cast<u32x4*>(lds_w + 16 * i) = breg[u];
+      if (i < CHUNKS) {
+        if constexpr (PITCH == 16 * CPR) {
+          *reinterpret_cast<u32x4*>(lds_w + 16 * i) = breg[u];
+        } else {  // padded rows: the piece lands 8-byte aligned
+          const int sr = i / CPR, c = i % CPR;
+          u32x2* dst = reinterpret_cast<u32x2*>(lds_w + sr * PITCH + 16 * c);
+          dst[0] = u32x2{breg[u].x, breg[u].y};
+          dst[1] = u32x2{breg[u].z, breg[u].w};
+        }
+      }
     }
   };
   // A operand of block j of superblock b (this lane's row and K-slice g).
@@ -502,9 +516,8 @@ __global__ __launch_bounds__(64 * QMM_WAVES, 2) void qmm_mfma_kernel(
 // grid is otherwise too small to fill 256 CUs.  With fewer superblocks than
 // slices the extra waves idle (K = 256: one superblock, two slices).
 inline int qmm_ksplit(int N, int K) {
-  const int n_tiles = (N + QMM_BN - 1) / QMM_BN;
   const int nsb = K / QK;
-  int kp = n_tiles <= 32 ? 4 : 2;
+  int kp = N <= 2048 ? 4 : 2;
   if (kp > nsb) kp = 2;
   return kp;
 }
