@@ -48,9 +48,11 @@ def parse():
     p.add_argument("--workload", default="qwen3-8b-decode",
                    choices=["qwen3-8b-decode", "qwen3-8b-prefill-512", "iq4xs-h5120-decode",
                             "qwen2.5-1.5b-decode", "qwen3-8b-q4_0-q8_0-decode", "qwen3-8b-mid-batch",
-                            "qwen3-8b-rmsnorm-q8_1"])
+                            "qwen3-8b-rmsnorm-q8_1", "q4k-matvec-1536"])
     p.add_argument("--ms", default=None, help="comma-separated M values (default per workload)")
     p.add_argument("--layers", type=int, default=None, help="override the layer count")
+    p.add_argument("--same-weights", action="store_true",
+                   help="every layer reads layer 0's weights (cache-hot timing of the same launches)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true", help="skip the sampled oracle check")
     p.add_argument("--kernel-reps", type=int, default=None,
@@ -79,6 +81,12 @@ def workload_def(name):
         return 5, synth.QWEN3_8B_Q40_Q80, 36, [1, 2, 4, 8]
     if name == "qwen3-8b-mid-batch":
         return 6, synth.QWEN3_8B, 36, [16, 32, 64, 96]
+    if name == "q4k-matvec-1536":
+        # One 1536 x 1536 Q4_K matrix at M = 1, as 400 distinct seeded copies
+        # (531 MB, over twice the 256 MB Infinity Cache) launched in turn, so
+        # every launch reads its weights from HBM; --layers 1 repeats a single
+        # copy, which then stays in cache (the hot figure).
+        return 0, [("w", 1536, 1536, synth.Q4_K)], 400, [1]
     raise ValueError(name)
 
 
@@ -136,6 +144,46 @@ def copy_calibration(mib):
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+def copy_reference(dev, launch_bytes, reps=10):
+    """Measured HBM reference for the decode roofline: device-to-device copies
+    (torch copy_, i.e. the runtime's copy kernel), counting the bytes read plus
+    the bytes written.  Once as one 512 MiB copy (streaming rate), once as 36
+    copies of the dominant kernel's bytes per launch, each from its own buffer
+    (every copy cold in the Infinity Cache), timed together between HIP events
+    (what a single launch of that size reaches)."""
+    import torch
+    out = {}
+    n = 512 << 20
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    out["copy_512MiB_GBps"] = round(2 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del a, b
+    m = int(launch_bytes) // 256 * 256
+    srcs = [torch.ones(m, dtype=torch.uint8, device=dev) for _ in range(36)]
+    dsts = [torch.empty(m, dtype=torch.uint8, device=dev) for _ in range(36)]
+    for s_, d_ in zip(srcs, dsts):
+        d_.copy_(s_)
+    torch.cuda.synchronize()
+    e0.record()
+    for s_, d_ in zip(srcs, dsts):
+        d_.copy_(s_)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / 36
+    out["copy_at_launch_size"] = {"bytes_per_copy": m, "us": round(t * 1e6, 3),
+                                  "GBps": round(2 * m / t / 1e9, 1)}
+    return out
 
 
 def cpu_baseline(shapes, cfg_idx, Ms, budget_s=20.0, prefill=False):
@@ -320,6 +368,9 @@ def main():
     t0 = time.time()
     Wdev = []   # [layer][proj] device tensors
     for layer in range(layers):
+        if args.same_weights and layer > 0:
+            Wdev.append(Wdev[0])
+            continue
         row = []
         for pi, (name, N, K, t) in enumerate(shapes):
             row.append(torch.from_numpy(synth.weights(t, N, K, synth.weight_seed(cfg_idx, layer, pi))).to(dev))
@@ -542,6 +593,9 @@ def main():
                     "traffic": recorded_traffic(dname, args.workload),
                     "launches": dn, "avg_launch_us": round(dms * 1e3 / dn, 3),
                     "algorithmic_bytes_per_launch": round(dbytes / dn)}
+        ref = copy_reference(dev, dbytes / dn)
+        ref["frac_of_copy_512MiB"] = round(achieved / ref["copy_512MiB_GBps"], 4)
+        roofline["measured_reference"] = ref
     kernels = {k: {"launches_per_step": v[2], "ms_per_step": round(v[1], 4),
                    "GBps": round(v[0] / (v[1] * 1e-3) / 1e9, 1),
                    **({"TOPs": round(v[3] / (v[1] * 1e-3) / 1e12, 2)} if v[3] else {})}
@@ -557,7 +611,7 @@ def main():
             graphs[M].replay()
             torch.cuda.synchronize()
             b = bufs[M]
-            layer = layers - 1   # the buffers hold the last layer's outputs
+            layer = 0 if args.same_weights else layers - 1   # whose weights the last launches read
             for pi, (name, N, K, t) in enumerate(shapes):
                 W = synth.weights(t, N, K, synth.weight_seed(cfg_idx, layer, pi))
                 xq = b["xq"][INPUT_OF[name]].cpu().numpy()
@@ -598,7 +652,8 @@ def main():
                    "projections": [f"{n} {N}x{K} {synth.TYPE_NAMES[t]}" for n, N, K, t in shapes],
                    "weight_bytes_per_sweep": wbytes_sweep,
                    "launches_per_step": sum(len(units(M)) for M in Ms) * layers + len(Ms) * layers * len(inputs),
-                   "grouped_launches": not args.separate},
+                   "grouped_launches": not args.separate,
+                   **({"same_weights_every_layer": True} if args.same_weights else {})},
         **({"pct_mfma_i8_peak": round(100 * value / MFMA_I8_PEAK_TOPS, 2)} if prefill else
            {"pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1)}),
         "roofline": roofline,
