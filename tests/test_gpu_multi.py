@@ -55,6 +55,14 @@ def test_qkv_mixed_q4k_q6k(M):
     check_group([(200, synth.Q4_K), (70, synth.Q4_K), (33, synth.Q6_K)], 1024, M, seed=M)
 
 
+@pytest.mark.parametrize("M", [1, 5, 8])
+def test_group_q4k_q6k_long_rows(M):
+    """Q4_K and Q6_K matrices with 48-superblock rows (K = 12288) in one
+    group (the Q4_K ones on MFMA tiles, the group being small): each output bitwise equal
+    to its own single call."""
+    check_group([(96, synth.Q4_K), (40, synth.Q6_K), (33, synth.Q4_K)], 12288, M, seed=100 + M)
+
+
 @pytest.mark.parametrize("M", [1, 8])
 def test_gate_up_full_size(M):
     """Gate and up of the 8B FFN (two 12288 x 4096 Q4_K) in one launch."""

@@ -160,6 +160,27 @@ def test_zero_activations_give_zero():
         assert not y.any()
 
 
+def test_q6k_long_rows_all_M():
+    """Q6_K rows of 48 and 51 superblocks (the down projection's K = 12288,
+    and a K whose superblocks do not divide evenly over the waves of the K
+    split): sub-block sums bit-exact through the dump at every M = 1..8, every
+    output within 1e-5 rel, and rows bitwise the same at every M."""
+    for K in (12288, 13056):
+        N = 37
+        W = synth.weights(synth.Q6_K, N, K, (2026, 90, K))
+        Wd = to_dev(W)
+        x = synth.activations(8, K, (2026, 90, K, 8, 7))
+        xqd, xq = quantize(x)
+        y8, _ = qmatmul(Wd, synth.Q6_K, N, K, xqd, 8)
+        y64, _, _ = oracle.qmatmul(W, synth.Q6_K, N, K, xq, 8)
+        assert_close(y8, y64, f"Q6_K {N}x{K} M=8")
+        for M in range(1, 9):
+            xm = xqd[: qd.qdot_q8_1_bytes(M, K)]
+            y, isums = qmatmul(Wd, synth.Q6_K, N, K, xm, M, dump=True)
+            assert np.array_equal(isums, oracle.isums(W, synth.Q6_K, N, K, xq[: qd.qdot_q8_1_bytes(M, K)], M))
+            assert np.array_equal(y.view(np.uint32), y8[:M].view(np.uint32)), f"K={K} M={M}: rows differ from M=8"
+
+
 @pytest.mark.parametrize("wtype", TYPES)
 @pytest.mark.parametrize("M", [9, 16, 33, 96, 97])
 def test_qmatmul_m_above_8(wtype, M):
