@@ -225,13 +225,20 @@ template <int T, int KP> constexpr int qmm_lds_bytes() {
              : qmm_red_bytes<KP>();
 }
 
+// Two workgroups (two waves per SIMD) per CU wherever the LDS allows it;
+// the Q8_0 K-split-4 instance (a 272-byte-pitch stage) holds one, and so
+// does the sub-block-sum dump (a test path: fewer spills at one wave).
+template <int T, int KP, bool DUMP> constexpr int qmm_min_waves() {
+  return !DUMP && qmm_lds_bytes<T, KP>() <= 80 * 1024 ? 2 : 1;
+}
+
 template <int T> constexpr int qmm_ring() { return T == Q6_K ? 2 : 4; }  // A-operand ring: loads run ring-1 blocks ahead
 
 
 template <int KP> constexpr int qmm_bm() { return 32 * QMM_WAVES / KP; }  // activation rows per workgroup
 
 template <int T, int KP, bool DUMP>
-__global__ __launch_bounds__(64 * QMM_WAVES, 2) void qmm_mfma_kernel(
+__global__ __launch_bounds__(64 * QMM_WAVES, (qmm_min_waves<T, KP, DUMP>())) void qmm_mfma_kernel(
     const uint8_t* __restrict__ W, int N, int K, const uint8_t* __restrict__ xq, int M,
     float* __restrict__ y, int32_t* __restrict__ isums, int m_tiles, int n_tiles) {
   using F = QmmFmt<T>;
