@@ -420,8 +420,10 @@ def main():
 
     def unit_kernel(M, pis):
         if len(pis) == 1:
-            return qd.qdot_kernel_name(shapes[pis[0]][3], M)
-        return "qmv_multi<" + "+".join(qd.qdot_kernel_name(shapes[pi][3], M) for pi in pis) + ">"
+            _, N, K, t = shapes[pis[0]]
+            return qd.qdot_kernel_name_shape(t, N, K, M)
+        return "qmv_multi<" + "+".join(qd.qdot_kernel_name_shape(shapes[pi][3], shapes[pi][1], shapes[pi][2], M)
+                                       for pi in pis) + ">"
 
     P_, I32_, I64_ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     multi_args = {}   # (M, layer, label) -> prebuilt ctypes arrays

@@ -170,10 +170,19 @@ int qdot_rmsnorm_quantize_q8_1(const float *x, const float *w, float eps,
 /* Static text for a status code. */
 const char *qdot_status_str(int status);
 
-/* Name of the kernel qdot_qmatmul runs for (type, M), e.g. "qmv_dot4<Q4_K,4>",
- * "qmv_mfma<Q4_K,8>", "qmm_skinny<Q4_K>" or "qmm_mfma<Q6_K>"; "invalid" for bad
- * arguments.  Static text. */
+/* Name of the kernel qdot_qmatmul runs for (type, M) on a matrix of the
+ * default ranges, e.g. "qmv_dot4<Q4_K,4>", "qmv_mfma<Q4_K,8>",
+ * "qmm_skinny<Q4_K>" or "qmm_mfma<Q6_K>"; "invalid" for bad arguments.  Static
+ * text.  Exact for every matrix except the wide ones below, whose switch from
+ * the mid-batch to the prefill kernel comes earlier. */
 const char *qdot_kernel_name(int type, int64_t M);
+
+/* Name of the kernel qdot_qmatmul runs for a type-`type` N x K matrix and M
+ * activation rows; "invalid" if the dimensions would be rejected.  Equal to
+ * qdot_kernel_name(type, M) except for Q4_K and IQ4_XS matrices with
+ * N >= 8192 and K >= 4096, which leave the mid-batch kernel above M = 32
+ * (Q4_K) or 48 (IQ4_XS) instead of 96.  Static text. */
+const char *qdot_kernel_name_shape(int type, int64_t N, int64_t K, int64_t M);
 
 /* Build identifier of the library (compile date and time).  Static text. */
 const char *qdot_build_id(void);

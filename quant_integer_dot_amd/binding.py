@@ -62,6 +62,8 @@ def load():
     L.qdot_status_str.restype = ctypes.c_char_p
     L.qdot_kernel_name.argtypes = [i32, i64]
     L.qdot_kernel_name.restype = ctypes.c_char_p
+    L.qdot_kernel_name_shape.argtypes = [i32, i64, i64, i64]
+    L.qdot_kernel_name_shape.restype = ctypes.c_char_p
     L.qdot_build_id.argtypes = []
     L.qdot_build_id.restype = ctypes.c_char_p
     _lib = L
@@ -157,6 +159,10 @@ def qdot_status_str(status):
 
 def qdot_kernel_name(wtype, M):
     return load().qdot_kernel_name(wtype, M).decode()
+
+
+def qdot_kernel_name_shape(wtype, N, K, M):
+    return load().qdot_kernel_name_shape(wtype, N, K, M).decode()
 
 
 def qdot_build_id():

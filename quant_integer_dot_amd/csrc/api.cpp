@@ -42,19 +42,31 @@ int check_dims(int type, int64_t N, int64_t K, int64_t M) {
   return QDOT_OK;
 }
 
-// Mid-batch dispatch: 9 <= M <= QDOT_SKINNY_MAX_M runs the mid-batch MFMA
-// kernel (16 activation rows per tile, K split eight ways), larger M the
+// Mid-batch dispatch: 9 <= M <= mid_max_m(type, N, K) runs the mid-batch
+// MFMA kernel (16 activation rows per tile, K split eight ways), larger M the
 // prefill kernel (64 or 32 activation rows per tile).  Measured on MI355X at
 // the Qwen3-8B shapes the mid-batch kernel beats running the decode kernel
 // over 8-row chunks at every M from 9 to 32 (4096 x 4096, M = 16: 11.8 vs
-// 15.8 us) and the prefill kernel up to M = 48 on every shape; over a whole
-// layer it is faster up to M = 96 (M = 64: 270 vs 437 us; M = 96: 391 vs
-// 476 us; M = 128: equal), though 12288 x 4096 alone prefers the prefill
-// kernel from M = 56.  The choice depends on M only, so the kernel a call
-// runs is known from (type, M).
+// 15.8 us), and over a whole layer it is faster up to M = 96 (M = 96: 368 vs
+// 415 us on the prefill kernel at M = 97).  Wide matrices are the exception,
+// since the prefill kernel stays flat in M up to 64 rows: 12288 x 4096 Q4_K
+// takes 39.7-40.9 us there at M = 40..64 against 47.8-59.6 on the mid-batch
+// kernel, and 58.4 against 86.0 at M = 96; 17408 x 5120 IQ4_XS 80.6 against
+// 94.3 at M = 56 (but 79.0 against 75.3 at M = 48).  Q6_K stays on the
+// mid-batch kernel (down 4096 x 12288 at M = 97: 157 us prefill, 100 us
+// mid-batch at 96).  For a given matrix the switch happens at one M, so its
+// rows stay the same for every M on either side of it.
 #ifndef QDOT_SKINNY_MAX_M
 #define QDOT_SKINNY_MAX_M 96
 #endif
+
+int64_t mid_max_m(int type, int64_t N, int64_t K) {
+  if (N >= 8192 && K >= 4096) {
+    if (type == QDOT_Q4_K) return 32;
+    if (type == QDOT_IQ4_XS) return 48;
+  }
+  return QDOT_SKINNY_MAX_M;
+}
 
 int run_qmatmul(const void* W, int type, int64_t N, int64_t K, const void* x_q8, int64_t M,
                 float* y, int32_t* isums, void* stream, bool dump) {
@@ -66,7 +78,7 @@ int run_qmatmul(const void* W, int type, int64_t N, int64_t K, const void* x_q8,
   int rc = 0;
   if (M <= 8) {
     rc = qdot::launch_qmv(W, type, (int)N, (int)K, x_q8, (int)M, y, dump ? isums : nullptr, s);
-  } else if (M <= QDOT_SKINNY_MAX_M) {
+  } else if (M <= mid_max_m(type, N, K)) {
     rc = qdot::launch_qmm_skinny(W, type, (int)N, (int)K, x_q8, (int)M, y, dump ? isums : nullptr, s);
   } else {
     rc = qdot::launch_qmm(W, type, (int)N, (int)K, x_q8, (int)M, y, dump ? isums : nullptr, s);
@@ -187,6 +199,12 @@ const char* qdot_kernel_name(int type, int64_t M) {
   if (type < QDOT_Q4_K || type > QDOT_Q8_0 || M < 1 || M > kMaxDim) return "invalid";
   if (M <= 8) return dec[type - 1][M - 1];
   return M <= QDOT_SKINNY_MAX_M ? mid[type - 1] : pre[type - 1];
+}
+
+const char* qdot_kernel_name_shape(int type, int64_t N, int64_t K, int64_t M) {
+  if (check_dims(type, N, K, M) != QDOT_OK) return "invalid";
+  if (M <= 8 || M > QDOT_SKINNY_MAX_M) return qdot_kernel_name(type, M);
+  return qdot_kernel_name(type, M <= mid_max_m(type, N, K) ? M : QDOT_SKINNY_MAX_M + 1);
 }
 
 const char* qdot_build_id(void) { return "libqdot gfx950 " __DATE__ " " __TIME__; }
