@@ -171,17 +171,19 @@ int qdot_rmsnorm_quantize_q8_1(const float *x, const float *w, float eps,
 const char *qdot_status_str(int status);
 
 /* Name of the kernel qdot_qmatmul runs for (type, M) on a matrix of the
- * default ranges, e.g. "qmv_dot4<Q4_K,4>", "qmv_mfma<Q4_K,8>",
+ * default ranges (M <= 8 decode tile, M <= 96 mid-batch kernel, larger M
+ * prefill kernel), e.g. "qmv_dot4<Q4_K,4>", "qmv_mfma<Q4_K,8>",
  * "qmm_skinny<Q4_K>" or "qmm_mfma<Q6_K>"; "invalid" for bad arguments.  Static
- * text.  Exact for every matrix except the wide ones below, whose switch from
- * the mid-batch to the prefill kernel comes earlier. */
+ * text.  Exact for the M <= 8 names and for IQ4_XS below N = 8192, Q4_0 and
+ * Q8_0; qdot_kernel_name_shape is exact for every matrix. */
 const char *qdot_kernel_name(int type, int64_t M);
 
 /* Name of the kernel qdot_qmatmul runs for a type-`type` N x K matrix and M
- * activation rows; "invalid" if the dimensions would be rejected.  Equal to
- * qdot_kernel_name(type, M) except for Q4_K and IQ4_XS matrices with
- * N >= 8192 and K >= 4096, which leave the mid-batch kernel above M = 32
- * (Q4_K) or 48 (IQ4_XS) instead of 96.  Static text. */
+ * activation rows; "invalid" if the dimensions would be rejected.  The
+ * mid-batch kernel's range depends on the matrix: up to M = 32 for Q4_K and
+ * 48 for IQ4_XS when N >= 8192 and K >= 4096; up to 256 for Q6_K with
+ * N <= 2048 and 128 for other Q6_K; up to 128 for Q4_K with N <= 2048; else
+ * up to 96.  Static text. */
 const char *qdot_kernel_name_shape(int type, int64_t N, int64_t K, int64_t M);
 
 /* Build identifier of the library (compile date and time).  Static text. */

@@ -54,8 +54,13 @@ int check_dims(int type, int64_t N, int64_t K, int64_t M) {
 // kernel, and 58.4 against 86.0 at M = 96; 17408 x 5120 IQ4_XS 80.6 against
 // 94.3 at M = 56 (but 79.0 against 75.3 at M = 48).  Q6_K stays on the
 // mid-batch kernel (down 4096 x 12288 at M = 97: 157 us prefill, 100 us
-// mid-batch at 96).  For a given matrix the switch happens at one M, so its
-// rows stay the same for every M on either side of it.
+// mid-batch at 96).  Above M = 96 the mid-batch kernel still wins on Q6_K and
+// on narrow Q4_K matrices, the prefill kernel's Q6_K drain and its few
+// workgroups for N <= 2048 being slow: v (1024 x 4096 Q6_K) 17.4 / 26.0 us at
+// M = 128 / 256 against 41.3 / 41.6; k (1024 x 4096 Q4_K) 13.3 against 22.4
+// at 128, equal at 160; down (4096 x 12288 Q6_K) 129 against 162 at 128,
+// equal at 160, 188 against 162 at 192.  For a given matrix the switch
+// happens at one M, so its rows stay the same for every M on either side.
 #ifndef QDOT_SKINNY_MAX_M
 #define QDOT_SKINNY_MAX_M 96
 #endif
@@ -65,6 +70,8 @@ int64_t mid_max_m(int type, int64_t N, int64_t K) {
     if (type == QDOT_Q4_K) return 32;
     if (type == QDOT_IQ4_XS) return 48;
   }
+  if (type == QDOT_Q6_K) return N <= 2048 ? 256 : 128;
+  if (type == QDOT_Q4_K && N <= 2048) return 128;
   return QDOT_SKINNY_MAX_M;
 }
 
@@ -203,8 +210,9 @@ const char* qdot_kernel_name(int type, int64_t M) {
 
 const char* qdot_kernel_name_shape(int type, int64_t N, int64_t K, int64_t M) {
   if (check_dims(type, N, K, M) != QDOT_OK) return "invalid";
-  if (M <= 8 || M > QDOT_SKINNY_MAX_M) return qdot_kernel_name(type, M);
-  return qdot_kernel_name(type, M <= mid_max_m(type, N, K) ? M : QDOT_SKINNY_MAX_M + 1);
+  if (M <= 8) return qdot_kernel_name(type, M);
+  // the mid-batch or the prefill name of the type
+  return qdot_kernel_name(type, M <= mid_max_m(type, N, K) ? 9 : QDOT_SKINNY_MAX_M + 1);
 }
 
 const char* qdot_build_id(void) { return "libqdot gfx950 " __DATE__ " " __TIME__; }

@@ -74,14 +74,24 @@ def test_names_and_status(lib):
     assert ks(qd.QDOT_Q4_K, 12288, 3840, 33) == "qmm_skinny<Q4_K>"
     assert ks(qd.QDOT_IQ4_XS, 17408, 5120, 48) == "qmm_skinny<IQ4_XS>"
     assert ks(qd.QDOT_IQ4_XS, 17408, 5120, 49) == "qmm_mfma<IQ4_XS>"
-    assert ks(qd.QDOT_Q6_K, 12288, 4096, 96) == "qmm_skinny<Q6_K>"
+    assert ks(qd.QDOT_Q6_K, 12288, 4096, 128) == "qmm_skinny<Q6_K>"
+    assert ks(qd.QDOT_Q6_K, 12288, 4096, 129) == "qmm_mfma<Q6_K>"
+    assert ks(qd.QDOT_Q6_K, 2048, 4096, 256) == "qmm_skinny<Q6_K>"
+    assert ks(qd.QDOT_Q6_K, 2048, 4096, 257) == "qmm_mfma<Q6_K>"
+    assert ks(qd.QDOT_Q6_K, 2049, 4096, 129) == "qmm_mfma<Q6_K>"
+    assert ks(qd.QDOT_Q4_K, 2048, 4096, 128) == "qmm_skinny<Q4_K>"
+    assert ks(qd.QDOT_Q4_K, 2048, 4096, 129) == "qmm_mfma<Q4_K>"
+    assert ks(qd.QDOT_Q4_K, 4096, 4096, 97) == "qmm_mfma<Q4_K>"
     assert ks(qd.QDOT_Q4_0, 12288, 4096, 96) == "qmm_skinny<Q4_0>"
+    assert ks(qd.QDOT_Q4_0, 1024, 4096, 97) == "qmm_mfma<Q4_0>"
     assert ks(qd.QDOT_Q4_K, 12288, 4096, 8) == "qmv_mfma<Q4_K,8>"
     assert ks(qd.QDOT_Q4_K, 12288, 4096, 97) == "qmm_mfma<Q4_K>"
     assert ks(qd.QDOT_Q4_K, 12288, 100, 40) == "invalid"
-    for t in (qd.QDOT_Q4_K, qd.QDOT_Q6_K, qd.QDOT_IQ4_XS, qd.QDOT_Q4_0, qd.QDOT_Q8_0):
+    for t in (qd.QDOT_Q4_K, qd.QDOT_IQ4_XS, qd.QDOT_Q4_0, qd.QDOT_Q8_0):
         for M in (1, 5, 8, 9, 33, 49, 96, 97, 512):
             assert ks(t, 4096, 4096, M) == qd.qdot_kernel_name(t, M)
+    for M in (1, 5, 8, 9, 96, 512):
+        assert ks(qd.QDOT_Q6_K, 4096, 4096, M) == qd.qdot_kernel_name(qd.QDOT_Q6_K, M)
     assert qd.qdot_status_str(qd.QDOT_E_ALIGN) == "misaligned pointer"
     assert "gfx950" in qd.qdot_build_id()
 

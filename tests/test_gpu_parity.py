@@ -182,7 +182,7 @@ def test_q6k_long_rows_all_M():
 
 
 @pytest.mark.parametrize("wtype", TYPES)
-@pytest.mark.parametrize("M", [9, 16, 33, 96, 97])
+@pytest.mark.parametrize("M", [9, 16, 33, 96, 97, 300])
 def test_qmatmul_m_above_8(wtype, M):
     N, K = 70, 1536
     W = synth.weights(wtype, N, K, (9, wtype, M))
@@ -257,34 +257,36 @@ def test_mid_batch_full_size_sampled(name, N, K, wtype):
     assert np.array_equal(y9.view(np.uint32), y[:9].view(np.uint32)), "M invariance"
 
 
-@pytest.mark.parametrize("wtype,N,K,M_switch", [(synth.Q4_K, 8192, 4096, 32), (synth.IQ4_XS, 8192, 4096, 48)])
-def test_wide_matrix_kernel_switch(wtype, N, K, M_switch):
-    """Wide Q4_K / IQ4_XS matrices leave the mid-batch kernel above M = 32 / 48
-    (qdot_kernel_name_shape says which kernel runs): sampled rows on both
-    sides against the oracle, and rows bitwise equal for every M within each
-    side (M = 9 vs M_switch, M_switch + 1 vs 96 vs 200)."""
+@pytest.mark.parametrize("wtype,N,K,M_switch", [(synth.Q4_K, 8192, 4096, 32), (synth.IQ4_XS, 8192, 4096, 48),
+                                                  (synth.Q6_K, 1024, 4096, 256), (synth.Q4_K, 1024, 4096, 128),
+                                                  (synth.Q6_K, 4096, 2048, 128)])
+def test_matrix_kernel_switch(wtype, N, K, M_switch):
+    """The mid-batch kernel's range depends on the matrix (qdot_kernel_name_shape
+    says which kernel runs): sampled rows on both sides of the switch against
+    the oracle, and rows bitwise equal for every M within each side (M = 9 vs
+    M_switch, M_switch + 1 vs M_switch + 40)."""
+    Mmax = M_switch + 40
     W = synth.weights(wtype, N, K, (2026, 75, wtype, N, K))
     Wd = to_dev(W)
-    x = synth.activations(200, K, (2026, 75, K, 200, 7))
+    x = synth.activations(Mmax, K, (2026, 75, K, Mmax, 7))
     xqd, xq = quantize(x)
     assert qd.qdot_kernel_name_shape(wtype, N, K, M_switch).startswith("qmm_skinny")
     assert qd.qdot_kernel_name_shape(wtype, N, K, M_switch + 1).startswith("qmm_mfma")
     rows = np.unique(np.concatenate([np.random.default_rng(N + 5).integers(0, N, 12), [0, N - 1]]))
     ys = {}
-    for M in (9, M_switch, M_switch + 1, 96, 200):
+    for M in (9, M_switch, M_switch + 1, Mmax):
         y, _ = qmatmul(Wd, wtype, N, K, xqd[: qd.qdot_q8_1_bytes(M, K)], M)
         y64, _ = oracle.qmatmul_rows(W, wtype, N, K, xq[: qd.qdot_q8_1_bytes(M, K)], M, rows)
         assert_close(y[:, rows], y64, f"{TN[wtype]} {N}x{K} M={M}")
         ys[M] = y
     assert np.array_equal(ys[9].view(np.uint32), ys[M_switch][:9].view(np.uint32)), "mid-batch rows"
     s1 = M_switch + 1
-    assert np.array_equal(ys[s1].view(np.uint32), ys[96][:s1].view(np.uint32)), "prefill rows"
-    assert np.array_equal(ys[96].view(np.uint32), ys[200][:96].view(np.uint32)), "prefill rows"
+    assert np.array_equal(ys[s1].view(np.uint32), ys[Mmax][:s1].view(np.uint32)), "prefill rows"
 
 
 # --------------------------------------------------- prefill (MFMA path)
 @pytest.mark.parametrize("wtype", TYPES)
-@pytest.mark.parametrize("M,N,K", [(512, 200, 768), (130, 64, 256), (97, 333, 1280)])
+@pytest.mark.parametrize("M,N,K", [(512, 200, 768), (300, 64, 256), (260, 333, 1280), (130, 4096, 512)])
 def test_prefill_parity(wtype, M, N, K):
     """Several 128 x 64 output tiles with ragged edges in M and N: sub-block
     sums bit-exact through the dump, every output within 1e-5 rel."""
@@ -318,7 +320,7 @@ def test_prefill_full_size_sampled(name, N, K, wtype):
     rows = np.unique(np.concatenate([rng.integers(0, N, 24), [0, N - 1]]))
     y64, _ = oracle.qmatmul_rows(W, wtype, N, K, xq, M, rows)
     assert_close(y[:, rows], y64, f"{name} {N}x{K} M=512")
-    Ms = 100
+    Ms = 300  # above every matrix's mid-batch range, so the same kernel
     y_s, _ = qmatmul(Wd, wtype, N, K, xqd[: qd.qdot_q8_1_bytes(Ms, K)], Ms)
     assert np.array_equal(y_s.view(np.uint32), y[:Ms].view(np.uint32)), "M invariance"
 
