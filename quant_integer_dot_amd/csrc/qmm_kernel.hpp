@@ -226,10 +226,12 @@ template <int T, int KP> constexpr int qmm_lds_bytes() {
 }
 
 // Two workgroups (two waves per SIMD) per CU wherever the LDS allows it;
-// the Q8_0 K-split-4 instance (a 272-byte-pitch stage) holds one, and so
-// does the sub-block-sum dump (a test path: fewer spills at one wave).
+// the Q8_0 K-split-4 instance (a 272-byte-pitch stage) holds one, and so do
+// the Q6_K K-split-4 instance (its 56 staging registers spill at two waves:
+// 1024 x 4096 at M = 512 42 us at two, 37.6 at one) and the sub-block-sum
+// dump (a test path: fewer spills at one wave).
 template <int T, int KP, bool DUMP> constexpr int qmm_min_waves() {
-  return !DUMP && qmm_lds_bytes<T, KP>() <= 80 * 1024 ? 2 : 1;
+  return !DUMP && !(T == Q6_K && KP == 4) && qmm_lds_bytes<T, KP>() <= 80 * 1024 ? 2 : 1;
 }
 
 template <int T> constexpr int qmm_ring() { return T == Q6_K ? 2 : 4; }  // A-operand ring: loads run ring-1 blocks ahead
