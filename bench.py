@@ -422,8 +422,11 @@ def main():
         if len(pis) == 1:
             _, N, K, t = shapes[pis[0]]
             return qd.qdot_kernel_name_shape(t, N, K, M)
-        return "qmv_multi<" + "+".join(qd.qdot_kernel_name_shape(shapes[pi][3], shapes[pi][1], shapes[pi][2], M)
-                                       for pi in pis) + ">"
+        types = [shapes[pi][3] for pi in pis]
+        Ns = [shapes[pi][1] for pi in pis]
+        K = shapes[pis[0]][2]
+        return "qmv_multi<" + "+".join(qd.qdot_multi_kernel_name(types, Ns, K, M, i)
+                                       for i in range(len(pis))) + ">"
 
     P_, I32_, I64_ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     multi_args = {}   # (M, layer, label) -> prebuilt ctypes arrays

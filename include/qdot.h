@@ -186,6 +186,15 @@ const char *qdot_kernel_name(int type, int64_t M);
  * up to 96.  Static text. */
 const char *qdot_kernel_name_shape(int type, int64_t N, int64_t K, int64_t M);
 
+/* Name of the tile matrix i of a qdot_qmatmul_multi call with these types,
+ * row counts, K and M runs: for M <= 8 "qmv_mfma<Q4_K,M>" / "qmv_mfma<IQ4_XS,M>"
+ * where the group takes the MFMA tile (a choice made per launch, so it can
+ * differ from the matrix's own qdot_kernel_name), else "qmv_dot4<type,M>";
+ * for M > 8 qdot_kernel_name_shape of the matrix.  "invalid" if the call would
+ * be rejected or i is out of range.  Static text. */
+const char *qdot_multi_kernel_name(int n, const int *types, const int64_t *N,
+                                   int64_t K, int64_t M, int i);
+
 /* Build identifier of the library (compile date and time).  Static text. */
 const char *qdot_build_id(void);
 

@@ -64,6 +64,8 @@ def load():
     L.qdot_kernel_name.restype = ctypes.c_char_p
     L.qdot_kernel_name_shape.argtypes = [i32, i64, i64, i64]
     L.qdot_kernel_name_shape.restype = ctypes.c_char_p
+    L.qdot_multi_kernel_name.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(i64), i64, i64, i32]
+    L.qdot_multi_kernel_name.restype = ctypes.c_char_p
     L.qdot_build_id.argtypes = []
     L.qdot_build_id.restype = ctypes.c_char_p
     _lib = L
@@ -163,6 +165,15 @@ def qdot_kernel_name(wtype, M):
 
 def qdot_kernel_name_shape(wtype, N, K, M):
     return load().qdot_kernel_name_shape(wtype, N, K, M).decode()
+
+
+def qdot_multi_kernel_name(types, Ns, K, M, i):
+    n = len(types)
+    if len(Ns) != n:
+        raise ValueError("types and Ns must have the same length")
+    ta = (ctypes.c_int * n)(*types)
+    na = (ctypes.c_int64 * n)(*Ns)
+    return load().qdot_multi_kernel_name(n, ta, na, K, M, i).decode()
 
 
 def qdot_build_id():

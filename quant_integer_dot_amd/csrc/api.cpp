@@ -21,6 +21,7 @@ int launch_qmm_skinny(const void* W, int type, int N, int K, const void* xq, int
                       int32_t* isums, hipStream_t s);
 int launch_qmv_multi(int n, const void* const* W, const int* types, const int* N, int K, const void* xq,
                      int M, float* const* y, hipStream_t s);
+bool qmv_multi_uses_mfma(int n, const int* types, const int* N, int K, int M, int i);
 }  // namespace qdot
 
 namespace {
@@ -213,6 +214,34 @@ const char* qdot_kernel_name_shape(int type, int64_t N, int64_t K, int64_t M) {
   if (M <= 8) return qdot_kernel_name(type, M);
   // the mid-batch or the prefill name of the type
   return qdot_kernel_name(type, M <= mid_max_m(type, N, K) ? 9 : QDOT_SKINNY_MAX_M + 1);
+}
+
+const char* qdot_multi_kernel_name(int n, const int* types, const int64_t* N, int64_t K, int64_t M, int i) {
+  if (n < 1 || n > QDOT_MULTI_MAX || !types || !N || i < 0 || i >= n) return "invalid";
+  for (int j = 0; j < n; ++j)
+    if (check_dims(types[j], N[j], K, M) != QDOT_OK) return "invalid";
+  if (M > 8) return qdot_kernel_name_shape(types[i], N[i], K, M);
+  static const char* const dot4[5][8] = {
+      {"qmv_dot4<Q4_K,1>", "qmv_dot4<Q4_K,2>", "qmv_dot4<Q4_K,3>", "qmv_dot4<Q4_K,4>",
+       "qmv_dot4<Q4_K,5>", "qmv_dot4<Q4_K,6>", "qmv_dot4<Q4_K,7>", "qmv_dot4<Q4_K,8>"},
+      {"qmv_dot4<Q6_K,1>", "qmv_dot4<Q6_K,2>", "qmv_dot4<Q6_K,3>", "qmv_dot4<Q6_K,4>",
+       "qmv_dot4<Q6_K,5>", "qmv_dot4<Q6_K,6>", "qmv_dot4<Q6_K,7>", "qmv_dot4<Q6_K,8>"},
+      {"qmv_dot4<IQ4_XS,1>", "qmv_dot4<IQ4_XS,2>", "qmv_dot4<IQ4_XS,3>", "qmv_dot4<IQ4_XS,4>",
+       "qmv_dot4<IQ4_XS,5>", "qmv_dot4<IQ4_XS,6>", "qmv_dot4<IQ4_XS,7>", "qmv_dot4<IQ4_XS,8>"},
+      {"qmv_dot4<Q4_0,1>", "qmv_dot4<Q4_0,2>", "qmv_dot4<Q4_0,3>", "qmv_dot4<Q4_0,4>",
+       "qmv_dot4<Q4_0,5>", "qmv_dot4<Q4_0,6>", "qmv_dot4<Q4_0,7>", "qmv_dot4<Q4_0,8>"},
+      {"qmv_dot4<Q8_0,1>", "qmv_dot4<Q8_0,2>", "qmv_dot4<Q8_0,3>", "qmv_dot4<Q8_0,4>",
+       "qmv_dot4<Q8_0,5>", "qmv_dot4<Q8_0,6>", "qmv_dot4<Q8_0,7>", "qmv_dot4<Q8_0,8>"}};
+  static const char* const mfma[2][8] = {
+      {"qmv_mfma<Q4_K,1>", "qmv_mfma<Q4_K,2>", "qmv_mfma<Q4_K,3>", "qmv_mfma<Q4_K,4>",
+       "qmv_mfma<Q4_K,5>", "qmv_mfma<Q4_K,6>", "qmv_mfma<Q4_K,7>", "qmv_mfma<Q4_K,8>"},
+      {"qmv_mfma<IQ4_XS,1>", "qmv_mfma<IQ4_XS,2>", "qmv_mfma<IQ4_XS,3>", "qmv_mfma<IQ4_XS,4>",
+       "qmv_mfma<IQ4_XS,5>", "qmv_mfma<IQ4_XS,6>", "qmv_mfma<IQ4_XS,7>", "qmv_mfma<IQ4_XS,8>"}};
+  int n32[QDOT_MULTI_MAX];
+  for (int j = 0; j < n; ++j) n32[j] = (int)N[j];
+  if (qdot::qmv_multi_uses_mfma(n, types, n32, (int)K, (int)M, i))
+    return mfma[types[i] == QDOT_Q4_K ? 0 : 1][M - 1];
+  return dot4[types[i] - 1][M - 1];
 }
 
 const char* qdot_build_id(void) { return "libqdot gfx950 " __DATE__ " " __TIME__; }

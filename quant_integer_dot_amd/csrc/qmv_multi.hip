@@ -57,17 +57,34 @@ static int launch_multi_m(const QmvMulti& a, int K, const uint8_t* xq, int M, in
   }
 }
 
+// Whether the group idx[0..cnt-1] (types ta, tb) runs MFMA tiles for its
+// Q4_K / IQ4_XS matrices (measured, see qmv_kernel.hpp): with K >= 4096, from
+// M = 3, and at any M for groups under 4 MB per stage (q+k+v).  At K = 1536
+// (six superblocks a row) the dot4 tile stays faster.
+static bool group_mfma(const int* idx, int cnt, const int* types, const int* N, int K, int M, int ta,
+                       int tb, long* stage_out) {
+  long stage = 0;
+  for (int g = 0; g < cnt; ++g) stage += qmv_stage_bytes(types[idx[g]], N[idx[g]], K);
+  if (stage_out) *stage_out = stage;
+  return (ta == Q4_K || tb == Q4_K || ta == IQ4_XS || tb == IQ4_XS) && K >= 4096 &&
+         (M >= 3 || stage < (4L << 20));
+}
+
+// The fused type mixes of GGUF's usual mixed-precision files: Q4_K with Q6_K
+// and Q4_0 with Q8_0.  Any other mix runs one launch per weight type.
+static bool fused_mix(int nd, const int* distinct) {
+  return nd == 1 || (nd == 2 && ((distinct[0] == Q4_K && distinct[1] == Q6_K) ||
+                                 (distinct[0] == Q6_K && distinct[1] == Q4_K) ||
+                                 (distinct[0] == Q4_0 && distinct[1] == Q8_0) ||
+                                 (distinct[0] == Q8_0 && distinct[1] == Q4_0)));
+}
+
 // One launch over the matrices idx[0..cnt-1] (all of type ta or tb).
 static int launch_group(const int* idx, int cnt, const void* const* W, const int* types, const int* N,
                         int K, const void* xq, int M, float* const* y, int ta, int tb, hipStream_t s) {
   QmvMulti a{};
   long stage = 0;
-  for (int g = 0; g < cnt; ++g) stage += qmv_stage_bytes(types[idx[g]], N[idx[g]], K);
-  // MFMA tiles for the Q4_K matrices of the group (measured, see qmv_kernel.hpp):
-  // with K >= 4096, from M = 3, and at any M for groups under 4 MB per stage
-  // (q+k+v).  At K = 1536 (six superblocks a row) the dot4 tile stays faster.
-  const bool mf = (ta == Q4_K || tb == Q4_K || ta == IQ4_XS || tb == IQ4_XS) && K >= 4096 &&
-                  (M >= 3 || stage < (4L << 20));
+  const bool mf = group_mfma(idx, cnt, types, N, K, M, ta, tb, &stage);
   int tiles = 0;
   for (int g = 0; g < cnt; ++g) {
     const int i = idx[g];
@@ -99,22 +116,42 @@ static int launch_group(const int* idx, int cnt, const void* const* W, const int
   return -2;
 }
 
-// The mixes of GGUF's usual mixed-precision files are fused: Q4_K with Q6_K
-// and Q4_0 with Q8_0.  Any other mix runs one launch per weight type.
-int launch_qmv_multi(int n, const void* const* W, const int* types, const int* N, int K, const void* xq,
-                     int M, float* const* y, hipStream_t s) {
-  int distinct[QMV_MULTI_MAX];
+static int distinct_types(int n, const int* types, int* distinct) {
   int nd = 0;
   for (int i = 0; i < n; ++i) {
     bool seen = false;
     for (int d = 0; d < nd; ++d) seen = seen || distinct[d] == types[i];
     if (!seen) distinct[nd++] = types[i];
   }
+  return nd;
+}
+
+// Whether matrix i of a grouped call runs the MFMA tile (else the dot4 tile):
+// the decision of the launch that holds it.
+bool qmv_multi_uses_mfma(int n, const int* types, const int* N, int K, int M, int i) {
+  if (types[i] != Q4_K && types[i] != IQ4_XS) return false;
+  int distinct[QMV_MULTI_MAX];
+  const int nd = distinct_types(n, types, distinct);
   int idx[QMV_MULTI_MAX];
-  if (nd == 1 || (nd == 2 && ((distinct[0] == Q4_K && distinct[1] == Q6_K) ||
-                              (distinct[0] == Q6_K && distinct[1] == Q4_K) ||
-                              (distinct[0] == Q4_0 && distinct[1] == Q8_0) ||
-                              (distinct[0] == Q8_0 && distinct[1] == Q4_0)))) {
+  int cnt = 0, ta, tb;
+  if (fused_mix(nd, distinct)) {
+    for (int j = 0; j < n; ++j) idx[cnt++] = j;
+    ta = distinct[0];
+    tb = nd == 2 ? distinct[1] : distinct[0];
+  } else {
+    for (int j = 0; j < n; ++j)
+      if (types[j] == types[i]) idx[cnt++] = j;
+    ta = tb = types[i];
+  }
+  return group_mfma(idx, cnt, types, N, K, M, ta, tb, nullptr);
+}
+
+int launch_qmv_multi(int n, const void* const* W, const int* types, const int* N, int K, const void* xq,
+                     int M, float* const* y, hipStream_t s) {
+  int distinct[QMV_MULTI_MAX];
+  const int nd = distinct_types(n, types, distinct);
+  int idx[QMV_MULTI_MAX];
+  if (fused_mix(nd, distinct)) {
     for (int i = 0; i < n; ++i) idx[i] = i;
     int ta = distinct[0], tb = nd == 2 ? distinct[1] : distinct[0];
     if (ta > tb) { const int t = ta; ta = tb; tb = t; }

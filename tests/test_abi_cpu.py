@@ -92,6 +92,20 @@ def test_names_and_status(lib):
             assert ks(t, 4096, 4096, M) == qd.qdot_kernel_name(t, M)
     for M in (1, 5, 8, 9, 96, 512):
         assert ks(qd.QDOT_Q6_K, 4096, 4096, M) == qd.qdot_kernel_name(qd.QDOT_Q6_K, M)
+    # grouped launches choose the tile per launch: q+k+v of the 8B model
+    # (under 4 MB per stage) takes MFMA tiles for its Q4_K matrices at every M,
+    # gate+up from M = 3, and at K = 1536 the dot4 tile stays
+    mk = qd.qdot_multi_kernel_name
+    qkv = ([qd.QDOT_Q4_K, qd.QDOT_Q4_K, qd.QDOT_Q6_K], [4096, 1024, 1024])
+    assert [mk(*qkv, 4096, 1, i) for i in range(3)] == ["qmv_mfma<Q4_K,1>", "qmv_mfma<Q4_K,1>", "qmv_dot4<Q6_K,1>"]
+    gu = ([qd.QDOT_Q4_K, qd.QDOT_Q4_K], [12288, 12288])
+    assert mk(*gu, 4096, 2, 0) == "qmv_dot4<Q4_K,2>"
+    assert mk(*gu, 4096, 3, 1) == "qmv_mfma<Q4_K,3>"
+    assert mk(*([qd.QDOT_Q4_K, qd.QDOT_Q4_K], [8960, 8960]), 1536, 8, 0) == "qmv_dot4<Q4_K,8>"
+    assert mk(*([qd.QDOT_IQ4_XS] * 2, [17408, 17408]), 5120, 4, 0) == "qmv_mfma<IQ4_XS,4>"
+    assert mk(*gu, 4096, 64, 0) == "qmm_mfma<Q4_K>"
+    assert mk(*gu, 4096, 1, 2) == "invalid"
+    assert mk(*([qd.QDOT_Q4_K, 9], [64, 64]), 4096, 1, 0) == "invalid"
     assert qd.qdot_status_str(qd.QDOT_E_ALIGN) == "misaligned pointer"
     assert "gfx950" in qd.qdot_build_id()
 
