@@ -1,0 +1,53 @@
+"""CPU: the host side of bench.py -- its one-GPU contract, its workload table
+and the recorded HBM traffic it reports (no GPU calls)."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from quant_integer_dot_amd import synth  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("name", ["qwen3-8b-decode", "qwen3-8b-prefill-512", "iq4xs-h5120-decode",
+                                  "qwen2.5-1.5b-decode", "qwen3-8b-q4_0-q8_0-decode", "qwen3-8b-mid-batch"])
+def test_workloads_match_the_synthetic_configs(name):
+    """Each bench workload has the shapes and layer count of the synthetic
+    config it names, and M values inside that config's list."""
+    cfg_idx, shapes, layers, Ms = bench.workload_def(name)
+    w = synth.WORKLOADS[cfg_idx]
+    assert w["name"] == name
+    assert shapes == w["shapes"] and layers == w["layers"]
+    assert set(Ms) <= set(w["Ms"])
+
+
+def test_c0_workload_is_cold():
+    """C0 runs the single 1536 x 1536 Q4_K matrix as distinct copies whose
+    total is over twice the 256 MB Infinity Cache."""
+    cfg_idx, shapes, layers, Ms = bench.workload_def("q4k-matvec-1536")
+    assert cfg_idx == 0 and shapes == synth.WORKLOADS[0]["shapes"] and Ms == [1]
+    name, N, K, t = shapes[0]
+    assert layers * synth.weight_bytes(t, N, K) > 2 * 256e6
+
+
+@pytest.mark.parametrize("kernel,workload", [("qmv_multi_kernel", "qwen3-8b-decode"),
+                                             ("qmm_mfma_kernel", "qwen3-8b-prefill-512"),
+                                             ("qmm_skinny_kernel", "qwen3-8b-mid-batch"),
+                                             ("rmsnorm_q8_1_kernel", "qwen3-8b-rmsnorm-q8_1")])
+def test_recorded_traffic_matches_the_sources(kernel, workload):
+    """The committed HBM-traffic summary of each measured kernel was taken on
+    the current sources (its digest matches), so the bench line reports it."""
+    t = bench.recorded_traffic(kernel, workload)
+    assert isinstance(t, int) and t > 0
