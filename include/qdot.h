@@ -113,12 +113,14 @@ int qdot_quantize_q8_1(const float *x, int64_t M, int64_t K, void *x_q8,
  * M <= 8 runs the decode kernel (v_dot4_i32_i8, M-row tile; for Q4_K at
  * M = 7, 8 and IQ4_XS at M = 5..8 the integer dots run on
  * v_mfma_i32_32x32x32_i8 instead, summed in the same order, so the rows are
- * bitwise those of the dot4 tile); 8 < M <= 96 a
- * mid-batch MFMA i8 kernel (16-row activation tiles, K split eight ways);
- * M > 96 the MFMA i8 prefill kernel.  Within each of these three ranges a row
- * of y is bitwise the same whatever M it is computed with; across them it may
- * differ in the last fp32 bit (different fp64 summation orders).  K % 256 == 0
- * is required. */
+ * bitwise those of the dot4 tile); Q4_K and IQ4_XS keep that MFMA decode
+ * tile, with 16-row activation slots, up to M = 16.  Above the decode range
+ * and up to M = 96 runs a mid-batch MFMA i8 kernel (16-row activation tiles,
+ * K split eight ways); M > 96 the MFMA i8 prefill kernel (the mid-batch
+ * kernel's upper end depends on the matrix: qdot_kernel_name_shape).  Within
+ * each of these three ranges a row of y is bitwise the same whatever M it is
+ * computed with; across them it may differ in the last fp32 bit (different
+ * fp64 summation orders).  K % 256 == 0 is required. */
 int qdot_qmatmul(const void *W, int type, int64_t N, int64_t K,
                  const void *x_q8, int64_t M, float *y, void *stream);
 
@@ -171,10 +173,11 @@ int qdot_rmsnorm_quantize_q8_1(const float *x, const float *w, float eps,
 const char *qdot_status_str(int status);
 
 /* Name of the kernel qdot_qmatmul runs for (type, M) on a matrix of the
- * default ranges (M <= 8 decode tile, M <= 96 mid-batch kernel, larger M
- * prefill kernel), e.g. "qmv_dot4<Q4_K,4>", "qmv_mfma<Q4_K,8>",
+ * default ranges (decode tile for M <= 8, and for M <= 16 with Q4_K and
+ * IQ4_XS; M <= 96 mid-batch kernel; larger M prefill kernel), e.g.
+ * "qmv_dot4<Q4_K,4>", "qmv_mfma<Q4_K,8>", "qmv_mfma<IQ4_XS,12>",
  * "qmm_skinny<Q4_K>" or "qmm_mfma<Q6_K>"; "invalid" for bad arguments.  Static
- * text.  Exact for the M <= 8 names and for IQ4_XS below N = 8192, Q4_0 and
+ * text.  Exact for the decode names and for IQ4_XS below N = 8192, Q4_0 and
  * Q8_0; qdot_kernel_name_shape is exact for every matrix. */
 const char *qdot_kernel_name(int type, int64_t M);
 

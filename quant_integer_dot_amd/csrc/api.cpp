@@ -84,7 +84,7 @@ int run_qmatmul(const void* W, int type, int64_t N, int64_t K, const void* x_q8,
   if (!aligned4(x_q8) || !aligned4(y) || (dump && !aligned4(isums))) return QDOT_E_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   int rc = 0;
-  if (M <= 8) {
+  if (M <= 8 || (M <= 16 && (type == QDOT_Q4_K || type == QDOT_IQ4_XS))) {
     rc = qdot::launch_qmv(W, type, (int)N, (int)K, x_q8, (int)M, y, dump ? isums : nullptr, s);
   } else if (M <= mid_max_m(type, N, K)) {
     rc = qdot::launch_qmm_skinny(W, type, (int)N, (int)K, x_q8, (int)M, y, dump ? isums : nullptr, s);
@@ -200,20 +200,26 @@ const char* qdot_kernel_name(int type, int64_t M) {
        "qmv_dot4<Q4_0,5>", "qmv_dot4<Q4_0,6>", "qmv_dot4<Q4_0,7>", "qmv_dot4<Q4_0,8>"},
       {"qmv_dot4<Q8_0,1>", "qmv_dot4<Q8_0,2>", "qmv_dot4<Q8_0,3>", "qmv_dot4<Q8_0,4>",
        "qmv_dot4<Q8_0,5>", "qmv_dot4<Q8_0,6>", "qmv_dot4<Q8_0,7>", "qmv_dot4<Q8_0,8>"}};
+  static const char* const dec16[2][8] = {
+      {"qmv_mfma<Q4_K,9>", "qmv_mfma<Q4_K,10>", "qmv_mfma<Q4_K,11>", "qmv_mfma<Q4_K,12>",
+       "qmv_mfma<Q4_K,13>", "qmv_mfma<Q4_K,14>", "qmv_mfma<Q4_K,15>", "qmv_mfma<Q4_K,16>"},
+      {"qmv_mfma<IQ4_XS,9>", "qmv_mfma<IQ4_XS,10>", "qmv_mfma<IQ4_XS,11>", "qmv_mfma<IQ4_XS,12>",
+       "qmv_mfma<IQ4_XS,13>", "qmv_mfma<IQ4_XS,14>", "qmv_mfma<IQ4_XS,15>", "qmv_mfma<IQ4_XS,16>"}};
   static const char* const mid[5] = {"qmm_skinny<Q4_K>", "qmm_skinny<Q6_K>", "qmm_skinny<IQ4_XS>",
                                      "qmm_skinny<Q4_0>", "qmm_skinny<Q8_0>"};
   static const char* const pre[5] = {"qmm_mfma<Q4_K>", "qmm_mfma<Q6_K>", "qmm_mfma<IQ4_XS>",
                                      "qmm_mfma<Q4_0>", "qmm_mfma<Q8_0>"};
   if (type < QDOT_Q4_K || type > QDOT_Q8_0 || M < 1 || M > kMaxDim) return "invalid";
   if (M <= 8) return dec[type - 1][M - 1];
+  if (M <= 16 && (type == QDOT_Q4_K || type == QDOT_IQ4_XS)) return dec16[type == QDOT_Q4_K ? 0 : 1][M - 9];
   return M <= QDOT_SKINNY_MAX_M ? mid[type - 1] : pre[type - 1];
 }
 
 const char* qdot_kernel_name_shape(int type, int64_t N, int64_t K, int64_t M) {
   if (check_dims(type, N, K, M) != QDOT_OK) return "invalid";
-  if (M <= 8) return qdot_kernel_name(type, M);
+  if (M <= 8 || (M <= 16 && (type == QDOT_Q4_K || type == QDOT_IQ4_XS))) return qdot_kernel_name(type, M);
   // the mid-batch or the prefill name of the type
-  return qdot_kernel_name(type, M <= mid_max_m(type, N, K) ? 9 : QDOT_SKINNY_MAX_M + 1);
+  return qdot_kernel_name(type, M <= mid_max_m(type, N, K) ? QDOT_SKINNY_MAX_M : QDOT_SKINNY_MAX_M + 1);
 }
 
 const char* qdot_multi_kernel_name(int n, const int* types, const int64_t* N, int64_t K, int64_t M, int i) {

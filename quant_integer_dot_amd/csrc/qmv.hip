@@ -1,5 +1,5 @@
-// qmv.hip -- launches of the decode kernel (M = 1..8) for one matrix; the
-// kernel is in qmv_kernel.hpp.
+// qmv.hip -- launches of the decode kernel (M = 1..8; Q4_K and IQ4_XS up to
+// M = 16) for one matrix; the kernel is in qmv_kernel.hpp.
 #include "qmv_kernel.hpp"
 
 namespace qdot {
@@ -19,14 +19,23 @@ static int launch_qmv_k(const uint8_t* W, int N, int K, const uint8_t* xq, float
 template <int T, int M, bool DUMP>
 static int launch_qmv_r(const uint8_t* W, int N, int K, const uint8_t* xq, float* y,
                         int32_t* isums, hipStream_t s) {
-  if constexpr (DUMP) return launch_qmv_k<T, M, 2, true>(W, N, K, xq, y, isums, s);
-  switch (qmf_ok<T, M>() ? qmf_depth(qmv_stage_bytes(T, N, K)) : qmv_depth(T, M, N, K)) {
-    case 1: return launch_qmv_k<T, M, 1, false>(W, N, K, xq, y, isums, s);
-    case 2: return launch_qmv_k<T, M, 2, false>(W, N, K, xq, y, isums, s);
-    default:
-      if constexpr (T == Q6_K || T == Q8_0 || qmf_ok<T, M>())
-        return launch_qmv_k<T, M, 2, false>(W, N, K, xq, y, isums, s);
-      else return launch_qmv_k<T, M, 4, false>(W, N, K, xq, y, isums, s);
+  // 16-row MFMA tiles (M = 9..16): the depth rule of the 8-row tile; the
+  // debug dump keeps one superblock in flight (fewer registers to spill)
+  if constexpr (M > 8) {
+    if constexpr (!DUMP)
+      if (qmf_depth(qmv_stage_bytes(T, N, K)) == 2) return launch_qmv_k<T, M, 2, false>(W, N, K, xq, y, isums, s);
+    return launch_qmv_k<T, M, 1, DUMP>(W, N, K, xq, y, isums, s);
+  } else if constexpr (DUMP) {
+    return launch_qmv_k<T, M, 2, true>(W, N, K, xq, y, isums, s);
+  } else {
+    switch (qmf_ok<T, M>() ? qmf_depth(qmv_stage_bytes(T, N, K)) : qmv_depth(T, M, N, K)) {
+      case 1: return launch_qmv_k<T, M, 1, false>(W, N, K, xq, y, isums, s);
+      case 2: return launch_qmv_k<T, M, 2, false>(W, N, K, xq, y, isums, s);
+      default:
+        if constexpr (T == Q6_K || T == Q8_0 || qmf_ok<T, M>())
+          return launch_qmv_k<T, M, 2, false>(W, N, K, xq, y, isums, s);
+        else return launch_qmv_k<T, M, 4, false>(W, N, K, xq, y, isums, s);
+    }
   }
 }
 
@@ -42,8 +51,22 @@ static int launch_qmv_m(const uint8_t* W, int N, int K, const uint8_t* xq, int M
     case 6: return launch_qmv_r<T, 6, DUMP>(W, N, K, xq, y, isums, s);
     case 7: return launch_qmv_r<T, 7, DUMP>(W, N, K, xq, y, isums, s);
     case 8: return launch_qmv_r<T, 8, DUMP>(W, N, K, xq, y, isums, s);
-    default: return -2;
+    default: break;
   }
+  if constexpr (qmf_type<T>()) {  // M = 9..16 on the MFMA tile
+    switch (M) {
+      case 9: return launch_qmv_r<T, 9, DUMP>(W, N, K, xq, y, isums, s);
+      case 10: return launch_qmv_r<T, 10, DUMP>(W, N, K, xq, y, isums, s);
+      case 11: return launch_qmv_r<T, 11, DUMP>(W, N, K, xq, y, isums, s);
+      case 12: return launch_qmv_r<T, 12, DUMP>(W, N, K, xq, y, isums, s);
+      case 13: return launch_qmv_r<T, 13, DUMP>(W, N, K, xq, y, isums, s);
+      case 14: return launch_qmv_r<T, 14, DUMP>(W, N, K, xq, y, isums, s);
+      case 15: return launch_qmv_r<T, 15, DUMP>(W, N, K, xq, y, isums, s);
+      case 16: return launch_qmv_r<T, 16, DUMP>(W, N, K, xq, y, isums, s);
+      default: break;
+    }
+  }
+  return -2;
 }
 
 int launch_qmv(const void* W, int type, int N, int K, const void* xq, int M, float* y,

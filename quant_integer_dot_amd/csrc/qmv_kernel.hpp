@@ -1,13 +1,14 @@
-// qmv_kernel.hpp -- decode matmul for M = 1..8 token rows (rows a2-a5 of the hot
-// path): y[m][n] = sum_k w[n][k] * xhat[m][k] on the raw Q4_K / Q6_K / IQ4_XS
-// superblocks, with v_dot4_i32_i8 integer dots against Q8_1 activations.
+// qmv_kernel.hpp -- decode matmul for M = 1..8 token rows, and for Q4_K and
+// IQ4_XS up to 16 (rows a2-a5 of the hot path): y[m][n] = sum_k w[n][k] *
+// xhat[m][k] on the raw Q4_K / Q6_K / IQ4_XS superblocks, with v_dot4_i32_i8
+// or MFMA i8 integer dots against Q8_1 activations.
 //
 // What the pages fix, and what this kernel keeps:
 //  * integer dots on the raw quantized weights, fp32 out, no fp32 weight copy
 //    (xLLM v0.7 log, section 1);
 //  * an M-row tile, so each weight byte is read from HBM once for all M rows
-//    (xLLM section B2, q4k_dp4a_matmul_q8_v2_kernel<M>; V100TPS 2026-08-12,
-//    "batched MMVQ: weights read once, not once per token position");
+//    (xLLM section B2, q4k_dp4a_matmul_q8_v2_kernel<M>; V100TPS 2026-08-12:
+//    the batched matvec reads the weights once for all token positions);
 //  * the weight decode and the IQ4_NL lookup done once per weight, not once per
 //    row (V100TPS 2026-08-12: moving the kvalues lookup to load time gave 1.5x);
 //  * exact int32 sums inside each sub-block, scales applied afterwards
@@ -515,6 +516,11 @@ template <int T, int M> constexpr int qmv_tile_rows() { return qmf_ok<T, M>() ? 
 
 struct __attribute__((aligned(16))) QmfDs { double d, s; };  // fp64 D and S of one Q8_1 block
 
+// The MFMA tile also takes M = 9..16 (Q4_K and IQ4_XS, through qdot_qmatmul):
+// 16 activation rows per A-tile slot instead of 8, two sub-blocks per group.
+constexpr int QMF_MAX_M = 16;
+template <int M> constexpr int qmf_rows() { return M <= 8 ? 8 : 16; }
+
 template <int T, int M, int DEPTH, bool DUMP>
 __device__ __forceinline__ void qmf_tile(const uint8_t* __restrict__ W, int N, int K,
                                          const uint8_t* __restrict__ xq, float* __restrict__ y,
@@ -668,10 +674,195 @@ __device__ __forceinline__ void qmf_tile(const uint8_t* __restrict__ W, int N, i
   }
 }
 
+// ------------------------------------- the MFMA tile for M = 9..16
+//
+// qmf_tile's sums for up to 16 activation rows (Q4_K and IQ4_XS through
+// qdot_qmatmul): the A tile holds two slots of 16 rows, the MFMA of
+// sub-block 2q + jj fills slot jj, so one group of two MFMAs is one quarter,
+// and result register r of lane l holds activation row (8(r/4)) % 16 + 4s +
+// r%4 of sub-block 2q + (8(r/4))/16.  Each lane drains its eight rows into
+// per-quarter fp64 chains in qmf_tile's (and qmv_tile's) order, so rows are
+// bitwise the same for every M = 1..16.
+template <int T, int M, int DEPTH, bool DUMP>
+__device__ __forceinline__ void qmf16_tile(const uint8_t* __restrict__ W, int N, int K,
+                                         const uint8_t* __restrict__ xq, float* __restrict__ y,
+                                         int32_t* __restrict__ isums, int tile, uint8_t* smem) {
+  static_assert(qmf_type<T>(), "the MFMA decode tile takes Q4_K or IQ4_XS weights");
+  static_assert(M <= QMF_MAX_M, "the MFMA decode tile holds at most 16 activation rows");
+  // A-tile geometry: R activation rows per slot, S = 32/R slots, so one group
+  // of S MFMAs covers S consecutive sub-blocks.  With R = 16 (M = 9..16) a
+  // group is two sub-blocks, one quarter; the same code with R = 8 is
+  // qmf_tile's geometry.
+  constexpr int R = qmf_rows<M>();
+  constexpr int S = 32 / R;
+  constexpr int G = 8 / S;          // groups per superblock
+  constexpr int MM = R / 2;         // activation rows per lane (two sets of four)
+  constexpr int NDS = 8 * R / 64;   // scale entries each lane publishes per superblock
+  constexpr int NQ = T == Q4_K ? 4 : 8;  // 16-byte code loads per superblock and lane
+  constexpr int BYTES = Geom<T>::BYTES;
+  constexpr int SUB = Geom<T>::SUB;
+  const int P = blockDim.x >> 6;
+  const int nsb = K / QK;
+  const int nq8 = K / Q8_BLOCK;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 31, s = lane >> 5;
+  const int slot = (lane & 31) / R, mrow = (lane & 31) % R;  // this lane's A row: block slot, activation row
+  const int n0 = tile * QMF_ROWS;
+  const int nrow = n0 + n;
+  const uint8_t* wrow = W + (size_t)(nrow < N ? nrow : N - 1) * nsb * BYTES;
+  // this lane's A data: row mrow.  Rows >= M read row 0 (A data and scales),
+  // so they compute row 0's finite sums, which are never stored: the loop
+  // below is the same code for every M.
+  const uint8_t* xa_row = xq + ((size_t)(mrow < M ? mrow : 0) * nq8 + slot) * Q8_BYTES + 4 + 16 * s;
+  // scale entries this lane publishes per superblock: e = lane + 64u holds
+  // activation row e/8, block e%8
+  const uint8_t* xd_src[NDS];
+#pragma unroll
+  for (int u = 0; u < NDS; ++u) {
+    const int e = lane + 64 * u, dm = e >> 3, dj = e & 7;
+    xd_src[u] = xq + ((size_t)(dm < M ? dm : 0) * nq8 + dj) * Q8_BYTES;
+  }
+  QmfDs* lds_ds = reinterpret_cast<QmfDs*>(smem) + wave * 8 * R;
+
+  double acc[4][MM];  // [quarter][activation row of this lane]
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int mm = 0; mm < MM; ++mm) acc[q][mm] = 0.0;
+
+  // Q4_K: header (d, dmin, scales) and the code bytes of K-slice s of each
+  // quarter (low nibbles sub-block 2q, high 2q+1).  IQ4_XS: header (d,
+  // scales_h, scales_l) and the 16 code bytes of each sub-block (low nibbles
+  // its elements 0-15 = K-slice 0, high nibbles 16-31 = K-slice 1).
+  struct Stage {
+    u32x4 h, q[NQ];
+    u32x4 a[G];       // this lane's A data in each group
+    uint32_t ds[NDS]; // d, s of the published scale entries
+  };
+  Stage St[DEPTH];
+  auto fetch = [&](Stage& st, int bsb) {
+    const int bc = bsb < nsb ? bsb : nsb - 1;
+    const uint8_t* sb = wrow + (size_t)bc * BYTES;
+    st.h = ld16(sb);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+      st.q[q] = T == Q4_K ? ld16(sb + 16 + 32 * q + 16 * s) : ld16(sb + 8 + 16 * q);
+#pragma unroll
+    for (int g = 0; g < G; ++g) st.a[g] = ld16(xa_row + (size_t)(8 * bc + S * g) * Q8_BYTES);
+#pragma unroll
+    for (int u = 0; u < NDS; ++u) st.ds[u] = ld4(xd_src[u] + (size_t)8 * bc * Q8_BYTES);
+  };
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  auto compute = [&](const Stage& st, int b) {
+    wave_sync();  // the previous superblock's scale reads are done
+#pragma unroll
+    for (int u = 0; u < NDS; ++u)
+      lds_ds[lane + 64 * u] = QmfDs{(double)h2f(st.ds[u] & 0xFFFFu), (double)h2f(st.ds[u] >> 16)};
+    wave_sync();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const qmf_v4i a = qmf_v4i{(int)st.a[g].x, (int)st.a[g].y, (int)st.a[g].z, (int)st.a[g].w};
+      const qmf_v4i z4 = {0, 0, 0, 0};
+      qmf_v16i C = {0};
+#pragma unroll
+      for (int jj = 0; jj < S; ++jj) {
+        const int j = S * g + jj;  // sub-block
+        qmf_v4i bq;
+        if constexpr (T == Q4_K) {
+          // sub-block j: quarter j/2, low (j even) or high nibbles
+          const u32x4 v = st.q[j >> 1];
+          const int sh = 4 * (j & 1);
+          bq = qmf_v4i{(int)((v.x >> sh) & 0x0F0F0F0Fu), (int)((v.y >> sh) & 0x0F0F0F0Fu),
+                       (int)((v.z >> sh) & 0x0F0F0F0Fu), (int)((v.w >> sh) & 0x0F0F0F0Fu)};
+        } else {
+          // sub-block j: this lane's K-slice is the low (s = 0) or high
+          // nibbles of its 16 bytes, looked up in the codebook
+          const u32x4 v = st.q[j];
+          const int sh = 4 * s;
+          bq = qmf_v4i{(int)cb_lookup(v.x >> sh, CB0, CB1, CB2, CB3), (int)cb_lookup(v.y >> sh, CB0, CB1, CB2, CB3),
+                       (int)cb_lookup(v.z >> sh, CB0, CB1, CB2, CB3), (int)cb_lookup(v.w >> sh, CB0, CB1, CB2, CB3)};
+        }
+        C = __builtin_amdgcn_mfma_i32_32x32x32_i8(slot == jj ? a : z4, bq, C, 0, 0, 0);
+      }
+#pragma unroll
+      for (int jj = 0; jj < S; ++jj) {
+        const int j = S * g + jj;
+        // scale (and Q4_K min) of sub-block j, as qmv_tile's decode_sub computes them
+        double wsc, wmn = 0.0;
+        if constexpr (T == Q4_K) {
+          const int sh = 8 * (j & 3);
+          const uint32_t Ys = st.h.y >> sh, Zs = st.h.z >> sh, Ws = st.h.w >> sh;
+          const uint32_t sc = j < 4 ? (Ys & 63u) : ((Ws & 15u) | ((Ys >> 2) & 0x30u));
+          const uint32_t mn = j < 4 ? (Zs & 63u) : (((Ws >> 4) & 15u) | ((Zs >> 2) & 0x30u));
+          wsc = (double)(h2f(st.h.x) * (float)sc);
+          wmn = -(double)(h2f(st.h.x >> 16) * (float)mn);
+        } else {
+          const uint32_t sl = (st.h.y >> (4 * j)) & 15u;
+          const uint32_t shb = ((st.h.x >> 16) >> (2 * j)) & 3u;
+          const int ls = (int)(sl | (shb << 4));
+          wsc = (double)(h2f(st.h.x) * (float)(ls - 32));  // d*(ls-32), exact in fp32
+        }
+        // Result register r of lane l holds A row 8(r/4) + 4s + r%4, i.e.
+        // slot (8(r/4))/R -- the registers of slot jj carry sub-block j --
+        // and activation row m = (8(r/4)) % R + 4s + r%4.
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if ((8 * (r >> 2)) / R != jj) continue;
+          const int mm = (((8 * (r >> 2)) % R) >> 1) + (r & 3);   // 0..MM-1
+          const int m = (8 * (r >> 2)) % R + 4 * s + (r & 3);
+          const QmfDs e = lds_ds[m * 8 + j];
+          const int I = C[r];
+          acc[j >> 1][mm] = fma(wsc * e.d, (double)I, acc[j >> 1][mm]);
+          if constexpr (T == Q4_K) acc[j >> 1][mm] = fma(wmn, e.s, acc[j >> 1][mm]);
+          if (DUMP && m < M && nrow < N)
+            isums[((size_t)m * N + nrow) * (K / SUB) + (size_t)b * (QK / SUB) + j] = I;
+        }
+      }
+    }
+  };
+
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) fetch(St[d], wave + d * P);
+  const int niter = (((nsb + P - 1) / P) + DEPTH - 1) / DEPTH * DEPTH;
+  auto step = [&](Stage& st, int ii, bool refill) {
+    const int b = wave + ii * P;
+    if (b < nsb) compute(st, b);
+    if (refill) fetch(st, b + DEPTH * P);
+  };
+  int i = 0;
+  for (; i + DEPTH < niter; i += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) step(St[d], i + d, true);
+  }
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) step(St[d], i + d, false);
+
+  // quarters in qmv_tile's order ((q0 + q1) + (q2 + q3)), then the waves in order
+  double* red = reinterpret_cast<double*>(smem);
+  __syncthreads();  // the staging area is reused for the reduction
+#pragma unroll
+  for (int mm = 0; mm < MM; ++mm) {
+    const int m = 8 * (mm >> 2) + 4 * s + (mm & 3);
+    if (m < M) red[(wave * QMF_ROWS + n) * M + m] = (acc[0][mm] + acc[1][mm]) + (acc[2][mm] + acc[3][mm]);
+  }
+  __syncthreads();
+  for (int o = tid; o < QMF_ROWS * M; o += 64 * P) {
+    const int m = o % M, r = o / M;
+    double v = red[r * M + m];
+    for (int w = 1; w < P; ++w) v += red[(w * QMF_ROWS + r) * M + m];
+    if (n0 + r < N) y[(size_t)m * N + n0 + r] = (float)v;
+  }
+}
+
 // LDS bytes of a workgroup of `waves` waves running the MFMA tile (mfma) or
 // the dot4 tile.
 template <int M> inline size_t qmv_lds_bytes_tile(bool mfma, int waves) {
-  const size_t stage = (size_t)waves * (mfma ? 64 * sizeof(QmfDs) : (size_t)8 * M * (Q8_BLOCK + sizeof(DsEntry)));
+  const size_t stage = (size_t)waves * (mfma ? (size_t)8 * qmf_rows<M>() * sizeof(QmfDs)
+                                             : (size_t)8 * M * (Q8_BLOCK + sizeof(DsEntry)));
   const size_t red = (size_t)waves * (mfma ? QMF_ROWS : QMV_SLOTS) * M * sizeof(double);
   return stage > red ? stage : red;
 }
@@ -684,7 +875,9 @@ __global__ __launch_bounds__(QMV_MAX_THREADS) void qmv_kernel(
     const uint8_t* __restrict__ W, int N, int K, const uint8_t* __restrict__ xq,
     float* __restrict__ y, int32_t* __restrict__ isums) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  if constexpr (qmf_ok<T, M>())
+  if constexpr (M > 8)
+    qmf16_tile<T, M, DEPTH, DUMP>(W, N, K, xq, y, isums, blockIdx.x, smem);
+  else if constexpr (qmf_ok<T, M>())
     qmf_tile<T, M, DEPTH, DUMP>(W, N, K, xq, y, isums, blockIdx.x, smem);
   else
     qmv_tile<T, M, DEPTH, DUMP>(W, N, K, xq, y, isums, blockIdx.x, smem);

@@ -60,7 +60,11 @@ def test_names_and_status(lib):
     assert qd.qdot_kernel_name(qd.QDOT_Q4_0, 100) == "qmm_mfma<Q4_0>"
     assert qd.qdot_kernel_name(qd.QDOT_Q8_0, 16) == "qmm_skinny<Q8_0>"
     assert qd.qdot_kernel_name(qd.QDOT_Q6_K, 512) == "qmm_mfma<Q6_K>"
-    assert qd.qdot_kernel_name(qd.QDOT_Q4_K, 9) == "qmm_skinny<Q4_K>"
+    assert qd.qdot_kernel_name(qd.QDOT_Q4_K, 9) == "qmv_mfma<Q4_K,9>"
+    assert qd.qdot_kernel_name(qd.QDOT_IQ4_XS, 16) == "qmv_mfma<IQ4_XS,16>"
+    assert qd.qdot_kernel_name(qd.QDOT_Q4_K, 17) == "qmm_skinny<Q4_K>"
+    assert qd.qdot_kernel_name(qd.QDOT_Q6_K, 9) == "qmm_skinny<Q6_K>"
+    assert qd.qdot_kernel_name(qd.QDOT_Q4_0, 9) == "qmm_skinny<Q4_0>"
     assert qd.qdot_kernel_name(qd.QDOT_IQ4_XS, 96) == "qmm_skinny<IQ4_XS>"
     assert qd.qdot_kernel_name(qd.QDOT_Q4_K, 97) == "qmm_mfma<Q4_K>"
     assert qd.qdot_kernel_name(9, 1) == "invalid"
@@ -85,10 +89,14 @@ def test_names_and_status(lib):
     assert ks(qd.QDOT_Q4_0, 12288, 4096, 96) == "qmm_skinny<Q4_0>"
     assert ks(qd.QDOT_Q4_0, 1024, 4096, 97) == "qmm_mfma<Q4_0>"
     assert ks(qd.QDOT_Q4_K, 12288, 4096, 8) == "qmv_mfma<Q4_K,8>"
+    assert ks(qd.QDOT_Q4_K, 12288, 4096, 16) == "qmv_mfma<Q4_K,16>"
+    assert ks(qd.QDOT_Q4_K, 12288, 4096, 17) == "qmm_skinny<Q4_K>"
+    assert ks(qd.QDOT_IQ4_XS, 17408, 5120, 13) == "qmv_mfma<IQ4_XS,13>"
+    assert ks(qd.QDOT_Q6_K, 12288, 4096, 9) == "qmm_skinny<Q6_K>"
     assert ks(qd.QDOT_Q4_K, 12288, 4096, 97) == "qmm_mfma<Q4_K>"
     assert ks(qd.QDOT_Q4_K, 12288, 100, 40) == "invalid"
     for t in (qd.QDOT_Q4_K, qd.QDOT_IQ4_XS, qd.QDOT_Q4_0, qd.QDOT_Q8_0):
-        for M in (1, 5, 8, 9, 33, 49, 96, 97, 512):
+        for M in (1, 5, 8, 9, 16, 17, 33, 49, 96, 97, 512):
             assert ks(t, 4096, 4096, M) == qd.qdot_kernel_name(t, M)
     for M in (1, 5, 8, 9, 96, 512):
         assert ks(qd.QDOT_Q6_K, 4096, 4096, M) == qd.qdot_kernel_name(qd.QDOT_Q6_K, M)
@@ -104,6 +112,8 @@ def test_names_and_status(lib):
     assert mk(*([qd.QDOT_Q4_K, qd.QDOT_Q4_K], [8960, 8960]), 1536, 8, 0) == "qmv_dot4<Q4_K,8>"
     assert mk(*([qd.QDOT_IQ4_XS] * 2, [17408, 17408]), 5120, 4, 0) == "qmv_mfma<IQ4_XS,4>"
     assert mk(*gu, 4096, 64, 0) == "qmm_mfma<Q4_K>"
+    assert mk(*gu, 4096, 12, 1) == "qmv_mfma<Q4_K,12>"
+    assert mk(*gu, 4096, 17, 1) == "qmm_skinny<Q4_K>"
     assert mk(*gu, 4096, 1, 2) == "invalid"
     assert mk(*([qd.QDOT_Q4_K, 9], [64, 64]), 4096, 1, 0) == "invalid"
     assert qd.qdot_status_str(qd.QDOT_E_ALIGN) == "misaligned pointer"

@@ -4,7 +4,7 @@ Bars: Q8_1 bytes bit-exact; integer sub-block sums bit-exact (debug dump);
 fp32 y within relative 1e-5 of the oracle's fp64 result on every output;
 y fully written (NaN-poisoned before each call); bitwise determinism and
 batch invariance (row m of y is identical for every M within one kernel's
-range: 1..8, 9..96, above 96).
+range: 1..8 (1..16 for Q4_K and IQ4_XS), then up to 96, above 96).
 """
 import numpy as np
 import pytest
@@ -18,6 +18,11 @@ from gpu_util import assert_close, qmatmul, quantize, to_dev
 pytestmark = pytest.mark.gpu
 TYPES = [synth.Q4_K, synth.Q6_K, synth.IQ4_XS, synth.Q4_0, synth.Q8_0]
 TN = synth.TYPE_NAMES
+
+
+def mid_lo(wtype):
+    """Smallest M that runs the mid-batch kernel for this type."""
+    return 17 if wtype in (synth.Q4_K, synth.IQ4_XS) else 9
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -195,6 +200,56 @@ def test_qmatmul_m_above_8(wtype, M):
     assert_close(y, y64, f"{TN[wtype]} M={M}")
 
 
+# ------------------------------ the MFMA decode tile at M = 9..16 (Q4_K, IQ4_XS)
+@pytest.mark.parametrize("wtype", [synth.Q4_K, synth.IQ4_XS])
+@pytest.mark.parametrize("N,K", [(37, 256), (300, 4608), (129, 5120)])
+def test_decode16_rows_and_isums(wtype, N, K):
+    """Q4_K and IQ4_XS keep the MFMA decode tile up to M = 16 (16-row A-tile
+    slots): sub-block sums bit-exact through the dump at M = 9, 12 and 16,
+    every output within 1e-5 rel, and every row bitwise the one of M = 1..8
+    (ragged tiles of N, K split unevenly over the waves)."""
+    W = synth.weights(wtype, N, K, (2026, 76, wtype, N, K))
+    Wd = to_dev(W)
+    x = synth.activations(16, K, (2026, 76, K, 16, 7))
+    xqd, xq = quantize(x)
+    y64, _, _ = oracle.qmatmul(W, wtype, N, K, xq, 16)
+    is_all = oracle.isums(W, wtype, N, K, xq, 16)
+    y16, _ = qmatmul(Wd, wtype, N, K, xqd, 16)
+    assert_close(y16, y64, f"{TN[wtype]} {N}x{K} M=16")
+    for M in range(1, 17):
+        assert qd.qdot_kernel_name_shape(wtype, N, K, M).startswith("qmv_")
+        xm = xqd[: qd.qdot_q8_1_bytes(M, K)]
+        if M in (9, 12, 16):
+            y, isums = qmatmul(Wd, wtype, N, K, xm, M, dump=True)
+            assert np.array_equal(isums, is_all[:M]), f"M={M}: isums differ"
+        else:
+            y, _ = qmatmul(Wd, wtype, N, K, xm, M)
+        assert np.array_equal(y.view(np.uint32), y16[:M].view(np.uint32)), f"M={M}: rows differ from M=16"
+
+
+DEC16_FULL = [(name, N, K, t) for (name, N, K, t) in synth.QWEN3_8B + synth.IQ4XS_H5120
+              if t in (synth.Q4_K, synth.IQ4_XS)]
+
+
+@pytest.mark.parametrize("name,N,K,wtype", DEC16_FULL)
+def test_decode16_full_size_sampled(name, N, K, wtype):
+    """M = 16 on the MFMA decode tile at the full projection shapes: sampled
+    rows against the oracle, rows of M = 13 and M = 1 bitwise equal to them."""
+    M = 16
+    W = synth.weights(wtype, N, K, (2026, 77, N, K))
+    Wd = to_dev(W)
+    x = synth.activations(M, K, (2026, 77, K, M, 7))
+    xqd, xq = quantize(x)
+    y, _ = qmatmul(Wd, wtype, N, K, xqd, M)
+    rng = np.random.default_rng(N + K + 3)
+    rows = np.unique(np.concatenate([rng.integers(0, N, 24), [0, N - 1]]))
+    y64, _ = oracle.qmatmul_rows(W, wtype, N, K, xq, M, rows)
+    assert_close(y[:, rows], y64, f"{name} {N}x{K} M={M}")
+    for Mp in (13, 1):
+        yp, _ = qmatmul(Wd, wtype, N, K, xqd[: qd.qdot_q8_1_bytes(Mp, K)], Mp)
+        assert np.array_equal(yp.view(np.uint32), y[:Mp].view(np.uint32)), f"M={Mp} vs M=16"
+
+
 # ------------------------------------------------- mid-batch (8 < M <= 96)
 @pytest.mark.parametrize("wtype", TYPES)
 def test_mid_batch_parity_and_invariance(wtype):
@@ -212,26 +267,30 @@ def test_mid_batch_parity_and_invariance(wtype):
     y64, _, _ = oracle.qmatmul(W, wtype, N, K, xq[:M * row], M)
     assert_close(y, y64, f"{TN[wtype]} M={M}")
     ym96, _ = qmatmul(Wd, wtype, N, K, xqd, 96)
-    y9, _ = qmatmul(Wd, wtype, N, K, xqd, 9)
+    lo = mid_lo(wtype)
+    ylo, _ = qmatmul(Wd, wtype, N, K, xqd, lo)
+    assert qd.qdot_kernel_name_shape(wtype, N, K, lo).startswith("qmm_skinny")
     assert np.array_equal(ym96[:M].view(np.uint32), y.view(np.uint32)), "M=96 vs M=27"
-    assert np.array_equal(y9.view(np.uint32), y[:9].view(np.uint32)), "M=9 vs M=27"
+    assert np.array_equal(ylo.view(np.uint32), y[:lo].view(np.uint32)), f"M={lo} vs M=27"
 
 
-@pytest.mark.parametrize("wtype", [synth.Q4_K, synth.Q6_K])
-def test_mid_batch_tile_width_invariance(wtype):
-    """N = 4096: M = 16 runs one 16-row weight tile per wave, M = 17 two (the
-    grid reaches 144 workgroups); the shared rows are bitwise equal and both
-    calls match the oracle."""
-    N, K = 4096, 512
+@pytest.mark.parametrize("wtype,N,Mlo", [(synth.Q4_K, 2048, 32), (synth.Q6_K, 4096, 16)])
+def test_mid_batch_tile_width_invariance(wtype, N, Mlo):
+    """Mlo runs one 16-row weight tile per wave, Mlo + 1 two (the grid reaches
+    144 workgroups); the shared rows are bitwise equal and both calls match
+    the oracle."""
+    K, Mhi = 512, Mlo + 1
     W = synth.weights(wtype, N, K, (2026, 73, wtype))
     Wd = to_dev(W)
-    x = synth.activations(17, K, (2026, 73, K, 17, 7))
+    x = synth.activations(Mhi, K, (2026, 73, K, Mhi, 7))
     xqd, xq = quantize(x)
-    y17, _ = qmatmul(Wd, wtype, N, K, xqd, 17)
-    y16, _ = qmatmul(Wd, wtype, N, K, xqd, 16)
-    assert np.array_equal(y16.view(np.uint32), y17[:16].view(np.uint32))
-    y64, _, _ = oracle.qmatmul(W, wtype, N, K, xq, 17)
-    assert_close(y17, y64, f"{TN[wtype]} N={N} M=17")
+    assert qd.qdot_kernel_name_shape(wtype, N, K, Mlo).startswith("qmm_skinny")
+    assert qd.qdot_kernel_name_shape(wtype, N, K, Mhi).startswith("qmm_skinny")
+    yhi, _ = qmatmul(Wd, wtype, N, K, xqd, Mhi)
+    ylo, _ = qmatmul(Wd, wtype, N, K, xqd[: qd.qdot_q8_1_bytes(Mlo, K)], Mlo)
+    assert np.array_equal(ylo.view(np.uint32), yhi[:Mlo].view(np.uint32))
+    y64, _, _ = oracle.qmatmul(W, wtype, N, K, xq, Mhi)
+    assert_close(yhi, y64, f"{TN[wtype]} N={N} M={Mhi}")
 
 
 MID_FULL = [(name, N, K, t) for (name, N, K, t) in synth.QWEN3_8B] + \
@@ -242,7 +301,8 @@ MID_FULL = [(name, N, K, t) for (name, N, K, t) in synth.QWEN3_8B] + \
 @pytest.mark.parametrize("name,N,K,wtype", MID_FULL)
 def test_mid_batch_full_size_sampled(name, N, K, wtype):
     """M = 32 at the full projection shapes: sampled weight rows against the
-    oracle, and the rows of an M = 9 call bitwise equal to them."""
+    oracle, and the rows of a call at the lowest mid-batch M bitwise equal to
+    them."""
     M = 32
     W = synth.weights(wtype, N, K, (2026, 74, N, K))
     Wd = to_dev(W)
@@ -253,8 +313,9 @@ def test_mid_batch_full_size_sampled(name, N, K, wtype):
     rows = np.unique(np.concatenate([rng.integers(0, N, 24), [0, N - 1]]))
     y64, _ = oracle.qmatmul_rows(W, wtype, N, K, xq, M, rows)
     assert_close(y[:, rows], y64, f"{name} {N}x{K} M={M}")
-    y9, _ = qmatmul(Wd, wtype, N, K, xqd[: qd.qdot_q8_1_bytes(9, K)], 9)
-    assert np.array_equal(y9.view(np.uint32), y[:9].view(np.uint32)), "M invariance"
+    lo = mid_lo(wtype)
+    ylo, _ = qmatmul(Wd, wtype, N, K, xqd[: qd.qdot_q8_1_bytes(lo, K)], lo)
+    assert np.array_equal(ylo.view(np.uint32), y[:lo].view(np.uint32)), "M invariance"
 
 
 @pytest.mark.parametrize("wtype,N,K,M_switch", [(synth.Q4_K, 8192, 4096, 32), (synth.IQ4_XS, 8192, 4096, 48),
@@ -263,8 +324,8 @@ def test_mid_batch_full_size_sampled(name, N, K, wtype):
 def test_matrix_kernel_switch(wtype, N, K, M_switch):
     """The mid-batch kernel's range depends on the matrix (qdot_kernel_name_shape
     says which kernel runs): sampled rows on both sides of the switch against
-    the oracle, and rows bitwise equal for every M within each side (M = 9 vs
-    M_switch, M_switch + 1 vs M_switch + 40)."""
+    the oracle, and rows bitwise equal for every M within each side (the lowest
+    mid-batch M vs M_switch, M_switch + 1 vs M_switch + 40)."""
     Mmax = M_switch + 40
     W = synth.weights(wtype, N, K, (2026, 75, wtype, N, K))
     Wd = to_dev(W)
@@ -274,12 +335,13 @@ def test_matrix_kernel_switch(wtype, N, K, M_switch):
     assert qd.qdot_kernel_name_shape(wtype, N, K, M_switch + 1).startswith("qmm_mfma")
     rows = np.unique(np.concatenate([np.random.default_rng(N + 5).integers(0, N, 12), [0, N - 1]]))
     ys = {}
-    for M in (9, M_switch, M_switch + 1, Mmax):
+    lo = mid_lo(wtype)
+    for M in (lo, M_switch, M_switch + 1, Mmax):
         y, _ = qmatmul(Wd, wtype, N, K, xqd[: qd.qdot_q8_1_bytes(M, K)], M)
         y64, _ = oracle.qmatmul_rows(W, wtype, N, K, xq[: qd.qdot_q8_1_bytes(M, K)], M, rows)
         assert_close(y[:, rows], y64, f"{TN[wtype]} {N}x{K} M={M}")
         ys[M] = y
-    assert np.array_equal(ys[9].view(np.uint32), ys[M_switch][:9].view(np.uint32)), "mid-batch rows"
+    assert np.array_equal(ys[lo].view(np.uint32), ys[M_switch][:lo].view(np.uint32)), "mid-batch rows"
     s1 = M_switch + 1
     assert np.array_equal(ys[s1].view(np.uint32), ys[Mmax][:s1].view(np.uint32)), "prefill rows"
 
