@@ -60,6 +60,8 @@ def lib():
         L.oracle_qmatmul_rows.restype = ctypes.c_int
         L.oracle_rmsnorm.argtypes = [P, P, ctypes.c_float, i64, i64, P, P]
         L.oracle_rmsnorm.restype = None
+        L.oracle_attn_decode_kv4.argtypes = [P, i64, P, P, i64, i64, i64, ctypes.c_double, P, P]
+        L.oracle_attn_decode_kv4.restype = ctypes.c_int
         L.oracle_codebook.argtypes = []
         L.oracle_codebook.restype = ctypes.POINTER(ctypes.c_int)
         _lib = L
@@ -174,3 +176,25 @@ def qmatmul_rows(W, wtype, N, K, xq, M, rows):
     if rc:
         raise ValueError("oracle_qmatmul_rows: bad arguments")
     return y64, ab
+
+
+def kv4_row_bytes(D):
+    """Bytes of one K or V row of D elements: D/32 Q4_0 blocks of 18 bytes."""
+    return D // 32 * 18
+
+
+def attn_decode_kv4(q_q8, Hq, Kc, Vc, Hkv, T, D, scale):
+    """One decode step of attention over the int4 KV cache (oracle.c,
+    oracle_attn_decode_kv4: xLLM v0.7 section C.3, Kestrel #18 online-softmax
+    decode).  q_q8: Q8_1 blocks [Hq][D/32]; Kc, Vc: uint8 [Hkv][T][D/32*18].
+    Returns (out fp64 [Hq][D], scores fp64 [Hq][T])."""
+    q_q8, Kc, Vc = _u8(q_q8), _u8(Kc), _u8(Vc)
+    assert q_q8.size == Hq * (D // 32) * 36
+    assert Kc.size == Hkv * T * kv4_row_bytes(D) and Vc.size == Kc.size
+    out = np.empty((Hq, D), dtype=np.float64)
+    sc = np.empty((Hq, T), dtype=np.float64)
+    rc = lib().oracle_attn_decode_kv4(_ptr(q_q8), Hq, _ptr(Kc), _ptr(Vc), Hkv, T, D,
+                                      float(scale), _ptr(out), _ptr(sc))
+    if rc:
+        raise ValueError("oracle_attn_decode_kv4: bad arguments")
+    return out, sc

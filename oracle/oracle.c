@@ -1,7 +1,8 @@
 /*
  * oracle.c -- plain, slow, obviously-correct CPU oracle for the block-quantized
  * integer-dot matmul (Q8_1 activations x Q4_K / Q6_K / IQ4_XS / Q4_0 / Q8_0
- * weights -> fp32).
+ * weights -> fp32), and for one decode step of attention over a 4-bit KV
+ * cache (oracle_attn_decode_kv4, at the end of this file).
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  The product path (the
@@ -522,5 +523,73 @@ int oracle_qmatmul_rows(const uint8_t *W, int type, int64_t N, int64_t K,
   }
   free(t64);
   free(tab);
+  return 0;
+}
+
+/* ------------------------------------------------ int4-KV decode attention */
+
+/* One decode step of attention over a 4-bit KV cache (xLLM v0.7 log, section
+ * C.3: the long-context path runs paged attention with int4 K/V dot products
+ * over the whole context; Kestrel_VLLM #18, the online-softmax decode kernel:
+ * the query is quantized to int8, Q.K is an int32 dot, then softmax and a
+ * sequential P.V sum).  The pages do not print the int4 KV layout.  Readings:
+ *   - K and V rows of D elements are D/32 Q4_0 blocks (the pages' simplest
+ *     4-bit block: fp16 d, 16 bytes of nibbles, element i low nibble of byte
+ *     i, element 16 + i high nibble, value d * (q - 8));
+ *   - the cache is [Hkv][T][D/32 blocks]; query head h reads KV head
+ *     h / (Hq / Hkv) (grouped-query attention, consecutive heads share);
+ *   - the query is Q8_1 blocks [Hq][D/32] (the activation quantizer above);
+ *   - score s_t = scale * sum_b dK_b * D_b * I_b, I_b the exact integer dot
+ *     of block b's codes (q - 8) with the query's int8 codes; no mask.
+ * Then, per query head, in fp64 and in token order:
+ *   m = max_t s_t;  p_t = exp(s_t - m);  l = sum_t p_t;
+ *   out[d] = (sum_t p_t * v_t[d]) / l,  v_t[d] = dV * (q - 8).
+ * scores (optional) receives s [Hq][T]; out is fp64 [Hq][D].  Returns 0, or
+ * -1 for bad arguments (T < 1, D % 32, Hq % Hkv). */
+int oracle_attn_decode_kv4(const uint8_t *q_q8, int64_t Hq, const uint8_t *Kc,
+                           const uint8_t *Vc, int64_t Hkv, int64_t T, int64_t D,
+                           double scale, double *out, double *scores) {
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv || T < 1 || D < 32 || D % 32) return -1;
+  const int64_t nb = D / 32, row = nb * 18, G = Hq / Hkv;
+  double *s = (double *)malloc(sizeof(double) * (size_t)T);
+  if (!s) return -2;
+  for (int64_t h = 0; h < Hq; ++h) {
+    const int64_t g = h / G;
+    const uint8_t *qh = q_q8 + h * nb * OR_Q8_BYTES;
+    const uint8_t *Kh = Kc + g * T * row, *Vh = Vc + g * T * row;
+    for (int64_t t = 0; t < T; ++t) {
+      double acc = 0.0;
+      for (int64_t b = 0; b < nb; ++b) {
+        const uint8_t *kb = Kh + t * row + b * 18, *qb = qh + b * OR_Q8_BYTES;
+        int64_t I = 0;
+        for (int i = 0; i < 16; ++i) {
+          I += (int64_t)((kb[2 + i] & 15) - 8) * (int8_t)qb[4 + i];
+          I += (int64_t)((kb[2 + i] >> 4) - 8) * (int8_t)qb[4 + 16 + i];
+        }
+        acc += oracle_half_to_double(rd16(kb)) * oracle_half_to_double(rd16(qb)) * (double)I;
+      }
+      s[t] = scale * acc;
+      if (scores) scores[h * T + t] = s[t];
+    }
+    double m = s[0];
+    for (int64_t t = 1; t < T; ++t)
+      if (s[t] > m) m = s[t];
+    double l = 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+      s[t] = exp(s[t] - m);
+      l += s[t];
+    }
+    for (int64_t d = 0; d < D; ++d) {
+      const int64_t b = d / 32, i = d % 32;
+      double o = 0.0;
+      for (int64_t t = 0; t < T; ++t) {
+        const uint8_t *vb = Vh + t * row + b * 18;
+        const int code = i < 16 ? (vb[2 + i] & 15) : (vb[2 + i - 16] >> 4);
+        o += s[t] * (oracle_half_to_double(rd16(vb)) * (double)(code - 8));
+      }
+      out[h * D + d] = o / l;
+    }
+  }
+  free(s);
   return 0;
 }

@@ -98,6 +98,25 @@ def weights(wtype, N, K, seed):
     return raw.reshape(N, nb * B)
 
 
+def kv4_row_bytes(D):
+    """Bytes of one K or V row of D elements in the 4-bit KV cache."""
+    return D // 32 * 18
+
+
+def kv4_cache(Hkv, T, D, seed, dscale=0.08):
+    """4-bit KV cache, uint8 [Hkv][T][D/32 * 18]: per row D/32 blocks of an
+    fp16 scale d ~ |N(0, dscale^2)| + dscale/4 and 16 bytes of random
+    nibbles (values d * (q - 8), so elements up to about +-1 as in a model's
+    K and V)."""
+    assert D % 32 == 0 and T >= 1 and Hkv >= 1
+    rng = rng_for(*seed)
+    nb = D // 32
+    raw = np.frombuffer(rng.bytes(Hkv * T * nb * 18), dtype=np.uint8).reshape(Hkv, T, nb, 18).copy()
+    d = np.abs(rng.standard_normal((Hkv, T, nb))) * dscale + dscale / 4
+    raw[:, :, :, 0:2] = _half_bytes(d).reshape(Hkv, T, nb, 2)
+    return raw.reshape(Hkv, T, nb * 18)
+
+
 def activations(M, K, seed):
     """fp32 [M][K] ~ N(0, 1)."""
     rng = rng_for(*seed)
