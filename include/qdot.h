@@ -169,6 +169,49 @@ int qdot_qmatmul_multi(int n, const void *const *W, const int *types,
 int qdot_rmsnorm_quantize_q8_1(const float *x, const float *w, float eps,
                                int64_t M, int64_t K, void *x_q8, void *stream);
 
+/* One decode step of attention over a 4-bit KV cache (the long-context path
+ * of the xLLM v0.7 log, section C.3: paged attention with int4 K/V dot
+ * products over the whole context, whose cache misses L2 and streams from
+ * HBM every step; the integer Q.K of the Kestrel_VLLM #18 decode kernel, an
+ * int8 query with an int32 dot product, then softmax and the P.V sum).
+ * Layout (the pages print none; the reading): a K or V row of D elements is
+ * D/32 Q4_0 blocks of 18 bytes (binary16 d, then 16 bytes; byte i holds
+ * element i in its low nibble and element 16 + i in its high nibble; value
+ * d * (q - 8)); Kc and Vc are [Hkv][T][row] (device, 8-byte aligned);
+ * q_q8 is the query as Q8_1 blocks [Hq][D/32] (qdot_quantize_q8_1 of the
+ * fp32 query [Hq][D]); query head h reads KV head h / (Hq / Hkv).
+ *   s_t = scale * sum_b dK_b * D_b * I_b   (I_b the exact int32 dot of block
+ *         b's codes q - 8 with the query's codes; the products exact, the
+ *         blocks summed in fp64, rounded once to fp32)
+ *   out[h][d] = sum_t e^(s_t - max s) v_t[d] / sum_t e^(s_t - max s)
+ * in fp32 (expf; the context split in chunks of 256 tokens combined in
+ * order), out fp32 [Hq][D] (device).  workspace: device scratch of at least
+ * qdot_attn_kv4_workspace_bytes(Hq, T) bytes, 4-byte aligned, owned by the
+ * caller and overwritten (calls on one workspace must not overlap).  No mask:
+ * every one of the T tokens is attended.  Errors: QDOT_E_ARG for a null
+ * pointer, D != QDOT_ATTN_HEAD_DIM, Hq % Hkv != 0, Hq / Hkv >
+ * QDOT_ATTN_MAX_GROUP, Hq > QDOT_ATTN_MAX_HEADS, T outside 1..QDOT_ATTN_MAX_T,
+ * a non-finite scale or a short workspace; QDOT_E_ALIGN for Kc, Vc not 8-byte
+ * or q_q8, out, workspace not 4-byte aligned; QDOT_E_HIP if a launch fails. */
+#define QDOT_ATTN_HEAD_DIM 128
+#define QDOT_ATTN_MAX_GROUP 8
+#define QDOT_ATTN_MAX_HEADS 4096
+#define QDOT_ATTN_MAX_T (1 << 26)
+int qdot_attn_decode_kv4(const void *q_q8, int64_t Hq, const void *Kc,
+                         const void *Vc, int64_t Hkv, int64_t T, int64_t D,
+                         float scale, float *out, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/* Bytes of one K or V row of D elements in qdot_attn_decode_kv4's cache
+ * (D/32 blocks of 18 bytes); 0 unless D is a multiple of 32 in
+ * 32..QDOT_ATTN_HEAD_DIM. */
+size_t qdot_attn_kv4_row_bytes(int64_t D);
+
+/* Workspace bytes qdot_attn_decode_kv4 needs for Hq query heads over T
+ * tokens (per head and 256-token chunk: a max, a sum and D partial
+ * outputs, fp32); 0 for Hq or T out of range. */
+size_t qdot_attn_kv4_workspace_bytes(int64_t Hq, int64_t T);
+
 /* Static text for a status code. */
 const char *qdot_status_str(int status);
 

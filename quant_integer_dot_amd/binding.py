@@ -58,6 +58,12 @@ def load():
     L.qdot_qmatmul_multi.restype = i32
     L.qdot_rmsnorm_quantize_q8_1.argtypes = [P, P, ctypes.c_float, i64, i64, P, P]
     L.qdot_rmsnorm_quantize_q8_1.restype = i32
+    L.qdot_attn_decode_kv4.argtypes = [P, i64, P, P, i64, i64, i64, ctypes.c_float, P, P, ctypes.c_size_t, P]
+    L.qdot_attn_decode_kv4.restype = i32
+    L.qdot_attn_kv4_row_bytes.argtypes = [i64]
+    L.qdot_attn_kv4_row_bytes.restype = ctypes.c_size_t
+    L.qdot_attn_kv4_workspace_bytes.argtypes = [i64, i64]
+    L.qdot_attn_kv4_workspace_bytes.restype = ctypes.c_size_t
     L.qdot_status_str.argtypes = [i32]
     L.qdot_status_str.restype = ctypes.c_char_p
     L.qdot_kernel_name.argtypes = [i32, i64]
@@ -150,6 +156,21 @@ def qdot_qmatmul_dump_isums(W, wtype, N, K, x_q8, M, y, isums, stream=None):
     s = _stream(stream, W, x_q8, y, isums)
     _check(load().qdot_qmatmul_dump_isums(_addr(W), wtype, N, K, _addr(x_q8), M, _addr(y),
                                           _addr(isums), s), "qdot_qmatmul_dump_isums")
+
+
+def qdot_attn_kv4_row_bytes(D):
+    return load().qdot_attn_kv4_row_bytes(D)
+
+
+def qdot_attn_kv4_workspace_bytes(Hq, T):
+    return load().qdot_attn_kv4_workspace_bytes(Hq, T)
+
+
+def qdot_attn_decode_kv4(q_q8, Hq, Kc, Vc, Hkv, T, D, scale, out, workspace, workspace_bytes, stream=None):
+    st = _stream(stream, out)
+    _check(load().qdot_attn_decode_kv4(_addr(q_q8), Hq, _addr(Kc), _addr(Vc), Hkv, T, D, float(scale),
+                                        _addr(out), _addr(workspace), int(workspace_bytes), st),
+           "qdot_attn_decode_kv4")
 
 
 def qdot_status_str(status):

@@ -222,3 +222,37 @@ def test_binding_multi_lengths(lib):
 def test_rmsnorm_quantize_validation(lib, args, status):
     x, w, eps, M, K, xq = args
     assert lib.qdot_rmsnorm_quantize_q8_1(x, w, eps, M, K, xq, None) == status
+
+
+def test_attn_sizes(lib):
+    assert qd.qdot_attn_kv4_row_bytes(128) == 72
+    assert qd.qdot_attn_kv4_row_bytes(64) == 36
+    assert qd.qdot_attn_kv4_row_bytes(100) == 0 and qd.qdot_attn_kv4_row_bytes(256) == 0
+    # per head and 256-token chunk: max, sum and 128 partial outputs (fp32)
+    assert qd.qdot_attn_kv4_workspace_bytes(32, 32768) == 32 * 128 * 130 * 4
+    assert qd.qdot_attn_kv4_workspace_bytes(4, 257) == 4 * 2 * 130 * 4
+    assert qd.qdot_attn_kv4_workspace_bytes(4, 0) == 0 and qd.qdot_attn_kv4_workspace_bytes(0, 8) == 0
+
+
+WS = 1 << 20
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 32, FAKE, FAKE, 8, 100, 128, 0.1, FAKE, FAKE, WS), qd.QDOT_E_ARG),        # null query
+    ((FAKE, 32, FAKE, FAKE, 8, 100, 128, 0.1, FAKE, 0, WS), qd.QDOT_E_ARG),        # null workspace
+    ((FAKE, 32, FAKE, FAKE, 8, 100, 64, 0.1, FAKE, FAKE, WS), qd.QDOT_E_ARG),      # D != 128
+    ((FAKE, 30, FAKE, FAKE, 8, 100, 128, 0.1, FAKE, FAKE, WS), qd.QDOT_E_ARG),     # Hq % Hkv
+    ((FAKE, 32, FAKE, FAKE, 2, 100, 128, 0.1, FAKE, FAKE, WS), qd.QDOT_E_ARG),     # group of 16
+    ((FAKE, 32, FAKE, FAKE, 8, 0, 128, 0.1, FAKE, FAKE, WS), qd.QDOT_E_ARG),       # T = 0
+    ((FAKE, 32, FAKE, FAKE, 8, 2**26 + 1, 128, 0.1, FAKE, FAKE, 2**40), qd.QDOT_E_ARG),  # T too large
+    ((FAKE, 32, FAKE, FAKE, 8, 100, 128, float("nan"), FAKE, FAKE, WS), qd.QDOT_E_ARG),  # NaN scale
+    ((FAKE, 32, FAKE, FAKE, 8, 100, 128, float("inf"), FAKE, FAKE, WS), qd.QDOT_E_ARG),  # inf scale
+    ((FAKE, 32, FAKE, FAKE, 8, 300, 128, 0.1, FAKE, FAKE, 32 * 2 * 130 * 4 - 4), qd.QDOT_E_ARG),  # short ws
+    ((FAKE, 32, FAKE + 4, FAKE, 8, 100, 128, 0.1, FAKE, FAKE, WS), qd.QDOT_E_ALIGN),  # K not 8-aligned
+    ((FAKE, 32, FAKE, FAKE + 4, 8, 100, 128, 0.1, FAKE, FAKE, WS), qd.QDOT_E_ALIGN),  # V not 8-aligned
+    ((FAKE + 2, 32, FAKE, FAKE, 8, 100, 128, 0.1, FAKE, FAKE, WS), qd.QDOT_E_ALIGN),  # query
+    ((FAKE, 32, FAKE, FAKE, 8, 100, 128, 0.1, FAKE + 1, FAKE, WS), qd.QDOT_E_ALIGN),  # out
+])
+def test_attn_validation(lib, args, status):
+    q, Hq, K, V, Hkv, T, D, scale, out, ws, wsb = args
+    assert lib.qdot_attn_decode_kv4(q, Hq, K, V, Hkv, T, D, ctypes.c_float(scale), out, ws, wsb, None) == status
