@@ -22,9 +22,6 @@ int launch_qmm_skinny(const void* W, int type, int N, int K, const void* xq, int
 int launch_qmv_multi(int n, const void* const* W, const int* types, const int* N, int K, const void* xq,
                      int M, float* const* y, hipStream_t s);
 bool qmv_multi_uses_mfma(int n, const int* types, const int* N, int K, int M, int i);
-size_t attn_kv4_workspace_bytes(int64_t Hq, int64_t T);
-int launch_attn_kv4(const void* q_q8, int Hq, const void* Kc, const void* Vc, int Hkv, int T, float scale,
-                    float* out, void* workspace, hipStream_t s);
 }  // namespace qdot
 
 namespace {
@@ -143,32 +140,6 @@ int qdot_rmsnorm_quantize_q8_1(const float* x, const float* w, float eps, int64_
   if (!(eps >= 0.0f) || eps > 3.4e38f) return QDOT_E_ARG;  // also rejects NaN
   if (!aligned4(x) || !aligned4(w) || !aligned4(x_q8)) return QDOT_E_ALIGN;
   int rc = qdot::launch_rmsnorm_q8_1(x, w, eps, M, K, x_q8, static_cast<hipStream_t>(stream));
-  return rc == 0 ? QDOT_OK : QDOT_E_HIP;
-}
-
-size_t qdot_attn_kv4_row_bytes(int64_t D) {
-  return D >= 32 && D % 32 == 0 && D <= QDOT_ATTN_HEAD_DIM ? (size_t)(D / 32) * 18 : 0;
-}
-
-size_t qdot_attn_kv4_workspace_bytes(int64_t Hq, int64_t T) {
-  if (Hq < 1 || Hq > QDOT_ATTN_MAX_HEADS || T < 1 || T > QDOT_ATTN_MAX_T) return 0;
-  return qdot::attn_kv4_workspace_bytes(Hq, T);
-}
-
-int qdot_attn_decode_kv4(const void* q_q8, int64_t Hq, const void* Kc, const void* Vc, int64_t Hkv,
-                         int64_t T, int64_t D, float scale, float* out, void* workspace,
-                         size_t workspace_bytes, void* stream) {
-  if (!q_q8 || !Kc || !Vc || !out || !workspace) return QDOT_E_ARG;
-  if (D != QDOT_ATTN_HEAD_DIM) return QDOT_E_ARG;
-  if (Hq < 1 || Hkv < 1 || Hq > QDOT_ATTN_MAX_HEADS || Hq % Hkv != 0) return QDOT_E_ARG;
-  if (Hq / Hkv > QDOT_ATTN_MAX_GROUP) return QDOT_E_ARG;
-  if (T < 1 || T > QDOT_ATTN_MAX_T) return QDOT_E_ARG;
-  if (!(scale == scale) || scale > 3.4e38f || scale < -3.4e38f) return QDOT_E_ARG;  // NaN, inf
-  if (workspace_bytes < qdot::attn_kv4_workspace_bytes(Hq, T)) return QDOT_E_ARG;
-  if ((reinterpret_cast<uintptr_t>(Kc) & 7u) || (reinterpret_cast<uintptr_t>(Vc) & 7u)) return QDOT_E_ALIGN;
-  if (!aligned4(q_q8) || !aligned4(out) || !aligned4(workspace)) return QDOT_E_ALIGN;
-  int rc = qdot::launch_attn_kv4(q_q8, (int)Hq, Kc, Vc, (int)Hkv, (int)T, scale, out, workspace,
-                                 static_cast<hipStream_t>(stream));
   return rc == 0 ? QDOT_OK : QDOT_E_HIP;
 }
 

@@ -1,0 +1,48 @@
+// api_attn.cpp -- the C ABI of the int4-KV decode attention (declared in
+// include/qdot.h): argument validation before any HIP call, then the two
+// launches of attn_kv4.hip on the caller's stream.  No allocation: the caller
+// passes the workspace.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qdot.h"
+
+namespace qdot {
+size_t attn_kv4_workspace_bytes(int64_t Hq, int64_t T);
+int launch_attn_kv4(const void* q_q8, int Hq, const void* Kc, const void* Vc, int Hkv, int T, float scale,
+                    float* out, void* workspace, hipStream_t s);
+}  // namespace qdot
+
+namespace {
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+}  // namespace
+
+extern "C" {
+
+size_t qdot_attn_kv4_row_bytes(int64_t D) {
+  return D >= 32 && D % 32 == 0 && D <= QDOT_ATTN_HEAD_DIM ? (size_t)(D / 32) * 18 : 0;
+}
+
+size_t qdot_attn_kv4_workspace_bytes(int64_t Hq, int64_t T) {
+  if (Hq < 1 || Hq > QDOT_ATTN_MAX_HEADS || T < 1 || T > QDOT_ATTN_MAX_T) return 0;
+  return qdot::attn_kv4_workspace_bytes(Hq, T);
+}
+
+int qdot_attn_decode_kv4(const void* q_q8, int64_t Hq, const void* Kc, const void* Vc, int64_t Hkv,
+                         int64_t T, int64_t D, float scale, float* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!q_q8 || !Kc || !Vc || !out || !workspace) return QDOT_E_ARG;
+  if (D != QDOT_ATTN_HEAD_DIM) return QDOT_E_ARG;
+  if (Hq < 1 || Hkv < 1 || Hq > QDOT_ATTN_MAX_HEADS || Hq % Hkv != 0) return QDOT_E_ARG;
+  if (Hq / Hkv > QDOT_ATTN_MAX_GROUP) return QDOT_E_ARG;
+  if (T < 1 || T > QDOT_ATTN_MAX_T) return QDOT_E_ARG;
+  if (!(scale == scale) || scale > 3.4e38f || scale < -3.4e38f) return QDOT_E_ARG;  // NaN, inf
+  if (workspace_bytes < qdot::attn_kv4_workspace_bytes(Hq, T)) return QDOT_E_ARG;
+  if (!aligned(Kc, 8) || !aligned(Vc, 8)) return QDOT_E_ALIGN;
+  if (!aligned(q_q8, 4) || !aligned(out, 4) || !aligned(workspace, 4)) return QDOT_E_ALIGN;
+  int rc = qdot::launch_attn_kv4(q_q8, (int)Hq, Kc, Vc, (int)Hkv, (int)T, scale, out, workspace,
+                                 static_cast<hipStream_t>(stream));
+  return rc == 0 ? QDOT_OK : QDOT_E_HIP;
+}
+
+}  // extern "C"
