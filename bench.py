@@ -48,8 +48,10 @@ def parse():
     p.add_argument("--workload", default="qwen3-8b-decode",
                    choices=["qwen3-8b-decode", "qwen3-8b-prefill-512", "iq4xs-h5120-decode",
                             "qwen2.5-1.5b-decode", "qwen3-8b-q4_0-q8_0-decode", "qwen3-8b-mid-batch",
-                            "qwen3-8b-rmsnorm-q8_1", "q4k-matvec-1536"])
+                            "qwen3-8b-rmsnorm-q8_1", "q4k-matvec-1536", "qwen3-8b-attn-kv4-32k"])
     p.add_argument("--ms", default=None, help="comma-separated M values (default per workload)")
+    p.add_argument("--ctx", type=int, default=32768,
+                   help="context length of the attention workload (tokens in the KV cache)")
     p.add_argument("--layers", type=int, default=None, help="override the layer count")
     p.add_argument("--same-weights", action="store_true",
                    help="every layer reads layer 0's weights (cache-hot timing of the same launches)")
@@ -335,6 +337,125 @@ def producer_bench(args):
         "cpu_baseline": cpu, "sampled_check": check}), flush=True)
 
 
+def attention_bench(args):
+    """Decode attention over the 4-bit KV cache (qdot_attn_decode_kv4) with
+    Qwen3-8B heads (32 query heads, 8 KV heads, D = 128) at a 32K-token
+    context: one step = 36 layers, each quantizing its query (Q8_1) and
+    attending over its own cache, captured in one HIP graph.  The cache of
+    every layer is distinct (36 x 37.7 MB), so each step streams it from HBM
+    as on the pages' long-context path.  Algorithmic bytes per attention
+    call: K and V once, the Q8_1 query, the fp32 output."""
+    import numpy as np
+    import torch
+    from quant_integer_dot_amd import binding as qd
+    from quant_integer_dot_amd import synth
+    L = qd.load()
+    dev = torch.device("cuda:0")
+    Hq, Hkv, D, T = 32, 8, 128, args.ctx
+    layers = args.layers or 36
+    row = qd.qdot_attn_kv4_row_bytes(D)
+    scale = np.float32(1 / np.sqrt(D))
+    t0 = time.time()
+    Ks, Vs, xs, qs, outs = [], [], [], [], []
+    for layer in range(layers):
+        Ks.append(torch.from_numpy(synth.kv4_cache(Hkv, T, D, (2026, 80, layer, 1))).to(dev))
+        Vs.append(torch.from_numpy(synth.kv4_cache(Hkv, T, D, (2026, 80, layer, 2))).to(dev))
+        xs.append(torch.from_numpy(synth.activations(Hq, D, (2026, 80, layer, 3))).to(dev))
+        qs.append(torch.empty(qd.qdot_q8_1_bytes(Hq, D), dtype=torch.uint8, device=dev))
+        outs.append(torch.empty((Hq, D), dtype=torch.float32, device=dev))
+    wsb = qd.qdot_attn_kv4_workspace_bytes(Hq, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    kv_bytes = 2 * Hkv * T * row
+    log(f"[bench] workload {args.workload}: {layers} layers, Hq={Hq} Hkv={Hkv} D={D} T={T}; KV cache "
+        f"{layers * kv_bytes / 1e9:.3f} GB resident in {time.time() - t0:.1f} s; library {qd.qdot_build_id()}")
+
+    def step(quantize=True):
+        s = torch.cuda.current_stream(dev).cuda_stream
+        for i in range(layers):
+            if quantize:
+                assert L.qdot_quantize_q8_1(xs[i].data_ptr(), Hq, D, qs[i].data_ptr(), s) == 0
+            rc = L.qdot_attn_decode_kv4(qs[i].data_ptr(), Hq, Ks[i].data_ptr(), Vs[i].data_ptr(), Hkv, T, D,
+                                        ctypes.c_float(scale), outs[i].data_ptr(), ws.data_ptr(), wsb, s)
+            assert rc == 0, rc
+
+    if args.eager_only:   # counter runs: plain launches, no graphs, no timing
+        for _ in range(max(args.steps, 1)):
+            step(True)
+        torch.cuda.synchronize()
+        print(json.dumps({"eager_only": True, "workload": args.workload, "layers": layers, "ctx": T}), flush=True)
+        return
+
+    def graph_ms(quantize):
+        step(quantize)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(quantize)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    ms_step = graph_ms(True)
+    ms_attn = graph_ms(False)   # the attention calls alone (queries already quantized)
+    per_call_us = ms_attn * 1e3 / layers
+    alg = kv_bytes + qd.qdot_q8_1_bytes(Hq, D) + Hq * D * 4
+    achieved = alg / (per_call_us * 1e-6) / 1e9
+    value = layers * kv_bytes / (ms_step * 1e-3) / 1e9
+    check = None
+    if not args.no_check:
+        import oracle
+        step(True)
+        torch.cuda.synchronize()
+        i = layers - 1
+        o64, _ = oracle.attn_decode_kv4(qs[i].cpu().numpy(), Hq, Ks[i].cpu().numpy(), Vs[i].cpu().numpy(), Hkv,
+                                        T, D, float(scale))
+        got = outs[i].cpu().numpy().astype(np.float64)
+        d = np.abs(Vs[i].cpu().numpy().reshape(Hkv, T, D // 32, 18)[..., 0:2].copy().view(np.float16)
+                   .astype(np.float64))
+        vmax = np.repeat((8 * d).reshape(Hkv, -1).max(axis=1), Hq // Hkv)[:, None]
+        bad = int((np.abs(got - o64) > 1e-4 * vmax).sum())
+        check = {"outputs_checked": int(got.size), "outside_1e-4_of_max_v": bad, "layer": i}
+        if bad:
+            log(f"[bench] SAMPLED CHECK FAILED: {bad} of {got.size} outputs")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        K0, V0, q0 = Ks[0].cpu().numpy(), Vs[0].cpu().numpy(), qs[0].cpu().numpy()
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 10.0:
+            oracle.attn_decode_kv4(q0, Hq, K0, V0, Hkv, T, D, float(scale))
+            reps += 1
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(reps * kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{reps} attention calls of layer 0 (all {Hq} heads, T = {T}) in {dt:.1f} s, "
+                         "single thread"}
+    log(f"[bench] step {ms_step:.3f} ms -> {value:.1f} GB/s of KV cache; attention call {per_call_us:.2f} us "
+        f"({achieved:.1f} GB/s)")
+    print(json.dumps({
+        "metric": "KV-cache GB/s of int4-KV decode attention, Qwen3-8B heads",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8/f32", "data": "synthetic",
+        "config": {"workload": args.workload, "layers": layers, "Hq": Hq, "Hkv": Hkv, "D": D, "ctx": T,
+                   "kv_bytes_per_layer": kv_bytes, "launches_per_step": 3 * layers},
+        "roofline": {"bound": "hbm", "kernel": "attn_kv4_partial_kernel+attn_kv4_combine_kernel",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 5),
+                     "traffic": recorded_traffic("attn_kv4_partial_kernel+attn_kv4_combine_kernel", args.workload),
+                     "launches": layers, "avg_launch_us": round(per_call_us, 3),
+                     "algorithmic_bytes_per_launch": alg,
+                     "note": "one launch = one qdot_attn_decode_kv4 call (the partial and combine kernels)"},
+        "cpu_baseline": cpu, "sampled_check": check}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -346,6 +467,9 @@ def main():
         return
     if args.workload == "qwen3-8b-rmsnorm-q8_1":
         producer_bench(args)
+        return
+    if args.workload == "qwen3-8b-attn-kv4-32k":
+        attention_bench(args)
         return
 
     import numpy as np

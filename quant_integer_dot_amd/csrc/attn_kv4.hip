@@ -22,7 +22,7 @@
 //                     in LDS; writes the chunk's max m, sum l and unnormalised
 //                     output o[128] per head to the workspace.
 //   attn_kv4_combine  per head: M = max m_c, L = sum l_c e^(m_c - M),
-//                     out = sum o_c e^(m_c - M) / L, chunks in order.
+//                     out = sum o_c e^(m_c - M) / L, in a fixed order.
 #include "qdot_common.hpp"
 
 namespace qdot {
@@ -61,6 +61,27 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kv4_partial_kernel(
   const int ntok = min(AT_CH, T - t0);
   const size_t row0 = (size_t)kvh * T + t0;
 
+  // Every global load of the chunk goes out first: this thread's K row
+  // (token t0 + tid, clamped to the chunk's last token) and its nine 8-byte
+  // pieces of the chunk's V rows (indices clamped into the chunk, stored
+  // only when in range), so all of them are in flight together.
+  constexpr int VP = AT_CH * AT_ROW / 8 / AT_THREADS;  // V pieces per thread
+  uint32_t kw[AT_ROW / 4];
+  u32x2 vreg[VP];
+  const int npieces = ntok * (AT_ROW / 8);
+  {
+    const u32x2* krow = reinterpret_cast<const u32x2*>(Kc + (row0 + min(tid, ntok - 1)) * AT_ROW);
+#pragma unroll
+    for (int k = 0; k < AT_ROW / 8; ++k) {
+      const u32x2 v = krow[k];
+      kw[2 * k] = v.x;
+      kw[2 * k + 1] = v.y;
+    }
+    const u32x2* vsrc = reinterpret_cast<const u32x2*>(Vc + row0 * AT_ROW);
+#pragma unroll
+    for (int k = 0; k < VP; ++k) vreg[k] = vsrc[min(tid + k * AT_THREADS, npieces - 1)];
+  }
+
   // query blocks of this KV head's G query heads
   if (tid < G * AT_NB) {
     const int g = tid / AT_NB, b = tid % AT_NB;
@@ -76,25 +97,15 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kv4_partial_kernel(
     }
     q_sum[g][b] = s;
   }
-  // stage the chunk's V rows (8-byte pieces, coalesced)
-  {
-    const u32x2* vsrc = reinterpret_cast<const u32x2*>(Vc + row0 * AT_ROW);
-    const int npieces = ntok * (AT_ROW / 8);
-    for (int i = tid; i < npieces; i += AT_THREADS) v_s[i] = vsrc[i];
-  }
+  // stage the chunk's V rows
+#pragma unroll
+  for (int k = 0; k < VP; ++k)
+    if (tid + k * AT_THREADS < npieces) v_s[tid + k * AT_THREADS] = vreg[k];
   __syncthreads();
 
   // scores: token t0 + tid
   float s_own[G];
   if (tid < ntok) {
-    uint32_t kw[AT_ROW / 4];
-    const u32x2* krow = reinterpret_cast<const u32x2*>(Kc + (row0 + tid) * AT_ROW);
-#pragma unroll
-    for (int k = 0; k < AT_ROW / 8; ++k) {
-      const u32x2 v = krow[k];
-      kw[2 * k] = v.x;
-      kw[2 * k + 1] = v.y;
-    }
     double acc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) acc[g] = 0.0;
@@ -192,23 +203,51 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kv4_partial_kernel(
   }
 }
 
-__global__ __launch_bounds__(AT_D) void attn_kv4_combine_kernel(const float* __restrict__ ws_o,
-                                                                const float* __restrict__ ws_m,
-                                                                const float* __restrict__ ws_l,
-                                                                int nchunks, float* __restrict__ out) {
-  const int h = blockIdx.x, d = threadIdx.x;
+// One workgroup per query head: 4 x 128 threads, thread (k, d) sums element d
+// over the chunks c = k (mod 4); the four partial sums, the max and the
+// denominator are joined in a fixed order, so the result depends on the
+// number of chunks only.
+constexpr int AC_SPLIT = 4;
+__global__ __launch_bounds__(AC_SPLIT * AT_D) void attn_kv4_combine_kernel(const float* __restrict__ ws_o,
+                                                                           const float* __restrict__ ws_m,
+                                                                           const float* __restrict__ ws_l,
+                                                                           int nchunks, float* __restrict__ out) {
+  __shared__ float red_m[AC_SPLIT * AT_D / 64];
+  __shared__ float red_l[AC_SPLIT * AT_D / 64];
+  __shared__ float o_s[AC_SPLIT][AT_D];
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k = tid / AT_D, d = tid % AT_D;
   const float* m = ws_m + (size_t)h * nchunks;
   const float* l = ws_l + (size_t)h * nchunks;
   const float* o = ws_o + (size_t)h * nchunks * AT_D + d;
-  float M = m[0];
-  for (int c = 1; c < nchunks; ++c) M = fmaxf(M, m[c]);
-  float L = 0.0f, O = 0.0f;
-  for (int c = 0; c < nchunks; ++c) {
-    const float e = expf(m[c] - M);
-    L = fmaf(l[c], e, L);
-    O = fmaf(o[(size_t)c * AT_D], e, O);
+  constexpr int NW = AC_SPLIT * AT_D / 64;
+  float mx = -__builtin_inff();
+  for (int c = tid; c < nchunks; c += AC_SPLIT * AT_D) mx = fmaxf(mx, m[c]);
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) mx = fmaxf(mx, __shfl_xor(mx, s, 64));
+  if (lane == 0) red_m[wave] = mx;
+  __syncthreads();
+  float M = red_m[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, red_m[w]);
+  // denominator: chunk c by thread c (mod 512), then the waves in order
+  float Lp = 0.0f;
+  for (int c = tid; c < nchunks; c += AC_SPLIT * AT_D) Lp = fmaf(l[c], expf(m[c] - M), Lp);
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) Lp += __shfl_xor(Lp, s, 64);
+  if (lane == 0) red_l[wave] = Lp;
+  float O = 0.0f;
+#pragma unroll 8
+  for (int c = k; c < nchunks; c += AC_SPLIT) O = fmaf(o[(size_t)c * AT_D], expf(m[c] - M), O);
+  o_s[k][d] = O;
+  __syncthreads();
+  if (k == 0) {
+    float L = red_l[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) L += red_l[w];
+    const float v = ((o_s[0][d] + o_s[1][d]) + o_s[2][d]) + o_s[3][d];
+    out[(size_t)h * AT_D + d] = v / L;
   }
-  out[(size_t)h * AT_D + d] = O / L;
 }
 
 size_t attn_kv4_workspace_bytes(int64_t Hq, int64_t T) {
@@ -249,7 +288,7 @@ int launch_attn_kv4(const void* q_q8, int Hq, const void* Kc, const void* Vc, in
     default: return -2;
   }
   if (rc) return rc;
-  hipLaunchKernelGGL(attn_kv4_combine_kernel, dim3(Hq), dim3(AT_D), 0, s, wo, wm, wl, nchunks, out);
+  hipLaunchKernelGGL(attn_kv4_combine_kernel, dim3(Hq), dim3(AC_SPLIT * AT_D), 0, s, wo, wm, wl, nchunks, out);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
