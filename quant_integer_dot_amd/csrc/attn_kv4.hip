@@ -50,10 +50,16 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kv4_partial_kernel(
   __shared__ uint32_t q_codes[G][AT_NB][8];     // the query's int8 codes, 4 per dword
   __shared__ double q_d[G][AT_NB];              // the query blocks' D
   __shared__ int q_sum[G][AT_NB];               // sum of each query block's codes
-  __shared__ float p_s[G][AT_CH];               // scores, then softmax numerators
   __shared__ float w_red[AT_WAVES][G];          // per-wave max, then per-wave sum
   __shared__ __attribute__((aligned(16))) u32x2 v_s[AT_CH * AT_ROW / 8];  // the chunk's V rows
-  __shared__ float o_red[AT_WAVES][G][AT_D];    // per-wave P.V partials
+  // the chunk's K rows until the scores are formed; then the softmax
+  // numerators p_s[G][AT_CH] during P.V, and after it the per-wave P.V
+  // partials o_red[AT_WAVES][G][AT_D]
+  __shared__ __attribute__((aligned(16))) u32x2 k_s[AT_CH * AT_ROW / 8];
+  static_assert(AT_WAVES * G * AT_D * sizeof(float) <= sizeof(k_s), "P.V partials fit the K stage");
+  static_assert(G * AT_CH * sizeof(float) <= sizeof(k_s), "numerators fit the K stage");
+  float (*p_s)[AT_CH] = reinterpret_cast<float (*)[AT_CH]>(k_s);
+  float (*o_red)[G][AT_D] = reinterpret_cast<float (*)[G][AT_D]>(k_s);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x, kvh = blockIdx.y;
@@ -61,23 +67,18 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kv4_partial_kernel(
   const int ntok = min(AT_CH, T - t0);
   const size_t row0 = (size_t)kvh * T + t0;
 
-  // Every global load of the chunk goes out first: this thread's K row
-  // (token t0 + tid, clamped to the chunk's last token) and its nine 8-byte
-  // pieces of the chunk's V rows (indices clamped into the chunk, stored
-  // only when in range), so all of them are in flight together.
-  constexpr int VP = AT_CH * AT_ROW / 8 / AT_THREADS;  // V pieces per thread
-  uint32_t kw[AT_ROW / 4];
-  u32x2 vreg[VP];
+  // Every global load of the chunk goes out first, coalesced: this
+  // thread's nine 8-byte pieces of the chunk's K rows and nine of its V rows
+  // (indices clamped into the chunk, stored to LDS only when in range), so
+  // all of them are in flight together.
+  constexpr int VP = AT_CH * AT_ROW / 8 / AT_THREADS;  // pieces per thread and cache
+  u32x2 kreg[VP], vreg[VP];
   const int npieces = ntok * (AT_ROW / 8);
   {
-    const u32x2* krow = reinterpret_cast<const u32x2*>(Kc + (row0 + min(tid, ntok - 1)) * AT_ROW);
-#pragma unroll
-    for (int k = 0; k < AT_ROW / 8; ++k) {
-      const u32x2 v = krow[k];
-      kw[2 * k] = v.x;
-      kw[2 * k + 1] = v.y;
-    }
+    const u32x2* ksrc = reinterpret_cast<const u32x2*>(Kc + row0 * AT_ROW);
     const u32x2* vsrc = reinterpret_cast<const u32x2*>(Vc + row0 * AT_ROW);
+#pragma unroll
+    for (int k = 0; k < VP; ++k) kreg[k] = ksrc[min(tid + k * AT_THREADS, npieces - 1)];
 #pragma unroll
     for (int k = 0; k < VP; ++k) vreg[k] = vsrc[min(tid + k * AT_THREADS, npieces - 1)];
   }
@@ -97,15 +98,25 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kv4_partial_kernel(
     }
     q_sum[g][b] = s;
   }
-  // stage the chunk's V rows
+  // stage the chunk's K and V rows
 #pragma unroll
   for (int k = 0; k < VP; ++k)
-    if (tid + k * AT_THREADS < npieces) v_s[tid + k * AT_THREADS] = vreg[k];
+    if (tid + k * AT_THREADS < npieces) {
+      k_s[tid + k * AT_THREADS] = kreg[k];
+      v_s[tid + k * AT_THREADS] = vreg[k];
+    }
   __syncthreads();
 
   // scores: token t0 + tid
   float s_own[G];
   if (tid < ntok) {
+    uint32_t kw[AT_ROW / 4];
+#pragma unroll
+    for (int k = 0; k < AT_ROW / 8; ++k) {
+      const u32x2 v = k_s[tid * (AT_ROW / 8) + k];
+      kw[2 * k] = v.x;
+      kw[2 * k + 1] = v.y;
+    }
     double acc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) acc[g] = 0.0;
@@ -145,7 +156,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kv4_partial_kernel(
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
     if (lane == 0) w_red[wave][g] = m;
   }
-  __syncthreads();
+  __syncthreads();  // also: every K row has been read, so k_s now takes p_s
   float mx[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) mx[g] = fmaxf(fmaxf(w_red[0][g], w_red[1][g]), fmaxf(w_red[2][g], w_red[3][g]));
@@ -171,12 +182,37 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kv4_partial_kernel(
     for (int g = 0; g < G; ++g) acc0[g] = acc1[g] = 0.0f;
     const uint8_t* vb = reinterpret_cast<const uint8_t*>(v_s);
     const int tend = min(ntok, 64 * wave + 64);
-    for (int t = 64 * wave; t < tend; ++t) {
+    // value pair of token t for this lane (exact: fp16 d times a small integer)
+    auto vpair = [&](int t, float& v0, float& v1) {
       const uint8_t* blk = vb + t * AT_ROW + 18 * b;
-      const float dv = h2f((uint32_t)blk[0] | ((uint32_t)blk[1] << 8));
+      const float dv = h2f(*reinterpret_cast<const uint16_t*>(blk));
       const uint32_t code = blk[2 + j];
-      const float v0 = dv * (float)((int)(code & 15u) - 8);   // exact
-      const float v1 = dv * (float)((int)(code >> 4) - 8);
+      v0 = dv * (float)((int)(code & 15u) - 8);
+      v1 = dv * (float)((int)(code >> 4) - 8);
+    };
+    // four tokens a step (their LDS reads issued together; p of the four
+    // tokens in one 16-byte read), the sums still in token order
+    int t = 64 * wave;
+    for (; t + 4 <= tend; t += 4) {
+      float v0[4], v1[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) vpair(t + u, v0[u], v1[u]);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float4 p4 = *reinterpret_cast<const float4*>(&p_s[g][t]);
+        acc0[g] = fmaf(p4.x, v0[0], acc0[g]);
+        acc1[g] = fmaf(p4.x, v1[0], acc1[g]);
+        acc0[g] = fmaf(p4.y, v0[1], acc0[g]);
+        acc1[g] = fmaf(p4.y, v1[1], acc1[g]);
+        acc0[g] = fmaf(p4.z, v0[2], acc0[g]);
+        acc1[g] = fmaf(p4.z, v1[2], acc1[g]);
+        acc0[g] = fmaf(p4.w, v0[3], acc0[g]);
+        acc1[g] = fmaf(p4.w, v1[3], acc1[g]);
+      }
+    }
+    for (; t < tend; ++t) {
+      float v0, v1;
+      vpair(t, v0, v1);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float p = p_s[g][t];
@@ -184,6 +220,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kv4_partial_kernel(
         acc1[g] = fmaf(p, v1, acc1[g]);
       }
     }
+    __syncthreads();  // every wave is done with p_s before o_red overwrites it
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       o_red[wave][g][32 * b + j] = acc0[g];
@@ -203,26 +240,27 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kv4_partial_kernel(
   }
 }
 
-// One workgroup per query head: 4 x 128 threads, thread (k, d) sums element d
-// over the chunks c = k (mod 4); the four partial sums, the max and the
-// denominator are joined in a fixed order, so the result depends on the
-// number of chunks only.
-constexpr int AC_SPLIT = 4;
-__global__ __launch_bounds__(AC_SPLIT * AT_D) void attn_kv4_combine_kernel(const float* __restrict__ ws_o,
-                                                                           const float* __restrict__ ws_m,
-                                                                           const float* __restrict__ ws_l,
-                                                                           int nchunks, float* __restrict__ out) {
-  __shared__ float red_m[AC_SPLIT * AT_D / 64];
-  __shared__ float red_l[AC_SPLIT * AT_D / 64];
-  __shared__ float o_s[AC_SPLIT][AT_D];
-  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int k = tid / AT_D, d = tid % AT_D;
-  const float* m = ws_m + (size_t)h * nchunks;
-  const float* l = ws_l + (size_t)h * nchunks;
-  const float* o = ws_o + (size_t)h * nchunks * AT_D + d;
-  constexpr int NW = AC_SPLIT * AT_D / 64;
+// One workgroup per (query head, 32 output elements): 16 x 32 threads,
+// thread (k, e) sums element e of the slice over the partials c = k
+// (mod 16); the sixteen partial sums, the max and the denominator are joined
+// in a fixed order, so the result depends on the number of partials only.
+constexpr int AC_SPLIT = 16, AC_COLS = 32;
+__global__ __launch_bounds__(AC_SPLIT * AC_COLS) void attn_kv4_combine_kernel(const float* __restrict__ ws_o,
+                                                                              const float* __restrict__ ws_m,
+                                                                              const float* __restrict__ ws_l,
+                                                                              int nparts, float* __restrict__ out) {
+  constexpr int NT = AC_SPLIT * AC_COLS, NW = NT / 64;
+  __shared__ float red_m[NW];
+  __shared__ float red_l[NW];
+  __shared__ float o_s[AC_SPLIT][AC_COLS];
+  const int h = blockIdx.x, d0 = blockIdx.y * AC_COLS;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k = tid / AC_COLS, e = tid % AC_COLS;
+  const float* m = ws_m + (size_t)h * nparts;
+  const float* l = ws_l + (size_t)h * nparts;
+  const float* o = ws_o + (size_t)h * nparts * AT_D + d0 + e;
   float mx = -__builtin_inff();
-  for (int c = tid; c < nchunks; c += AC_SPLIT * AT_D) mx = fmaxf(mx, m[c]);
+  for (int c = tid; c < nparts; c += NT) mx = fmaxf(mx, m[c]);
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) mx = fmaxf(mx, __shfl_xor(mx, s, 64));
   if (lane == 0) red_m[wave] = mx;
@@ -230,23 +268,25 @@ __global__ __launch_bounds__(AC_SPLIT * AT_D) void attn_kv4_combine_kernel(const
   float M = red_m[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) M = fmaxf(M, red_m[w]);
-  // denominator: chunk c by thread c (mod 512), then the waves in order
+  // denominator: partial c by thread c (mod 512), then the waves in order
   float Lp = 0.0f;
-  for (int c = tid; c < nchunks; c += AC_SPLIT * AT_D) Lp = fmaf(l[c], expf(m[c] - M), Lp);
+  for (int c = tid; c < nparts; c += NT) Lp = fmaf(l[c], expf(m[c] - M), Lp);
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) Lp += __shfl_xor(Lp, s, 64);
   if (lane == 0) red_l[wave] = Lp;
   float O = 0.0f;
-#pragma unroll 8
-  for (int c = k; c < nchunks; c += AC_SPLIT) O = fmaf(o[(size_t)c * AT_D], expf(m[c] - M), O);
-  o_s[k][d] = O;
+#pragma unroll 4
+  for (int c = k; c < nparts; c += AC_SPLIT) O = fmaf(o[(size_t)c * AT_D], expf(m[c] - M), O);
+  o_s[k][e] = O;
   __syncthreads();
   if (k == 0) {
     float L = red_l[0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) L += red_l[w];
-    const float v = ((o_s[0][d] + o_s[1][d]) + o_s[2][d]) + o_s[3][d];
-    out[(size_t)h * AT_D + d] = v / L;
+    float v = o_s[0][e];
+#pragma unroll
+    for (int i = 1; i < AC_SPLIT; ++i) v += o_s[i][e];
+    out[(size_t)h * AT_D + d0 + e] = v / L;
   }
 }
 
@@ -288,7 +328,8 @@ int launch_attn_kv4(const void* q_q8, int Hq, const void* Kc, const void* Vc, in
     default: return -2;
   }
   if (rc) return rc;
-  hipLaunchKernelGGL(attn_kv4_combine_kernel, dim3(Hq), dim3(AC_SPLIT * AT_D), 0, s, wo, wm, wl, nchunks, out);
+  hipLaunchKernelGGL(attn_kv4_combine_kernel, dim3(Hq, AT_D / AC_COLS), dim3(AC_SPLIT * AC_COLS), 0, s, wo, wm,
+                     wl, nchunks, out);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -45,7 +45,9 @@ def test_c0_workload_is_cold():
 @pytest.mark.parametrize("kernel,workload", [("qmv_multi_kernel", "qwen3-8b-decode"),
                                              ("qmm_mfma_kernel", "qwen3-8b-prefill-512"),
                                              ("qmm_skinny_kernel", "qwen3-8b-mid-batch"),
-                                             ("rmsnorm_q8_1_kernel", "qwen3-8b-rmsnorm-q8_1")])
+                                             ("rmsnorm_q8_1_kernel", "qwen3-8b-rmsnorm-q8_1"),
+                                             ("attn_kv4_partial_kernel+attn_kv4_combine_kernel",
+                                              "qwen3-8b-attn-kv4-32k")])
 def test_recorded_traffic_matches_the_sources(kernel, workload):
     """The committed HBM-traffic summary of each measured kernel was taken on
     the current sources (its digest matches), so the bench line reports it."""
