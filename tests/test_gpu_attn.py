@@ -96,12 +96,11 @@ def test_peaked_scores():
     check(out, o64, V, Hq, Hkv, "peaked")
 
 
-@pytest.mark.parametrize("T", [28672, 32768])
-def test_full_size(T):
+@pytest.mark.parametrize("Hq,Hkv,T", [(32, 8, 28672), (32, 8, 32768), (12, 2, 32768)])
+def test_full_size(Hq, Hkv, T):
     """Qwen3-8B heads (32 query, 8 KV, D = 128) at the long-context lengths
-    of the pages (28K and 32K tokens), every output against the oracle;
-    bitwise deterministic."""
-    Hq, Hkv = 32, 8
+    of the pages (28K and 32K tokens) and Qwen2.5-1.5B heads (12 query, 2 KV)
+    at 32K, every output against the oracle; bitwise deterministic."""
     scale = np.float32(1 / math.sqrt(D))
     K, V, xqd, xq = case(Hq, Hkv, T, 11)
     Kd, Vd = to_dev(K), to_dev(V)
