@@ -138,3 +138,26 @@ def test_offset_cache_views():
     out = run(xqd, Hq, Kb.data_ptr() + 8, Vb.data_ptr() + 24, Hkv, T, scale)
     o64, _ = oracle.attn_decode_kv4(xq, Hq, K, V, Hkv, T, D, float(scale))
     check(out, o64, V, Hq, Hkv, "offset views")
+
+
+def test_million_token_context():
+    """T = 1,000,003 (3907 chunks, a ragged tail): the combine joins 3907
+    partials per head (245 per residue); every output against the oracle."""
+    Hq, Hkv, T = 4, 1, 1_000_003
+    scale = np.float32(1 / math.sqrt(D))
+    K, V, xqd, xq = case(Hq, Hkv, T, 21)
+    out = run(xqd, Hq, to_dev(K), to_dev(V), Hkv, T, scale)
+    o64, _ = oracle.attn_decode_kv4(xq, Hq, K, V, Hkv, T, D, float(scale))
+    check(out, o64, V, Hq, Hkv, "T=1000003")
+
+
+def test_negative_and_large_scale():
+    """A negative scale (softmax of -s) and a large one (weights nearly
+    one-hot) are ordinary finite arguments."""
+    Hq, Hkv, T = 8, 2, 600
+    K, V, xqd, xq = case(Hq, Hkv, T, 23)
+    Kd, Vd = to_dev(K), to_dev(V)
+    for scale in (np.float32(-0.05), np.float32(2.0)):
+        out = run(xqd, Hq, Kd, Vd, Hkv, T, scale)
+        o64, _ = oracle.attn_decode_kv4(xq, Hq, K, V, Hkv, T, D, float(scale))
+        check(out, o64, V, Hq, Hkv, f"scale={scale}")
