@@ -50,7 +50,8 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kv4_partial_kernel(
   __shared__ uint32_t q_codes[G][AT_NB][8];     // the query's int8 codes, 4 per dword
   __shared__ double q_d[G][AT_NB];              // the query blocks' D
   __shared__ int q_sum[G][AT_NB];               // sum of each query block's codes
-  __shared__ float w_red[AT_WAVES][G];          // per-wave max, then per-wave sum
+  __shared__ float w_red[AT_WAVES][G];          // per-wave max
+  __shared__ float w_sum[AT_WAVES][G];          // per-wave sum
   __shared__ __attribute__((aligned(16))) u32x2 v_s[AT_CH * AT_ROW / 8];  // the chunk's V rows
   // the chunk's K rows until the scores are formed; then the softmax
   // numerators p_s[G][AT_CH] during P.V, and after it the per-wave P.V
@@ -160,7 +161,6 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kv4_partial_kernel(
   float mx[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) mx[g] = fmaxf(fmaxf(w_red[0][g], w_red[1][g]), fmaxf(w_red[2][g], w_red[3][g]));
-  __syncthreads();  // w_red is reused for the sums
   // numerators and their sum (butterfly in a fixed order, then the waves in order)
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kv4_partial_kernel(
     float l = p;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);
-    if (lane == 0) w_red[wave][g] = l;
+    if (lane == 0) w_sum[wave][g] = l;
   }
   __syncthreads();
 
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kv4_partial_kernel(
   if (tid < G) {
     const size_t i = (size_t)(kvh * G + tid) * nchunks + c;
     ws_m[i] = mx[tid];
-    ws_l[i] = ((w_red[0][tid] + w_red[1][tid]) + w_red[2][tid]) + w_red[3][tid];
+    ws_l[i] = ((w_sum[0][tid] + w_sum[1][tid]) + w_sum[2][tid]) + w_sum[3][tid];
   }
 }
 
