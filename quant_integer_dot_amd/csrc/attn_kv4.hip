@@ -13,7 +13,9 @@
 // Two kernels, split over the context (flash-decoding):
 //   attn_kv4_partial  one workgroup per (256-token chunk, KV head) serves the
 //                     G query heads of that KV head, so each K and V byte is
-//                     read from HBM once per step.  Scores: exact int32 dots
+//                     read from HBM once per step.  The chunk's K and V rows
+//                     are staged in LDS by coalesced loads, all issued before
+//                     the first wait.  Scores: exact int32 dots
 //                     (v_dot4_i32_i8 on the nibbles, minus 8 * the query
 //                     block's code sum), the scale products and the four
 //                     blocks summed in fp64 (every product exact) and rounded
@@ -21,8 +23,9 @@
 //                     expf, fixed-order sums), then P.V from the V rows staged
 //                     in LDS; writes the chunk's max m, sum l and unnormalised
 //                     output o[128] per head to the workspace.
-//   attn_kv4_combine  per head: M = max m_c, L = sum l_c e^(m_c - M),
-//                     out = sum o_c e^(m_c - M) / L, in a fixed order.
+//   attn_kv4_combine  per (head, 32 outputs): M = max m_c, L = sum l_c
+//                     e^(m_c - M), out = sum o_c e^(m_c - M) / L, the chunks
+//                     in 16 residues joined in a fixed order.
 #include "qdot_common.hpp"
 
 namespace qdot {
