@@ -86,9 +86,11 @@ def test_unfused_mix_runs_per_type(M):
                 seed=40 + M)
 
 
-@pytest.mark.parametrize("M", [9, 40, 100])
+@pytest.mark.parametrize("M", [9, 16, 17, 40, 100])
 def test_above_decode_launches_each(M):
-    check_group([(96, synth.Q4_K), (50, synth.Q6_K)], 512, M, seed=50 + M)
+    """Above M = 8 each matrix is its own launch: Q4_K and IQ4_XS on the
+    16-row decode tile up to M = 16, Q6_K on the mid-batch kernel."""
+    check_group([(96, synth.Q4_K), (50, synth.Q6_K), (80, synth.IQ4_XS)], 512, M, seed=50 + M)
 
 
 def test_single_matrix_group():
