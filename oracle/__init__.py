@@ -6,7 +6,9 @@ library under ``quant_integer_dot_amd``) never does: the two share no code.
 
 This module is argument marshalling over ``liboracle.so`` (plain C, fp64), which
 ``build()`` compiles from ``oracle.c``.  Every function states the passage of the
-pages it follows in ``oracle.c``.
+pages it follows in ``oracle.c``.  The loops over independent outputs run on
+several host threads (OpenMP; ``set_threads``); each output is computed by one
+thread in the written order, so results do not depend on the thread count.
 """
 import ctypes
 import os
@@ -26,7 +28,7 @@ def build(verbose=False):
     """Compile oracle.c into liboracle.so with the host C compiler."""
     import subprocess
 
-    cmd = ["gcc", "-std=c99", "-O1", "-ffp-contract=off", "-fno-fast-math",
+    cmd = ["gcc", "-std=c99", "-O1", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
            "-fPIC", "-shared", "-Wall", "-o", _LIB_PATH,
            os.path.join(_HERE, "oracle.c"), "-lm"]
     if verbose:
@@ -62,6 +64,10 @@ def lib():
         L.oracle_rmsnorm.restype = None
         L.oracle_attn_decode_kv4.argtypes = [P, i64, P, P, i64, i64, i64, ctypes.c_double, P, P]
         L.oracle_attn_decode_kv4.restype = ctypes.c_int
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_threads.restype = None
+        L.oracle_max_threads.argtypes = []
+        L.oracle_max_threads.restype = ctypes.c_int
         L.oracle_codebook.argtypes = []
         L.oracle_codebook.restype = ctypes.POINTER(ctypes.c_int)
         _lib = L
@@ -77,6 +83,16 @@ def _u8(a):
     if a.dtype != np.uint8:
         a = a.view(np.uint8)
     return a
+
+
+def set_threads(n):
+    """Host threads for the loops over outputs (n < 1: the OpenMP default)."""
+    lib().oracle_set_threads(int(n))
+
+
+def max_threads():
+    """Threads the next loop over outputs will use."""
+    return int(lib().oracle_max_threads())
 
 
 def half_to_double(bits):
@@ -104,7 +120,8 @@ def quantize_q8_1(x):
 
 def rmsnorm(x, w, eps):
     """RMSNorm of each row of fp32 [M][K] with weight w[K] (oracle.c,
-    oracle_rmsnorm: Kestrel 3.6 numerics, fixed sum-of-squares tree);
+    oracle_rmsnorm: Kestrel #18 section 3.6 numerics, 8-element group sums
+    added left to right);
     returns (xn fp32 [M][K], ss fp32 [M])."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     w = np.ascontiguousarray(w, dtype=np.float32)

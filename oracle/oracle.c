@@ -33,11 +33,20 @@
  * so d*sc*D*I needs at most 11+6+11+17 = 45 bits < 53); the terms are summed in
  * fp64 in K order and the result is rounded once to fp32 (round to nearest
  * even).  Built with -O1 -ffp-contract=off, no fast-math, no SIMD intrinsics.
+ *
+ * Threads: the matmul and sub-block-sum loops run their independent outputs
+ * on several host threads (OpenMP, when built with it; oracle_set_threads
+ * picks the count).  Each output is still computed by one thread with exactly
+ * the operations and order written below, so the results do not depend on
+ * the thread count.
  */
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define OR_Q4_K 1
 #define OR_Q6_K 2
@@ -99,6 +108,24 @@ uint16_t oracle_double_to_half(double v) {
   return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)((int)m - 1024));
 }
 
+/* Host threads used by the loops over outputs below (1 when built without
+ * OpenMP).  n < 1 leaves the OpenMP default (OMP_NUM_THREADS or all cores). */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
 static uint16_t rd16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
 static void wr16(uint8_t *p, uint16_t v) { p[0] = (uint8_t)(v & 255); p[1] = (uint8_t)(v >> 8); }
 
@@ -154,56 +181,47 @@ void oracle_quantize_q8_1(const float *x, int64_t M, int64_t K, uint8_t *out) {
 
 /* RMSNorm of each row (the producer of the Q8_1 activations of the Q/K/V and
  * gate/up projections: the xLLM engine quantizes the normalized input into
- * one shared buffer, d_xn_q8, section C.1; Kestrel_VLLM #18 section 3.6
- * gives the RMSNorm numerics it matches against the CPU).
- * Numerics as Kestrel 3.6: fp32 throughout, r = 1.0f / sqrtf(ss / K + eps)
- * (correctly rounded division and square root, not an rsqrt approximation),
- * out_i = (x_i * r) * w_i.
- * Reading (the order of the sum of squares): Kestrel sums each group of 8
- * squares as (lo0 + lo1) + (lo2 + lo3) with lo_k = s_k + s_{k+4}; here every
- * 8-group is summed that way, the four groups of each 32-element block
- * pairwise, (t0 + t1) + (t2 + t3), and the block sums of a row in a pairwise
- * tree (zero-padded to a power of two: level by level u_i = u_2i + u_2i+1).
- * Every operation is a single fp32 operation; nothing is fused.
+ * one shared buffer, d_xn_q8, section C.1).  Kestrel_VLLM #18, section 3.6
+ * (the CPU-order RMSNorm kernel and the first row of its table) fixes the
+ * numerics, including the order of the sum of squares:
+ *   - each group of 8 consecutive elements e_0..e_7 is summed as a
+ *     horizontal 8-wide sum: lo_k = e_k^2 + e_(k+4)^2 for k < 4, then
+ *     (lo_0 + lo_1) + (lo_2 + lo_3);
+ *   - the group sums are added one after the other, left to right, into a
+ *     single fp32 accumulator that starts at zero (ss = ss + group);
+ *   - r = 1.0f / sqrtf(ss / K + eps), a correctly rounded division and
+ *     square root, not an rsqrt approximation;
+ *   - out_i = (x_i * r) * w_i.
+ * Every operation is one fp32 operation (built with -ffp-contract=off, so
+ * nothing is fused).  K is a multiple of 32 here, so no element is left over
+ * after the last group of 8.
  * xn is [M][K] fp32; ss[m] receives the row's sum of squares. */
 void oracle_rmsnorm(const float *x, const float *w, float eps, int64_t M, int64_t K, float *xn,
                     float *ss) {
-  int64_t nblk = K / OR_Q8_BLOCK;
-  int64_t p2 = 1;
-  while (p2 < nblk) p2 *= 2;
-  float *u = (float *)calloc((size_t)p2, sizeof(float));
   for (int64_t m = 0; m < M; ++m) {
     const float *xr = x + m * K;
-    for (int64_t i = 0; i < p2; ++i) u[i] = 0.0f;
-    for (int64_t b = 0; b < nblk; ++b) {
-      float t[4];
-      for (int g = 0; g < 4; ++g) {
-        const float *e = xr + b * OR_Q8_BLOCK + 8 * g;
-        float lo[4];
-        for (int k = 0; k < 4; ++k) {
-          float s0 = e[k] * e[k];
-          float s1 = e[k + 4] * e[k + 4];
-          lo[k] = s0 + s1;
-        }
-        float s01 = lo[0] + lo[1];
-        float s23 = lo[2] + lo[3];
-        t[g] = s01 + s23;
+    float acc = 0.0f;
+    for (int64_t g = 0; g + 8 <= K; g += 8) {
+      const float *e = xr + g;
+      float lo[4];
+      for (int k = 0; k < 4; ++k) {
+        float s0 = e[k] * e[k];
+        float s1 = e[k + 4] * e[k + 4];
+        lo[k] = s0 + s1;
       }
-      float t01 = t[0] + t[1];
-      float t23 = t[2] + t[3];
-      u[b] = t01 + t23;
+      float s01 = lo[0] + lo[1];
+      float s23 = lo[2] + lo[3];
+      float grp = s01 + s23;
+      acc = acc + grp;
     }
-    for (int64_t len = p2; len > 1; len /= 2)
-      for (int64_t i = 0; i < len / 2; ++i) u[i] = u[2 * i] + u[2 * i + 1];
-    float mean = u[0] / (float)K;
+    float mean = acc / (float)K;
     float r = 1.0f / sqrtf(mean + eps);
-    ss[m] = u[0];
+    ss[m] = acc;
     for (int64_t k = 0; k < K; ++k) {
       float a = xr[k] * r;
       xn[m * K + k] = a * w[k];
     }
   }
-  free(u);
 }
 
 /* Exact dequantization of Q8_1 blocks: xhat[m][k] = D * q. */
@@ -435,11 +453,13 @@ int oracle_isums(const uint8_t *W, int type, int64_t N, int64_t K,
   if (check_args(type, N, K, M)) return -1;
   int bb = block_bytes(type);
   int64_t nsb = K / OR_QK, nq8 = K / OR_Q8_BLOCK;
-  oracle_sb s;
-  decode_sb(type, W, &s); /* for sublen */
-  int64_t nsubrow = K / s.sublen;
+  oracle_sb s0;
+  decode_sb(type, W, &s0); /* for sublen */
+  int64_t nsubrow = K / s0.sublen;
+#pragma omp parallel for schedule(dynamic, 16)
   for (int64_t n = 0; n < N; ++n)
     for (int64_t b = 0; b < nsb; ++b) {
+      oracle_sb s;
       decode_sb(type, W + (n * nsb + b) * bb, &s);
       for (int64_t m = 0; m < M; ++m)
         for (int j = 0; j < s.nsub; ++j) {
@@ -469,11 +489,12 @@ int oracle_qmatmul(const uint8_t *W, int type, int64_t N, int64_t K,
   if (check_args(type, N, K, M)) return -1;
   int bb = block_bytes(type);
   int64_t nsb = K / OR_QK, nq8 = K / OR_Q8_BLOCK;
-  oracle_sb s;
+#pragma omp parallel for collapse(2) schedule(dynamic, 16)
   for (int64_t m = 0; m < M; ++m)
     for (int64_t n = 0; n < N; ++n) {
       double acc = 0.0, aabs = 0.0;
       for (int64_t b = 0; b < nsb; ++b) {
+        oracle_sb s;
         decode_sb(type, W + (n * nsb + b) * bb, &s);
         for (int j = 0; j < s.nsub; ++j) {
           int64_t k0 = b * OR_QK + (int64_t)j * s.sublen;
@@ -511,19 +532,29 @@ int oracle_qmatmul_rows(const uint8_t *W, int type, int64_t N, int64_t K,
   for (int64_t r = 0; r < nrows; ++r) {
     if (rows[r] < 0 || rows[r] >= N) return -1;
   }
-  double *t64 = (double *)malloc(sizeof(double) * (size_t)M);
-  double *tab = (double *)malloc(sizeof(double) * (size_t)M);
-  if (!t64 || !tab) { free(t64); free(tab); return -2; }
-  for (int64_t r = 0; r < nrows; ++r) {
-    oracle_qmatmul(W + rows[r] * row_bytes, type, 1, K, xq, M, t64, tab, NULL);
-    for (int64_t m = 0; m < M; ++m) {
-      if (y64) y64[m * nrows + r] = t64[m];
-      if (absum) absum[m * nrows + r] = tab[m];
+  int fail = 0;
+#pragma omp parallel
+  {
+    double *t64 = (double *)malloc(sizeof(double) * (size_t)M);
+    double *tab = (double *)malloc(sizeof(double) * (size_t)M);
+    if (!t64 || !tab) {
+#pragma omp atomic write
+      fail = 1;
     }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+      if (!t64 || !tab) continue;
+      /* one output row: the single-row matmul above, run by this thread */
+      oracle_qmatmul(W + rows[r] * row_bytes, type, 1, K, xq, M, t64, tab, NULL);
+      for (int64_t m = 0; m < M; ++m) {
+        if (y64) y64[m * nrows + r] = t64[m];
+        if (absum) absum[m * nrows + r] = tab[m];
+      }
+    }
+    free(t64);
+    free(tab);
   }
-  free(t64);
-  free(tab);
-  return 0;
+  return fail ? -2 : 0;
 }
 
 /* ------------------------------------------------ int4-KV decode attention */

@@ -30,8 +30,13 @@ def f16_frac(bits):
     return Fraction(float(np.array([bits], dtype=np.uint16).view(np.float16)[0]))
 
 
-def random_f16_bits(rng, scale=1e-3, allow_sub=True):
-    v = abs(rng.standard_normal()) * scale
+def random_f16_bits(rng, scale=1e-3, allow_sub=True, signed=True):
+    """fp16 bits of N(0, scale^2) (|N| when signed is False).  The workloads
+    draw positive d and dmin, but the formats store them as signed binary16,
+    so the pins feed both signs."""
+    v = rng.standard_normal() * scale
+    if not signed:
+        v = abs(v)
     b = f16_bits(v)
     if not allow_sub and (b & 0x7C00) == 0:
         b |= 0x0400

@@ -14,8 +14,9 @@
   argmax kept (golden fixture with its citation).
 - RMSNorm (the fused producer of the Q8_1 activations): a closed form on
   constant rows, exact power-of-two scale invariances, the fp64 formula within
-  the fp32 error bound, and the stated summation tree on an input where
-  another order gives another fp32 sum.
+  the fp32 error bound, and the page's summation order (8-element group sums
+  added left to right) on a row worked out by hand where other orders give
+  other fp32 sums.
 """
 import json
 import os
@@ -108,6 +109,60 @@ def test_q8_1_ties_round_away_from_zero(oracle_lib):
     assert list(q[0, 0, :12]) == [127, 1, -1, 2, -2, 3, -3, 127, -127, 0, 2, -4]
 
 
+def _rne32(v):
+    """Exact round-to-nearest-even of a Fraction to binary32 (normal range)."""
+    v = Fraction(v)
+    if v == 0:
+        return Fraction(0)
+    sgn, a = (-1 if v < 0 else 1), abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while a / Fraction(2) ** e >= 2:
+        e += 1
+    while a / Fraction(2) ** e < 1:
+        e -= 1
+    m = a / Fraction(2) ** (e - 23)            # in [2^23, 2^24)
+    n = m.numerator // m.denominator
+    rem = m - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sgn * Fraction(n) * Fraction(2) ** (e - 23)
+
+
+def _round_half_away(v):
+    a = abs(Fraction(v))
+    n = a.numerator // a.denominator
+    if a - n >= Fraction(1, 2):
+        n += 1
+    return n if v >= 0 else -n
+
+
+def test_q8_1_division_is_correctly_rounded(oracle_lib):
+    """Readings R1-R2: d32 = amax / 127 and q = roundf(x / d32), each one
+    correctly rounded fp32 division.  The block below (amax = A) was chosen
+    so that both reciprocal shortcuts give other codes: d32 taken as
+    A * fl(1/127) is one ulp lower, and x * fl(1/d32) rounds across a
+    half-integer.  The expected codes come from exact rational arithmetic."""
+    A = 1.6125396490097046
+    xs = [A, 0.08253155648708344, -0.33647480607032776, 0.5269322395324707,
+          -0.5396293997764587, 0.0698343887925148, 0.03174290433526039, -0.057137228548526764]
+    x = np.zeros((1, 32), np.float32)
+    x[0, :len(xs)] = xs
+    assert all(float(np.float32(v)) == v for v in xs)
+    d32 = _rne32(Fraction(A) / 127)
+    exp = [_round_half_away(_rne32(Fraction(v) / d32)) for v in xs]
+    # the shortcuts' codes differ (so a shortcut in the oracle would fail here)
+    d_rcp = _rne32(Fraction(A) * _rne32(Fraction(1, 127)))
+    q_rcp = [_round_half_away(_rne32(Fraction(v) * _rne32(1 / d32))) for v in xs]
+    q_drcp = [_round_half_away(_rne32(Fraction(v) / d_rcp)) for v in xs]
+    assert d_rcp != d32 and q_rcp != exp and q_drcp != exp
+    assert exp[:7] == [127, 6, -26, 41, -42, 5, 2]
+    D, S, q = _q8_fields(oracle_lib.quantize_q8_1(x), 1, 32)
+    assert list(q[0, 0, :len(xs)]) == exp
+    assert not q[0, 0, len(xs):].any()
+    assert D[0, 0] == float(np.float16(float(d32)))
+    assert Fraction(S[0, 0]) == Fraction(float(np.float16(float(Fraction(D[0, 0]) * sum(exp)))))
+
+
 def test_q8_1_dequant_is_d_times_q(oracle_lib):
     rng = np.random.default_rng(6)
     x = rng.standard_normal((2, 512)).astype(np.float32)
@@ -158,7 +213,7 @@ def test_decoder_single_bit_positions(oracle_lib, wtype):
         base["sc"] = [int(v) or 1 for v in base["sc"]]
         key, val = "code", 21
     elif wtype in (qf.Q4_0, qf.Q8_0):
-        base["d"] = [v or 0x3C00 for v in base["d"]]
+        base["d"] = [v if v & 0x7FFF else 0x3C00 for v in base["d"]]
         base["q"] = [0] * 256
         key, val = "q", 9 if wtype == qf.Q4_0 else 77
     else:
@@ -342,8 +397,8 @@ def test_activation_quantization_noise_matches_pages(oracle_lib, wtype):
 
 # ------------------------------------------------ RMSNorm (fused producer)
 # Pins of oracle.rmsnorm: a closed form, exact scale invariances, the fp64
-# textbook formula within the fp32 error bound, and the stated summation
-# tree on an input where a different order gives a different fp32 sum.
+# textbook formula within the fp32 error bound, and the page's summation
+# order on a row worked out by hand where other orders give other fp32 sums.
 def test_rmsnorm_constant_row_is_exactly_unit(oracle_lib):
     """x = c (a power of two), w = 1, eps = 0: mean = c^2, r = 1/|c| exactly,
     so every output is +-1 and the quantized block is the closed form."""
@@ -394,19 +449,52 @@ def test_rmsnorm_matches_fp64_formula(oracle_lib, eps):
 
 
 def test_rmsnorm_sum_of_squares_order(oracle_lib):
-    """x = [2^12, 1, 1, ...] over K = 64: the 8-group sums give
-    (2^24 + 2) + 4 = 2^24 + 6 for the first group and 8 for the others, the
-    blocks (2^24 + 6 + 8) + 16 = 2^24 + 30 and 32, the tree 2^24 + 62; a
-    left-to-right fp32 sum stays at 2^24 (each +1 on 2^24 rounds back)."""
+    """Kestrel_VLLM #18, section 3.6: each group of 8 squares is summed as
+    (lo0 + lo1) + (lo2 + lo3), lo_k = s_k + s_(k+4), and the group sums are
+    added left to right into one fp32 accumulator.  Row (K = 64): group 0 is
+    [2^12, 1, 1, 1, 1, 1, 1, 1], groups 1..7 are [1, 0, ..., 0].
+      group 0: lo0 = 2^24 + 1, a tie, rounds to the even 2^24; lo1..lo3 = 2;
+               s01 = 2^24 + 2, s23 = 4, group = 2^24 + 6 (all exact);
+      groups 1..7: 1 each.
+      serial:  (2^24 + 6) + 1 = 2^24 + 7, a tie between 2^24 + 6 (odd
+               significand) and 2^24 + 8 (even): 2^24 + 8; every further + 1
+               is a tie that rounds back to 2^24 + 8.  ss = 2^24 + 8.
+    Other orders give other sums on this row (worked out the same way): the
+    four groups of a 32-element block pairwise, then the blocks, gives
+    2^24 + 14; one element at a time gives 2^24."""
     K = 64
-    x = np.ones((1, K), np.float32)
-    x[0, 0] = 2.0 ** 12
+    x = np.zeros((1, K), np.float32)
+    x[0, 0:8] = [2.0 ** 12, 1, 1, 1, 1, 1, 1, 1]
+    x[0, 8::8] = 1.0
     _, ss = oracle_lib.rmsnorm(x, np.ones(K, np.float32), 0.0)
-    assert ss[0] == np.float32(2.0 ** 24 + 62)
-    seq = np.float32(0)
-    for v in (x[0].astype(np.float32) ** 2):
-        seq = np.float32(seq + v)
-    assert seq != ss[0]
+    assert ss[0] == np.float32(2.0 ** 24 + 8)
+    # the orders the page does not use give 2^24 + 14 and 2^24 on this row
+    assert ss[0] != np.float32(2.0 ** 24 + 14) and ss[0] != np.float32(2.0 ** 24)
+    # r and the outputs follow from ss: r = 1 / sqrt(ss / 64), x * r * 1
+    r = np.float32(1.0) / np.sqrt(np.float32(ss[0] / np.float32(K)), dtype=np.float32)
+    xn, _ = oracle_lib.rmsnorm(x, np.ones(K, np.float32), 0.0)
+    assert np.array_equal(xn[0], (x[0] * r).astype(np.float32))
+
+
+def test_rmsnorm_group_order_on_random_rows(oracle_lib):
+    """The serial group order on ordinary rows: ss equals the group sums
+    (each formed as the page's 8-wide horizontal sum) added left to right in
+    numpy float32, for every row; the fp64 sum of squares is within K*2^-24
+    relative of it."""
+    rng = np.random.default_rng(13)
+    M, K = 6, 4096
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    _, ss = oracle_lib.rmsnorm(x, np.ones(K, np.float32), 1e-6)
+    sq = (x * x).astype(np.float32).reshape(M, K // 8, 8)
+    lo = (sq[:, :, 0:4] + sq[:, :, 4:8]).astype(np.float32)
+    grp = ((lo[:, :, 0] + lo[:, :, 1]).astype(np.float32) + (lo[:, :, 2] + lo[:, :, 3]).astype(np.float32))
+    for m in range(M):
+        acc = np.float32(0.0)
+        for g in grp[m].astype(np.float32):
+            acc = np.float32(acc + g)
+        assert ss[m] == acc, m
+    ref = (x.astype(np.float64) ** 2).sum(axis=1)
+    assert np.all(np.abs(ss - ref) <= K * 2.0 ** -24 * ref)
 
 
 def test_rmsnorm_zero_row_quantizes_to_zero(oracle_lib):
