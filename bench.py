@@ -188,47 +188,135 @@ def copy_reference(dev, launch_bytes, reps=10):
     return out
 
 
-def cpu_baseline(shapes, cfg_idx, Ms, budget_s=20.0, prefill=False):
-    """The CPU oracle (plain scalar C, fp64, one thread) on a bounded sample:
-    the first layer's projections at each M, stopping once the budget is spent.
-    Decode: whole projections, rated in weight GB/s.  Prefill: 64 weight rows
-    of each projection for all M rows, rated in int8 TOP/s (2 ops per MAC)."""
+def cpu_info():
+    """Host CPU model (from /proc/cpuinfo) and the cores this process may use."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count()
+    return model, nproc
+
+
+def cpu_baseline(shapes, cfg_idx, Ms, prefill=False, layers=36):
+    """The CPU oracle (plain scalar C, fp64) timed on a bounded sample of the
+    same workload, twice: on one thread and on every thread OpenMP gives it
+    (OMP_NUM_THREADS, else all cores), with the loop over output rows split
+    across threads (no change to any output's arithmetic).  It is a
+    correctness reference, not a tuned CPU kernel.
+      decode:  layer 0's projections, whole matmuls at every M (quantize +
+               qmatmul), in weight GB/s;
+      prefill: the full q (4096 x 4096) and down (4096 x 12288) matrices at
+               M = 512 on all threads, 256 weight rows of each on one thread,
+               in int8 TOP/s (2 ops per MAC); the 36-layer sweep time is
+               extrapolated from that rate and labelled as such."""
     import numpy as np
     import oracle
     from quant_integer_dot_amd import synth
-    done_bytes = 0
-    done_ops = 0
-    t_used = 0.0
-    parts = []
-    for M in Ms:
-        for pi, (name, N, K, t) in enumerate(shapes):
-            if t_used > budget_s:
-                break
+    model, nproc = cpu_info()
+
+    def timed(threads, jobs):
+        oracle.set_threads(threads)
+        used = oracle.max_threads()
+        t0 = time.perf_counter()
+        for fn in jobs:
+            fn()
+        return time.perf_counter() - t0, used
+
+    note = "the oracle: plain scalar C, fp64; a correctness reference, not a tuned CPU kernel"
+    if prefill:
+        picks = [(pi, sh) for pi, sh in enumerate(shapes) if sh[0] in ("q", "down")]
+        M = Ms[0]
+        data = []
+        for pi, (name, N, K, t) in picks:
             W = synth.weights(t, N, K, synth.weight_seed(cfg_idx, 0, pi))
             x = synth.activations(M, K, synth.act_seed(cfg_idx, K, M))
-            t0 = time.perf_counter()
-            xq = oracle.quantize_q8_1(x)
-            if prefill:
-                rows = np.arange(64)
-                oracle.qmatmul_rows(W, t, N, K, xq, M, rows)
-                done_ops += 2 * M * rows.size * K
-            else:
-                oracle.qmatmul(W, t, N, K, xq, M)
-            t_used += time.perf_counter() - t0
-            done_bytes += W.nbytes
+            data.append((name, N, K, t, W, x))
+        rows = np.arange(256)
+        one = [lambda d=d: oracle.qmatmul_rows(d[4], d[3], d[1], d[2], oracle.quantize_q8_1(d[5]), M, rows)
+               for d in data]
+        full = [lambda d=d: oracle.qmatmul(d[4], d[3], d[1], d[2], oracle.quantize_q8_1(d[5]), M) for d in data]
+        ops_one = sum(2 * M * rows.size * d[2] for d in data)
+        ops_full = sum(2 * M * d[1] * d[2] for d in data)
+        t1, _ = timed(1, one)
+        tn, used = timed(0, full)
+        oracle.set_threads(0)
+        rate = ops_full / tn / 1e12
+        sweep_ops = sum(2 * M * N * K for _, N, K, _ in shapes) * layers
+        names = " and ".join(f"{d[0]} {d[1]}x{d[2]}" for d in data)
+        return {"value": round(rate, 6), "unit": "TOP/s", "cores": used, "kind": "oracle",
+                "sample": f"layer 0 of the same workload: the full {names} matrices at M={M} "
+                          f"({ops_full / 1e9:.1f} G int8 ops, {tn:.1f} s on {used} threads); single thread: "
+                          f"256 weight rows of each ({ops_one / 1e9:.1f} G ops, {t1:.1f} s)",
+                "single_thread": {"value": round(ops_one / t1 / 1e12, 6), "unit": "TOP/s", "cores": 1},
+                "sweep_s_extrapolated": round(sweep_ops / (rate * 1e12), 1),
+                "sweep_note": f"extrapolated: {sweep_ops / 1e12:.2f} T int8 ops per {layers}-layer sweep "
+                              f"at the all-threads rate",
+                "nproc": nproc, "cpu_model": model, "note": note}
+    jobs, parts, wbytes = [], [], 0
+    for M in Ms:
+        for pi, (name, N, K, t) in enumerate(shapes):
+            W = synth.weights(t, N, K, synth.weight_seed(cfg_idx, 0, pi))
+            x = synth.activations(M, K, synth.act_seed(cfg_idx, K, M))
+            jobs.append(lambda W=W, t=t, N=N, K=K, x=x, M=M:
+                        oracle.qmatmul(W, t, N, K, oracle.quantize_q8_1(x), M))
+            wbytes += W.nbytes
             parts.append(f"{name}@M={M}")
-    cpu = platform.processor() or platform.machine()
-    if prefill:
-        return {"value": round(done_ops / t_used / 1e12, 6), "unit": "TOP/s", "cores": 1,
-                "kind": "oracle",
-                "sample": f"layer 0 of the same workload, weight rows 0-63 of {', '.join(parts)} "
-                          f"({done_ops / 1e9:.1f} G int8 ops, {t_used:.1f} s, single thread, "
-                          f"quantize + qmatmul per projection; CPU: {cpu})"}
-    return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"layer 0 of the same workload: {', '.join(parts)} "
-                      f"({done_bytes / 1e6:.1f} MB of weights, {t_used:.1f} s, single thread, "
-                      f"quantize + qmatmul per projection; CPU: {cpu})"}
+    t1, _ = timed(1, jobs)
+    tn, used = timed(0, jobs)
+    oracle.set_threads(0)
+    return {"value": round(wbytes / tn / 1e9, 4), "unit": "GB/s", "cores": used, "kind": "oracle",
+            "sample": f"layer 0 of the same workload, whole matmuls: {', '.join(parts)} "
+                      f"({wbytes / 1e6:.1f} MB of weights, quantize + qmatmul per projection; "
+                      f"{tn:.2f} s on {used} threads, {t1:.1f} s on one)",
+            "single_thread": {"value": round(wbytes / t1 / 1e9, 4), "unit": "GB/s", "cores": 1},
+            "nproc": nproc, "cpu_model": model, "note": note}
+
+
+def stream_reference(dev, launch_bytes, reps=10):
+    """Measured read-only reference for the decode roofline: the library's
+    plain streaming read kernel (qdot_stream_read), once over 512 MiB (the
+    streaming rate) and once as 36 reads of the dominant kernel's bytes per
+    launch, each from its own buffer (cold in the Infinity Cache), timed
+    together between HIP events (what one launch of that size reaches)."""
+    import torch
+    from quant_integer_dot_amd import binding as qd
+    out = {}
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    n = 512 << 20
+    a = torch.ones(n, dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        qd.qdot_stream_read(a, n, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        qd.qdot_stream_read(a, n, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    out["read_512MiB_GBps"] = round(n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del a
+    m = int(launch_bytes) // 256 * 256
+    srcs = [torch.ones(m, dtype=torch.uint8, device=dev) for _ in range(36)]
+    for b_ in srcs:
+        qd.qdot_stream_read(b_, m, sink)
+    torch.cuda.synchronize()
+    e0.record()
+    for b_ in srcs:
+        qd.qdot_stream_read(b_, m, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / 36
+    out["read_at_launch_size"] = {"bytes_per_read": m, "us": round(t * 1e6, 3), "GBps": round(m / t / 1e9, 1)}
+    return out
 
 
 def producer_bench(args):
@@ -723,7 +811,10 @@ def main():
                     "launches": dn, "avg_launch_us": round(dms * 1e3 / dn, 3),
                     "algorithmic_bytes_per_launch": round(dbytes / dn)}
         ref = copy_reference(dev, dbytes / dn)
+        ref.update(stream_reference(dev, dbytes / dn))
         ref["frac_of_copy_512MiB"] = round(achieved / ref["copy_512MiB_GBps"], 4)
+        ref["frac_of_read_512MiB"] = round(achieved / ref["read_512MiB_GBps"], 4)
+        ref["frac_of_read_at_launch_size"] = round(achieved / ref["read_at_launch_size"]["GBps"], 4)
         roofline["measured_reference"] = ref
     kernels = {k: {"launches_per_step": v[2], "ms_per_step": round(v[1], 4),
                    "GBps": round(v[0] / (v[1] * 1e-3) / 1e9, 1),
@@ -755,7 +846,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(shapes, cfg_idx, Ms, prefill=prefill)
+        cpu = cpu_baseline(shapes, cfg_idx, Ms, prefill=prefill, layers=layers)
 
     if prefill:
         metric, unit = "int8 TOP/s (% of MFMA int8 peak), M=512 prefill chunk, Qwen3-8B shapes", "TOP/s"

@@ -120,13 +120,22 @@ int qdot_quantize_q8_1(const float *x, int64_t M, int64_t K, void *x_q8,
  * kernel's upper end depends on the matrix: qdot_kernel_name_shape).  Within
  * each of these three ranges a row of y is bitwise the same whatever M it is
  * computed with; across them it may differ in the last fp32 bit (different
- * fp64 summation orders).  K % 256 == 0 is required. */
+ * fp64 summation orders).  K % 256 == 0 is required.
+ * The operation is the xLLM v0.7 log's integer-dot matmul on raw Q4_K / Q6_K
+ * weights (section 1 "background"; section B2, the M-templated tile that
+ * reads each weight once for all M rows), with the sub-block dot an exact
+ * int32 sum and the scales applied after it (Kestrel_VLLM #18, section 5);
+ * the IQ4_XS sub-block scale d*(ls-32) and its codebook lookup are the
+ * V100TPS log's (2026-08-12 entries). */
 int qdot_qmatmul(const void *W, int type, int64_t N, int64_t K,
                  const void *x_q8, int64_t M, float *y, void *stream);
 
 /* Same as qdot_qmatmul (same kernel template, same y) and also writes every
  * integer sub-block sum I to isums [M][N][K/S] (int32, device,
- * qdot_isum_count elements): a debug dump for bit-exact checks. */
+ * qdot_isum_count elements): a debug dump for bit-exact checks against a CPU
+ * reference, after the Kestrel_VLLM #18 page's practice of dumping the same
+ * intermediate buffers on the CPU and the GPU side and diffing them to find
+ * the first value that differs (section 3.4, the full-model dump harness). */
 int qdot_qmatmul_dump_isums(const void *W, int type, int64_t N, int64_t K,
                             const void *x_q8, int64_t M, float *y,
                             int32_t *isums, void *stream);
@@ -158,9 +167,10 @@ int qdot_qmatmul_multi(int n, const void *const *W, const int *types,
  * buffer).  Per row of x [M][K] (fp32, device): ss = sum of x_k^2, r =
  * 1.0f / sqrtf(ss / K + eps), xn_k = (x_k * r) * w_k, all in fp32 with
  * correctly rounded division and square root as on the Kestrel_VLLM #18
- * page (section 3.6); ss is summed in a fixed order (each group of 8 squares
- * as on that page, the four groups of a 32-element block pairwise, the blocks
- * in a pairwise tree), so the output bytes are reproducible bit for bit.  xn
+ * page (section 3.6); ss is summed in that page's order (each group of 8
+ * squares as lo_k = s_k + s_(k+4), (lo0 + lo1) + (lo2 + lo3), and the group
+ * sums added left to right into one fp32 accumulator), so the output bytes
+ * equal those of a plain serial CPU loop bit for bit.  xn
  * is then quantized exactly as qdot_quantize_q8_1 does.  w is fp32 [K]
  * (device); x_q8 receives qdot_q8_1_bytes(M, K) bytes.  32 <= K <=
  * QDOT_RMSNORM_MAX_K, K % 32 == 0, eps finite and >= 0, else E_ARG; x, w,
@@ -212,10 +222,16 @@ size_t qdot_attn_kv4_row_bytes(int64_t D);
  * outputs, fp32); 0 for Hq or T out of range. */
 size_t qdot_attn_kv4_workspace_bytes(int64_t Hq, int64_t T);
 
-/* Static text for a status code. */
+/* Static text for a status code.  Failures are reported, never papered
+ * over by a slower path: the xLLM v0.7 log's fail-fast rule (section A2.2,
+ * a failed preload aborts loudly) and its explicit decode-mode contract
+ * (section B1.2, a mismatch errors out instead of degrading). */
 const char *qdot_status_str(int status);
 
-/* Name of the kernel qdot_qmatmul runs for (type, M) on a matrix of the
+/* Which kernel ran, so that a measurement names its arm (the V100TPS log
+ * prints the live kernel path with every benchmark entry, e.g. the
+ * 2026-08-12 batch-kernel entries).
+ * Name of the kernel qdot_qmatmul runs for (type, M) on a matrix of the
  * default ranges (decode tile for M <= 8, and for M <= 16 with Q4_K and
  * IQ4_XS; M <= 96 mid-batch kernel; larger M prefill kernel), e.g.
  * "qmv_dot4<Q4_K,4>", "qmv_mfma<Q4_K,8>", "qmv_mfma<IQ4_XS,12>",
@@ -240,6 +256,17 @@ const char *qdot_kernel_name_shape(int type, int64_t N, int64_t K, int64_t M);
  * be rejected or i is out of range.  Static text. */
 const char *qdot_multi_kernel_name(int n, const int *types, const int64_t *N,
                                    int64_t K, int64_t M, int i);
+
+/* Measurement reference, not part of the matmul path: reads `bytes` bytes
+ * at src (device, 16-byte aligned, bytes a positive multiple of 16) once with
+ * coalesced 16-byte loads and no arithmetic beyond an XOR fold, the plain
+ * read-only rate the HBM-bound decode launches are compared with (the pages
+ * judge a kernel by its bandwidth against what the memory delivers: xLLM
+ * v0.7 log, section B2, the ncu DRAM-throughput table).  sink: one device
+ * dword, written only when the fold hits a fixed improbable value.  Errors:
+ * E_ARG for null pointers or a bad size, E_ALIGN, E_HIP. */
+int qdot_stream_read(const void *src, int64_t bytes, uint32_t *sink,
+                     void *stream);
 
 /* Build identifier of the library (compile date and time).  Static text. */
 const char *qdot_build_id(void);

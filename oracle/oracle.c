@@ -109,10 +109,13 @@ uint16_t oracle_double_to_half(double v) {
 }
 
 /* Host threads used by the loops over outputs below (1 when built without
- * OpenMP).  n < 1 leaves the OpenMP default (OMP_NUM_THREADS or all cores). */
+ * OpenMP).  n < 1 restores the OpenMP default this process started with
+ * (OMP_NUM_THREADS, else all cores). */
 void oracle_set_threads(int n) {
 #ifdef _OPENMP
-  if (n >= 1) omp_set_num_threads(n);
+  static int initial = 0;
+  if (initial == 0) initial = omp_get_max_threads();
+  omp_set_num_threads(n >= 1 ? n : initial);
 #else
   (void)n;
 #endif

@@ -72,6 +72,8 @@ def load():
     L.qdot_kernel_name_shape.restype = ctypes.c_char_p
     L.qdot_multi_kernel_name.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(i64), i64, i64, i32]
     L.qdot_multi_kernel_name.restype = ctypes.c_char_p
+    L.qdot_stream_read.argtypes = [P, i64, P, P]
+    L.qdot_stream_read.restype = i32
     L.qdot_build_id.argtypes = []
     L.qdot_build_id.restype = ctypes.c_char_p
     _lib = L
@@ -195,6 +197,12 @@ def qdot_multi_kernel_name(types, Ns, K, M, i):
     ta = (ctypes.c_int * n)(*types)
     na = (ctypes.c_int64 * n)(*Ns)
     return load().qdot_multi_kernel_name(n, ta, na, K, M, i).decode()
+
+
+def qdot_stream_read(src, nbytes, sink, stream=None):
+    """Read-only streaming reference kernel over nbytes of src (measurement)."""
+    s = _stream(stream, sink)
+    _check(load().qdot_stream_read(_addr(src), int(nbytes), _addr(sink), s), "qdot_stream_read")
 
 
 def qdot_build_id():

@@ -22,6 +22,7 @@ int launch_qmm_skinny(const void* W, int type, int N, int K, const void* xq, int
 int launch_qmv_multi(int n, const void* const* W, const int* types, const int* N, int K, const void* xq,
                      int M, float* const* y, hipStream_t s);
 bool qmv_multi_uses_mfma(int n, const int* types, const int* N, int K, int M, int i);
+int launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);
 }  // namespace qdot
 
 namespace {
@@ -248,6 +249,13 @@ const char* qdot_multi_kernel_name(int n, const int* types, const int64_t* N, in
   if (qdot::qmv_multi_uses_mfma(n, types, n32, (int)K, (int)M, i))
     return mfma[types[i] == QDOT_Q4_K ? 0 : 1][M - 1];
   return dot4[types[i] - 1][M - 1];
+}
+
+int qdot_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink || bytes < 16 || bytes % 16 != 0) return QDOT_E_ARG;
+  if ((reinterpret_cast<uintptr_t>(src) & 15u) != 0 || !aligned4(sink)) return QDOT_E_ALIGN;
+  int rc = qdot::launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream));
+  return rc == 0 ? QDOT_OK : QDOT_E_HIP;
 }
 
 const char* qdot_build_id(void) { return "libqdot gfx950 " __DATE__ " " __TIME__; }

@@ -3,20 +3,22 @@
 // of a norm launch followed by a quantize launch (the xLLM engine keeps one
 // quantized normalized-input buffer per step, d_xn_q8, section C.1).
 //
-// Numerics as the Kestrel_VLLM #18 page gives them (section 3.6): fp32
-// throughout, r = 1.0f / sqrtf(ss / K + eps) with correctly rounded division
-// and square root (never an rsqrt approximation), out = (x * r) * w.  The sum
-// of squares ss is formed in a fixed order: each group of 8 squares s_0..s_7
-// as (lo0 + lo1) + (lo2 + lo3) with lo_k = s_k + s_(k+4), the four groups of a
-// 32-element block pairwise, and the block sums in a pairwise tree -- inside a
-// wave by xor shuffles (lane i adds lane i ^ s at s = 1, 2, 4, ...), then over
-// the waves in the same pairing.  FMA contraction is off in this file, so
+// Numerics as the Kestrel_VLLM #18 page gives them (section 3.6, its
+// CPU-order RMSNorm kernel and the first row of its table): fp32 throughout;
+// each group of 8 consecutive squares s_0..s_7 summed as (lo0 + lo1) +
+// (lo2 + lo3) with lo_k = s_k + s_(k+4); the group sums added left to right
+// into one accumulator (the page's fix for a GPU tree reduction that broke
+// bitwise agreement with the CPU); r = 1.0f / sqrtf(ss / K + eps) with
+// correctly rounded division and square root (never an rsqrt
+// approximation); out = (x * r) * w.  FMA contraction is off in this file, so
 // every operation rounds once, as written.  The normalized values then go
 // through the quantizer's own reading (amax/127, roundf(x/d32), fp16 D and S).
 //
-// Mapping: one workgroup per row, thread b owns Q8_1 block b (32 elements;
-// K <= 32768).  Threads past the last block hold a zero sum (adding +0 is
-// exact, so the tree's padding does not change the value).
+// Mapping: one workgroup per row, thread b owns Q8_1 block b (32 elements,
+// four groups of 8; K <= 32768).  The group sums are formed in parallel and
+// staged in LDS; one thread then adds all K/8 of them in order (the only
+// serial part: K/8 dependent fp32 adds), and every thread normalizes and
+// quantizes its own block.
 #include "qdot_common.hpp"
 
 #pragma clang fp contract(off)
@@ -28,17 +30,15 @@ constexpr int RN_MAX_THREADS = 1024;
 __global__ __launch_bounds__(RN_MAX_THREADS) void rmsnorm_q8_1_kernel(
     const float* __restrict__ x, const float* __restrict__ w, float eps, int K,
     uint8_t* __restrict__ out) {
-  __shared__ float wave_sum[RN_MAX_THREADS / 64];
+  __shared__ float4 group_sums[RN_MAX_THREADS];  // block b's four group sums
   __shared__ float r_shared;
   const int m = blockIdx.x;
   const int b = threadIdx.x;
   const int nb = K / Q8_BLOCK;
-  const int lane = b & 63, wave = b >> 6, waves = blockDim.x >> 6;
   const bool live = b < nb;
 
   float v[Q8_BLOCK];
   u32x4 wr[Q8_BLOCK / 4];  // this block's weights, loaded with x (one memory round trip)
-  float u = 0.0f;
   if (live) {
     const uint8_t* xb = reinterpret_cast<const uint8_t*>(x + (size_t)m * K + (size_t)b * Q8_BLOCK);
     const uint8_t* wb = reinterpret_cast<const uint8_t*>(w + (size_t)b * Q8_BLOCK);
@@ -65,18 +65,20 @@ __global__ __launch_bounds__(RN_MAX_THREADS) void rmsnorm_q8_1_kernel(
       const float s23 = lo[2] + lo[3];
       t[g] = s01 + s23;
     }
-    const float t01 = t[0] + t[1];
-    const float t23 = t[2] + t[3];
-    u = t01 + t23;
+    group_sums[b] = make_float4(t[0], t[1], t[2], t[3]);
   }
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) u = u + __shfl_xor(u, s);
-  if (lane == 0) wave_sum[wave] = u;
   __syncthreads();
   if (b == 0) {
-    for (int len = waves; len > 1; len >>= 1)
-      for (int i = 0; i < len / 2; ++i) wave_sum[i] = wave_sum[2 * i] + wave_sum[2 * i + 1];
-    const float mean = wave_sum[0] / (float)K;
+    float ss = 0.0f;  // the groups in order, one accumulator
+#pragma unroll 8
+    for (int i = 0; i < nb; ++i) {
+      const float4 g = group_sums[i];
+      ss = ss + g.x;
+      ss = ss + g.y;
+      ss = ss + g.z;
+      ss = ss + g.w;
+    }
+    const float mean = ss / (float)K;
     r_shared = 1.0f / sqrtf(mean + eps);
   }
   __syncthreads();
@@ -122,8 +124,7 @@ __global__ __launch_bounds__(RN_MAX_THREADS) void rmsnorm_q8_1_kernel(
 int launch_rmsnorm_q8_1(const float* x, const float* w, float eps, int64_t M, int64_t K, void* xq,
                         hipStream_t s) {
   const int nb = (int)(K / Q8_BLOCK);
-  int threads = 64;
-  while (threads < nb) threads *= 2;
+  const int threads = (nb + 63) / 64 * 64;
   if (threads > RN_MAX_THREADS || M > 0x7FFFFFFF) return -1;
   hipLaunchKernelGGL(rmsnorm_q8_1_kernel, dim3((unsigned)M), dim3(threads), 0, s, x, w, eps, (int)K,
                      static_cast<uint8_t*>(xq));

@@ -70,16 +70,24 @@ def weight_bytes(wtype, N, K):
     return N * (K // 256) * BLOCK_BYTES[wtype]
 
 
-def weights(wtype, N, K, seed):
-    """Raw superblocks, uint8 [N][K/256 * block_bytes] (GGUF row order)."""
+def weights(wtype, N, K, seed, signed_scales=False):
+    """Raw superblocks, uint8 [N][K/256 * block_bytes] (GGUF row order).
+
+    signed_scales: give every fp16 d (and Q4_K dmin) a random sign.  The
+    workloads draw them positive; the formats store signed binary16, and the
+    parity tests cover both signs."""
     assert K % 256 == 0 and N >= 1
     rng = rng_for(*seed)
     nb = K // 256
     B = BLOCK_BYTES[wtype]
     raw = np.frombuffer(rng.bytes(N * nb * B), dtype=np.uint8).reshape(N, nb, B).copy()
     d = np.abs(rng.standard_normal((N, nb)) * 1e-3)
+    if signed_scales:
+        d = d * rng.choice([-1.0, 1.0], size=d.shape)
     if wtype == Q4_K:
         dmin = np.abs(rng.standard_normal((N, nb)) * 1e-3)
+        if signed_scales:
+            dmin = dmin * rng.choice([-1.0, 1.0], size=dmin.shape)
         raw[:, :, 0:2] = _half_bytes(d).reshape(N, nb, 2)
         raw[:, :, 2:4] = _half_bytes(dmin).reshape(N, nb, 2)
     elif wtype == Q6_K:
@@ -91,6 +99,8 @@ def weights(wtype, N, K, seed):
     elif wtype in (Q4_0, Q8_0):
         bb = B // 8
         dj = np.abs(rng.standard_normal((N, nb, 8)) * 1e-3)
+        if signed_scales:
+            dj = dj * rng.choice([-1.0, 1.0], size=dj.shape)
         blk = raw.reshape(N, nb, 8, bb)
         blk[:, :, :, 0:2] = _half_bytes(dj).reshape(N, nb, 8, 2)
     else:

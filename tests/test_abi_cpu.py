@@ -256,3 +256,15 @@ WS = 1 << 20
 def test_attn_validation(lib, args, status):
     q, Hq, K, V, Hkv, T, D, scale, out, ws, wsb = args
     assert lib.qdot_attn_decode_kv4(q, Hq, K, V, Hkv, T, D, ctypes.c_float(scale), out, ws, wsb, None) == status
+
+
+@pytest.mark.parametrize("src,nbytes,sink,status", [
+    (0, 4096, FAKE, qd.QDOT_E_ARG),            # null source
+    (FAKE, 4096, 0, qd.QDOT_E_ARG),            # null sink
+    (FAKE, 0, FAKE, qd.QDOT_E_ARG),            # nothing to read
+    (FAKE, 4100, FAKE, qd.QDOT_E_ARG),         # not a multiple of 16 bytes
+    (FAKE + 8, 4096, FAKE, qd.QDOT_E_ALIGN),   # source not 16-byte aligned
+    (FAKE, 4096, FAKE + 2, qd.QDOT_E_ALIGN),   # sink misaligned
+])
+def test_stream_read_validation(lib, src, nbytes, sink, status):
+    assert lib.qdot_stream_read(src, nbytes, sink, None) == status

@@ -49,7 +49,20 @@ def test_c0_workload_is_cold():
                                              ("attn_kv4_partial_kernel+attn_kv4_combine_kernel",
                                               "qwen3-8b-attn-kv4-32k")])
 def test_recorded_traffic_matches_the_sources(kernel, workload):
-    """The committed HBM-traffic summary of each measured kernel was taken on
-    the current sources (its digest matches), so the bench line reports it."""
+    """Each measured kernel has a committed HBM-traffic summary, and the bench
+    line reports its figure only while the summary's source digest matches
+    the current kernel sources (null once a kernel has changed since the
+    counters were taken)."""
+    import glob
+    found = None
+    for path in glob.glob(os.path.join(bench.ROOT, "profiles", "hbm_traffic_*.md")):
+        text = open(path).read()
+        if f"kernel: {kernel}\n" in text and f"workload: {workload}\n" in text:
+            found = text
+    assert found is not None, (kernel, workload)
+    kv = dict(line.split(": ", 1) for line in found.splitlines()
+              if ": " in line and not line.startswith(("|", "#", " ")))
+    assert int(kv["traffic_bytes_per_launch"]) > 0
+    current = bench.kernel_source_digest(kv["source_files"].split()) == kv["source_digest"]
     t = bench.recorded_traffic(kernel, workload)
-    assert isinstance(t, int) and t > 0
+    assert (t == int(kv["traffic_bytes_per_launch"])) if current else (t is None)

@@ -31,8 +31,11 @@ def run_multi(Wds, types, Ns, K, xqd, M):
     return [y.cpu().numpy() for y in ys]
 
 
-def check_group(mats, K, M, seed, n_oracle_rows=6):
-    Ws = [synth.weights(t, N, K, (2026, 80, seed, i)) for i, (N, t) in enumerate(mats)]
+def check_group(mats, K, M, seed, n_oracle_rows=6, signed_scales=False):
+    """n_oracle_rows: sampled rows of each matrix checked against the oracle
+    (None: every row)."""
+    Ws = [synth.weights(t, N, K, (2026, 80, seed, i), signed_scales=signed_scales)
+          for i, (N, t) in enumerate(mats)]
     Wds = [to_dev(W) for W in Ws]
     x = synth.activations(M, K, (2026, 80, seed, K, M))
     xqd, xq = quantize(x)
@@ -43,6 +46,10 @@ def check_group(mats, K, M, seed, n_oracle_rows=6):
         y1, _ = qmatmul(Wds[i], t, N, K, xqd, M)
         assert np.array_equal(ys[i].view(np.uint32), y1.view(np.uint32)), \
             f"matrix {i} ({synth.TYPE_NAMES[t]} {N}x{K}) M={M}: group != single call"
+        if n_oracle_rows is None:
+            y64, _, _ = oracle.qmatmul(Ws[i], t, N, K, xq, M)
+            assert_close(ys[i], y64, f"group matrix {i} M={M}")
+            continue
         rows = np.unique(np.concatenate([np.random.default_rng(seed + i).integers(0, N, n_oracle_rows),
                                          [0, N - 1]]))
         y64, _ = oracle.qmatmul_rows(Ws[i], t, N, K, xq, M, rows)
@@ -63,15 +70,43 @@ def test_group_q4k_q6k_long_rows(M):
     check_group([(96, synth.Q4_K), (40, synth.Q6_K), (33, synth.Q4_K)], 12288, M, seed=100 + M)
 
 
-@pytest.mark.parametrize("M", [1, 8])
+QKV_8B = [(4096, synth.Q4_K), (1024, synth.Q4_K), (1024, synth.Q6_K)]
+GATE_UP_8B = [(12288, synth.Q4_K), (12288, synth.Q4_K)]
+
+
+def headline_tiles(mats, K, M):
+    return [qd.qdot_multi_kernel_name([t for _, t in mats], [N for N, _ in mats], K, M, i)
+            for i in range(len(mats))]
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_gate_up_full_size(M):
-    """Gate and up of the 8B FFN (two 12288 x 4096 Q4_K) in one launch."""
-    check_group([(12288, synth.Q4_K), (12288, synth.Q4_K)], 4096, M, seed=10 + M, n_oracle_rows=8)
+    """Gate and up of the 8B FFN (two 12288 x 4096 Q4_K) in one launch, as
+    the benchmark step runs them at every M: the dot4 tile at M = 1, 2 and
+    the MFMA tile from M = 3 (asserted through the tile names), every output
+    against the oracle."""
+    tiles = headline_tiles(GATE_UP_8B, 4096, M)
+    kind = "qmv_dot4" if M <= 2 else "qmv_mfma"
+    assert tiles == [f"{kind}<Q4_K,{M}>"] * 2, tiles
+    check_group(GATE_UP_8B, 4096, M, seed=10 + M, n_oracle_rows=None)
 
 
-@pytest.mark.parametrize("M", [1, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_qkv_full_size(M):
-    check_group([(4096, synth.Q4_K), (1024, synth.Q4_K), (1024, synth.Q6_K)], 4096, M, seed=20 + M)
+    """q, k (Q4_K, MFMA tiles at every M) and v (Q6_K, dot4 tile) of the 8B
+    attention in one launch, as the benchmark step runs them; every output
+    against the oracle."""
+    tiles = headline_tiles(QKV_8B, 4096, M)
+    assert tiles == [f"qmv_mfma<Q4_K,{M}>"] * 2 + [f"qmv_dot4<Q6_K,{M}>"], tiles
+    check_group(QKV_8B, 4096, M, seed=20 + M, n_oracle_rows=None)
+
+
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_headline_groups_signed_scales(M):
+    """The same two groups with weights whose fp16 d and dmin carry random
+    signs (the workloads draw them positive)."""
+    check_group(QKV_8B, 4096, M, seed=90 + M, n_oracle_rows=None, signed_scales=True)
+    check_group(GATE_UP_8B, 4096, M, seed=95 + M, n_oracle_rows=64, signed_scales=True)
 
 
 @pytest.mark.parametrize("M", [1, 4, 8])

@@ -370,8 +370,9 @@ PREFILL = [(name, N, K, t) for (name, N, K, t) in synth.QWEN3_8B]
 @pytest.mark.parametrize("name,N,K,wtype", PREFILL)
 def test_prefill_full_size_sampled(name, N, K, wtype):
     """M=512 at the 8B projection shapes, in the launch the benchmark times;
-    sampled weight rows against the oracle, and rows of a smaller M > 8 call
-    bitwise equal to the same rows of the M=512 call."""
+    256 seeded weight rows (plus the first and last) against the oracle, and
+    rows of a smaller M > 8 call bitwise equal to the same rows of the M=512
+    call."""
     M = 512
     W = synth.weights(wtype, N, K, (2026, 71, N, K))
     Wd = to_dev(W)
@@ -379,7 +380,8 @@ def test_prefill_full_size_sampled(name, N, K, wtype):
     xqd, xq = quantize(x)
     y, _ = qmatmul(Wd, wtype, N, K, xqd, M)
     rng = np.random.default_rng(N + K + 1)
-    rows = np.unique(np.concatenate([rng.integers(0, N, 24), [0, N - 1]]))
+    rows = np.unique(np.concatenate([rng.choice(N, 256, replace=False), [0, N - 1]]))
+    assert rows.size >= 256
     y64, _ = oracle.qmatmul_rows(W, wtype, N, K, xq, M, rows)
     assert_close(y[:, rows], y64, f"{name} {N}x{K} M=512")
     Ms = 300  # above every matrix's mid-batch range, so the same kernel
@@ -395,19 +397,46 @@ FULL = [(name, N, K, t) for (name, N, K, t) in synth.QWEN3_8B] + \
 
 
 @pytest.mark.parametrize("name,N,K,wtype", FULL)
-def test_full_size_sampled(name, N, K, wtype):
+def test_full_size_all_rows(name, N, K, wtype):
+    """M = 8 at the full projection shapes (the Qwen3-8B and hidden-5120
+    matrices, Qwen2.5-1.5B's down, the single 1536 x 1536 matrix, the Q4_0 /
+    Q8_0 variants): every output against the oracle; rows of M = 1 bitwise
+    equal to those of M = 8."""
     M = 8
     W = synth.weights(wtype, N, K, (2026, 60, N, K))
     Wd = to_dev(W)
     x = synth.activations(M, K, (2026, 60, K, M, 7))
     xqd, xq = quantize(x)
     y, _ = qmatmul(Wd, wtype, N, K, xqd, M)
-    rng = np.random.default_rng(N + K)
-    rows = np.unique(np.concatenate([rng.integers(0, N, 48), [0, N - 1]]))
-    y64, _ = oracle.qmatmul_rows(W, wtype, N, K, xq, M, rows)
-    assert_close(y[:, rows], y64, f"{name} {N}x{K}")
+    y64, _, _ = oracle.qmatmul(W, wtype, N, K, xq, M)
+    assert_close(y, y64, f"{name} {N}x{K}")
     y1, _ = qmatmul(Wd, wtype, N, K, xqd, 1)
     assert np.array_equal(y1.view(np.uint32), y[:1].view(np.uint32)), "batch invariance"
+
+
+# ------------------------------------- negative fp16 scales, every kernel
+@pytest.mark.parametrize("wtype", TYPES)
+def test_signed_scales_every_kernel(wtype):
+    """Weights whose fp16 d (and Q4_K dmin) carry random signs, through the
+    decode tiles (M = 1..8; for Q4_K and IQ4_XS the 16-row tile at M = 12),
+    the mid-batch kernel (M = 40) and the prefill kernel (M = 300): sub-block
+    sums exact through the dump, every output within 1e-5 rel."""
+    N, K = 133, 2560
+    W = synth.weights(wtype, N, K, (2026, 78, wtype), signed_scales=True)
+    d = W.reshape(N, K // 256, -1)
+    d16 = d[:, :, 0:2].copy().view(np.float16)[..., 0] if wtype not in (synth.Q6_K,) else \
+        d[:, :, 208:210].copy().view(np.float16)[..., 0]
+    assert (d16 < 0).any() and (d16 > 0).any()
+    Wd = to_dev(W)
+    x = synth.activations(300, K, (2026, 78, K, 300, 7))
+    xqd, xq = quantize(x)
+    for M in (1, 2, 3, 5, 8, 12, 40, 300):
+        xm, xmh = xqd[: qd.qdot_q8_1_bytes(M, K)], xq[: qd.qdot_q8_1_bytes(M, K)]
+        y, isums = qmatmul(Wd, wtype, N, K, xm, M, dump=M in (1, 8, 12, 40, 300))
+        y64, _, _ = oracle.qmatmul(W, wtype, N, K, xmh, M)
+        assert_close(y, y64, f"{TN[wtype]} signed scales M={M}")
+        if isums is not None:
+            assert np.array_equal(isums, oracle.isums(W, wtype, N, K, xmh, M)), f"M={M}: isums differ"
 
 
 # ------------------------------------------------- the pages' noise anchor

@@ -1,6 +1,8 @@
 """GPU: the fused RMSNorm + Q8_1 producer (qdot_rmsnorm_quantize_q8_1)
-against the oracle, byte for byte.  Both sides run the same fp32 operations
-in the same order, so every quantized code, D and S must agree exactly."""
+against the oracle, byte for byte.  The oracle is the Kestrel_VLLM #18
+(section 3.6) serial CPU order: 8-element group sums added left to right in
+one fp32 accumulator.  The kernel forms the group sums in parallel and adds
+them in that order, so every quantized code, D and S must agree exactly."""
 import numpy as np
 import pytest
 
@@ -56,6 +58,7 @@ def test_eps_and_edge_rows(eps):
     x[1] = 0.0                      # zero row: all-zero blocks (eps > 0) or 0/0 -> NaN codes skipped
     x[2, :] = 1.0
     x[2, 0] = 2.0 ** 12             # a sum whose fp32 value depends on the order
+    x[2, 1:8] = 0.0                 # group 0 = 2^24, then groups of 8: serial 2^24 + ...
     x[3] *= 1e-20                   # tiny values
     x[4, 100:132] = 0.0             # one all-zero block inside a row
     x[5] = np.float32(3.0)          # constant row
@@ -78,3 +81,20 @@ def test_equals_quantizer_of_oracle_norm():
     qd.qdot_quantize_q8_1(to_dev(xn), M, K, xq)
     torch.cuda.synchronize()
     assert np.array_equal(run(x, w, 1e-6), xq.cpu().numpy())
+
+
+def test_serial_group_order_row():
+    """The row worked out by hand in the oracle's pins (Kestrel #18 section
+    3.6 order: ss = 2^24 + 8, where the pairwise block tree gives 2^24 + 14),
+    repeated along a long row and mixed with ordinary rows, so that the
+    kernel's serial pass over the group sums is what decides the bytes."""
+    K = 4096
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((3, K)).astype(np.float32)
+    x[1] = 0.0
+    x[1, 0:8] = [2.0 ** 12, 1, 1, 1, 1, 1, 1, 1]
+    x[1, 8::8] = 1.0
+    w = rng.uniform(0.5, 1.5, K).astype(np.float32)
+    _, ss = oracle.rmsnorm(x, w, 0.0)
+    assert ss[1] == np.float32(2.0 ** 24 + 8)   # every further + 1 is a tie that rounds back
+    check(x, w, 0.0, "serial order row")
