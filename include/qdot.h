@@ -44,8 +44,10 @@
  * Ownership and threading.  The caller owns and allocates every buffer;
  * device pointers must be device memory of the current HIP device.  The
  * library never allocates, frees or synchronizes, keeps no mutable global
- * state, and enqueues its kernels on the caller's stream (0 = the null
- * stream).  Calls are asynchronous and thread-safe.
+ * state (one exception: qdot_attn_decode_kv4_noalloc's static device
+ * workspace and the per-device address it caches), and enqueues its kernels
+ * on the caller's stream (0 = the null stream).  Calls are asynchronous and
+ * thread-safe (qdot_attn_decode_kv4_noalloc: see its limits).
  *
  * Errors.  Arguments are validated before any HIP call; on failure nothing is
  * launched and a negative status is returned:
@@ -211,6 +213,27 @@ int qdot_attn_decode_kv4(const void *q_q8, int64_t Hq, const void *Kc,
                          const void *Vc, int64_t Hkv, int64_t T, int64_t D,
                          float scale, float *out, void *workspace,
                          size_t workspace_bytes, void *stream);
+
+/* qdot_attn_decode_kv4 for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and the same result, bit for bit, with the
+ * workspace held in a static device array of QDOT_ATTN_NOALLOC_BYTES bytes
+ * inside the library (each GPU the library runs on holds one copy until the
+ * process ends; its address is looked up once per device, on the first call
+ * with that device current).  The call allocates and frees nothing.  Limit:
+ * qdot_attn_kv4_workspace_bytes(Hq, T) <= QDOT_ATTN_NOALLOC_BYTES (e.g.
+ * Hq = 32 up to T = 258,048 tokens), else QDOT_E_ARG.  Every call on one GPU
+ * shares that GPU's array, which keeps the last call's contents (nothing in
+ * it has to start at zero): calls that overlap on one GPU (concurrent
+ * streams, or host threads issuing calls that can run at the same time)
+ * race and give wrong results; serialize them.  Other arguments, alignment
+ * and errors as qdot_attn_decode_kv4; QDOT_E_HIP also if the array's device
+ * address cannot be obtained. */
+#define QDOT_ATTN_NOALLOC_BYTES (16 << 20)
+int qdot_attn_decode_kv4_noalloc(const void *q_q8, int64_t Hq, const void *Kc,
+                                 const void *Vc, int64_t Hkv, int64_t T,
+                                 int64_t D, float scale, float *out,
+                                 void *stream);
 
 /* Bytes of one K or V row of D elements in qdot_attn_decode_kv4's cache
  * (D/32 blocks of 18 bytes); 0 unless D is a multiple of 32 in

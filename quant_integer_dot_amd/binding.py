@@ -11,6 +11,7 @@ import os
 
 QDOT_Q4_K, QDOT_Q6_K, QDOT_IQ4_XS, QDOT_Q4_0, QDOT_Q8_0 = 1, 2, 3, 4, 5
 QDOT_OK, QDOT_E_ARG, QDOT_E_ALIGN, QDOT_E_HIP = 0, -1, -2, -3
+QDOT_ATTN_NOALLOC_BYTES = 16 << 20   # include/qdot.h
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libqdot.so"
@@ -60,6 +61,8 @@ def load():
     L.qdot_rmsnorm_quantize_q8_1.restype = i32
     L.qdot_attn_decode_kv4.argtypes = [P, i64, P, P, i64, i64, i64, ctypes.c_float, P, P, ctypes.c_size_t, P]
     L.qdot_attn_decode_kv4.restype = i32
+    L.qdot_attn_decode_kv4_noalloc.argtypes = [P, i64, P, P, i64, i64, i64, ctypes.c_float, P, P]
+    L.qdot_attn_decode_kv4_noalloc.restype = i32
     L.qdot_attn_kv4_row_bytes.argtypes = [i64]
     L.qdot_attn_kv4_row_bytes.restype = ctypes.c_size_t
     L.qdot_attn_kv4_workspace_bytes.argtypes = [i64, i64]
@@ -173,6 +176,14 @@ def qdot_attn_decode_kv4(q_q8, Hq, Kc, Vc, Hkv, T, D, scale, out, workspace, wor
     _check(load().qdot_attn_decode_kv4(_addr(q_q8), Hq, _addr(Kc), _addr(Vc), Hkv, T, D, float(scale),
                                         _addr(out), _addr(workspace), int(workspace_bytes), st),
            "qdot_attn_decode_kv4")
+
+
+def qdot_attn_decode_kv4_noalloc(q_q8, Hq, Kc, Vc, Hkv, T, D, scale, out, stream=None):
+    """qdot_attn_decode_kv4 with the library's static workspace (no allocation)."""
+    st = _stream(stream, out)
+    _check(load().qdot_attn_decode_kv4_noalloc(_addr(q_q8), Hq, _addr(Kc), _addr(Vc), Hkv, T, D,
+                                                float(scale), _addr(out), st),
+           "qdot_attn_decode_kv4_noalloc")
 
 
 def qdot_status_str(status):

@@ -268,3 +268,19 @@ def test_attn_validation(lib, args, status):
 ])
 def test_stream_read_validation(lib, src, nbytes, sink, status):
     assert lib.qdot_stream_read(src, nbytes, sink, None) == status
+
+
+def test_attn_noalloc_validation(lib):
+    """The no-allocation attention call rejects a context whose workspace
+    would not fit the static array, and bad arguments, before any HIP call."""
+    D = 128
+    per_chunk = 4 * (D + 2) * 4                       # Hq = 4
+    T_ok = qd.QDOT_ATTN_NOALLOC_BYTES // per_chunk * 256
+    assert qd.qdot_attn_kv4_workspace_bytes(4, T_ok) <= qd.QDOT_ATTN_NOALLOC_BYTES
+    f = lib.qdot_attn_decode_kv4_noalloc
+    assert f(FAKE, 4, FAKE, FAKE, 1, T_ok + 256, D, ctypes.c_float(0.1), FAKE, None) == qd.QDOT_E_ARG
+    assert f(0, 4, FAKE, FAKE, 1, 100, D, ctypes.c_float(0.1), FAKE, None) == qd.QDOT_E_ARG
+    assert f(FAKE, 4, FAKE, FAKE, 1, 100, 64, ctypes.c_float(0.1), FAKE, None) == qd.QDOT_E_ARG
+    assert f(FAKE, 4, FAKE, FAKE, 3, 100, D, ctypes.c_float(0.1), FAKE, None) == qd.QDOT_E_ARG
+    assert f(FAKE, 4, FAKE + 4, FAKE, 1, 100, D, ctypes.c_float(0.1), FAKE, None) == qd.QDOT_E_ALIGN
+    assert f(FAKE, 4, FAKE, FAKE, 1, 100, D, ctypes.c_float(float("nan")), FAKE, None) == qd.QDOT_E_ARG
