@@ -31,7 +31,7 @@
 #pragma once
 #include <type_traits>
 
-#include "qdot_common.hpp"
+#include "formats.hpp"
 
 namespace qdot {
 
@@ -48,24 +48,6 @@ struct QmmDs { double d, s; };  // one Q8_1 block's scales, fp64 (Q6_K uses d on
 // Result register r of lane l -> row of the 32 x 32 tile.
 __device__ __forceinline__ int mfma_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
-// IQ4_NL-style codebook as four little-endian dwords, placeholder values
-// round_half_away(-127 + 240*(i/15)^1.4) (the pages do not print the table).
-constexpr uint32_t QMM_CB0 = 0x9A8F8681u, QMM_CB1 = 0xD4C4B5A7u, QMM_CB2 = 0x1C09F6E5u,
-                   QMM_CB3 = 0x715B4531u;
-__device__ __forceinline__ uint32_t qmm_cb(uint32_t idx) {
-  const uint32_t sel = idx & 0x07070707u;
-  const uint32_t lo = perm(QMM_CB1, QMM_CB0, sel);
-  const uint32_t hi = perm(QMM_CB3, QMM_CB2, sel);
-  return perm(hi, lo, ((idx >> 1) & 0x04040404u) | 0x03020100u);
-}
-
-// Q6_K: 6-bit codes (one per byte, 0..63) -> int8 code - 32.
-__device__ __forceinline__ uint32_t q6_signed(uint32_t u) {
-  const uint32_t v = u ^ 0x20202020u;        // bit 5 flipped: 6-bit two's complement
-  const uint32_t t = v & 0x20202020u;        // its sign bit, per byte
-  return v | (t << 1) | (t << 2);            // sign-extended to 8 bits
-}
-
 // -------------------------------------------------------------- per format
 // Per weight row and superblock: the scale fields.  Per weight row and
 // 32-element block: the B operand data of this lane's K-slice g.
@@ -79,16 +61,7 @@ template <> struct QmmFmt<Q4_K> {
   __device__ static Blk blk(const uint8_t* sb, int j, int g) { return Blk{ld16(sb + 16 + 32 * (j >> 1) + 16 * g)}; }
   // 6-bit scale and min of sub-block j (plain GGUF packing), as fp64 d*sc and -dmin*m.
   template <int J> __device__ static void scales(const Hdr& x, double& w, double& mn) {
-    uint32_t sc, m;
-    if (J < 4) {
-      sc = (x.h.y >> (8 * J)) & 63u;
-      m = (x.h.z >> (8 * J)) & 63u;
-    } else {
-      sc = ((x.h.w >> (8 * (J - 4))) & 15u) | (((x.h.y >> (8 * (J - 4) + 6)) & 3u) << 4);
-      m = ((x.h.w >> (8 * (J - 4) + 4)) & 15u) | (((x.h.z >> (8 * (J - 4) + 6)) & 3u) << 4);
-    }
-    w = (double)(h2f(x.h.x) * (float)sc);
-    mn = -(double)(h2f(x.h.x >> 16) * (float)m);
+    q4k_scales(x.h, J, w, mn);
   }
   template <int J> __device__ static v4i codes(const Blk& b, int /*g*/) {
     const u32x4 v = b.qs;
@@ -105,14 +78,13 @@ template <> struct QmmFmt<IQ4_XS> {
   __device__ static Hdr hdr(const uint8_t* sb) { return Hdr{ld8(sb)}; }
   __device__ static Blk blk(const uint8_t* sb, int j, int /*g*/) { return Blk{ld16(sb + 8 + 16 * j)}; }
   template <int J> __device__ static double scale(const Hdr& x, const Blk&) {
-    const int ls = (int)(((x.h.y >> (4 * J)) & 15u) | ((((x.h.x >> 16) >> (2 * J)) & 3u) << 4));
-    return (double)(h2f(x.h.x) * (float)(ls - 32));
+    return iq4xs_scale(x.h.x, x.h.y, J);
   }
   template <int J> __device__ static v4i codes(const Blk& b, int g) {
     const u32x4 v = b.qs;
     const int s = g ? 4 : 0;
-    return v4i{(int)qmm_cb(v.x >> s), (int)qmm_cb(v.y >> s), (int)qmm_cb(v.z >> s),
-               (int)qmm_cb(v.w >> s)};
+    return v4i{(int)iq4nl_lookup(v.x >> s), (int)iq4nl_lookup(v.y >> s), (int)iq4nl_lookup(v.z >> s),
+               (int)iq4nl_lookup(v.w >> s)};
   }
 };
 
@@ -132,9 +104,7 @@ template <> struct QmmFmt<Q4_0> {
   // nibble q (0..15) -> int8 q - 8, four bytes at once without borrows
   template <int J> __device__ static v4i codes(const Blk& b, int g) {
     const int s = g ? 4 : 0;
-    auto c = [&](uint32_t v) {
-      return (int)((((v >> s) & 0x0F0F0F0Fu) | 0x80808080u) - 0x08080808u) ^ (int)0x80808080u;
-    };
+    auto c = [&](uint32_t v) { return (int)q40_signed((v >> s) & 0x0F0F0F0Fu); };
     return v4i{c(b.qs.x), c(b.qs.y), c(b.qs.z), c(b.qs.w)};
   }
 };
@@ -188,9 +158,7 @@ template <> struct QmmFmt<Q6_K> {
     uint32_t c[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const uint32_t low = ((g6 >= 2 ? (lq[k] >> 4) : lq[k]) & 0x0F0F0F0Fu);
-      const uint32_t high = ((hq[k] >> (2 * g6)) & 0x03030303u) << 4;
-      c[k] = q6_signed(low | high);
+      c[k] = q6k_signed(q6k_code<(g6 >= 2)>(lq[k], hq[k], g6 & 1));
     }
     return (long)((uint64_t)c[0] | ((uint64_t)c[1] << 32));
   }

@@ -22,7 +22,7 @@
 // from four.  Both scale tables are fp64 and rebuilt per superblock.
 #include <type_traits>
 
-#include "qdot_common.hpp"
+#include "formats.hpp"
 
 namespace qdot {
 
@@ -43,26 +43,6 @@ struct __attribute__((aligned(16))) SkW {
 };
 struct __attribute__((aligned(16))) SkA { double d, s; };  // activation D, S
 
-// IQ4_NL-style codebook, placeholder values (the pages do not print the
-// table): round_half_away(-127 + 240*(i/15)^1.4), as four dwords.
-constexpr uint32_t SK_CB0 = 0x9A8F8681u, SK_CB1 = 0xD4C4B5A7u, SK_CB2 = 0x1C09F6E5u,
-                   SK_CB3 = 0x715B4531u;
-__device__ __forceinline__ uint32_t sk_cb(uint32_t idx) {
-  const uint32_t sel = idx & 0x07070707u;
-  const uint32_t lo = perm(SK_CB1, SK_CB0, sel);
-  const uint32_t hi = perm(SK_CB3, SK_CB2, sel);
-  return perm(hi, lo, ((idx >> 1) & 0x04040404u) | 0x03020100u);
-}
-// 6-bit two's complement per byte (value - 32 of a 0..63 code) -> int8
-__device__ __forceinline__ uint32_t sk_q6(uint32_t u) {
-  const uint32_t v = u ^ 0x20202020u;
-  const uint32_t t = v & 0x20202020u;
-  return v | (t << 1) | (t << 2);
-}
-// nibble 0..15 -> int8 value - 8, four bytes without borrows
-__device__ __forceinline__ uint32_t sk_q40(uint32_t v) {
-  return ((v | 0x80808080u) - 0x08080808u) ^ 0x80808080u;
-}
 __device__ __forceinline__ long sk_pack(uint32_t lo, uint32_t hi) {
   return (long)((uint64_t)lo | ((uint64_t)hi << 32));
 }
@@ -95,15 +75,8 @@ template <> struct Sk<Q4_K> {
     return sk_pack((v.x >> sh) & 0x0F0F0F0Fu, (v.y >> sh) & 0x0F0F0F0Fu);
   }
   __device__ static SkW entry(const Raw& r, int j) {
-    const u32x4 h = r.h;
-    const int k = j & 3;
-    const uint32_t bsc = j < 4 ? ((h.y >> (8 * k)) & 63u)
-                               : (((h.w >> (8 * k)) & 15u) | (((h.y >> (8 * k + 6)) & 3u) << 4));
-    const uint32_t bmn = j < 4 ? ((h.z >> (8 * k)) & 63u)
-                               : (((h.w >> (8 * k + 4)) & 15u) | (((h.z >> (8 * k + 6)) & 3u) << 4));
     SkW e;
-    e.w = (double)(h2f(h.x) * (float)bsc);          // d*sc, exact in fp32
-    e.mn = -(double)(h2f(h.x >> 16) * (float)bmn);  // -dmin*m, exact in fp32
+    q4k_scales(r.h, j, e.w, e.mn);  // d*sc, -dmin*m
     return e;
   }
 };
@@ -119,12 +92,11 @@ template <> struct Sk<IQ4_XS> {
   }
   template <int J> __device__ static long codes(const Raw& r, int s) {
     const int sh = (s >> 1) ? 4 : 0;
-    return sk_pack(sk_cb(r.q[J].x >> sh), sk_cb(r.q[J].y >> sh));
+    return sk_pack(iq4nl_lookup(r.q[J].x >> sh), iq4nl_lookup(r.q[J].y >> sh));
   }
   __device__ static SkW entry(const Raw& r, int j) {
-    const int ls = (int)(((r.h.y >> (4 * j)) & 15u) | ((((r.h.x >> 16) >> (2 * j)) & 3u) << 4));
     SkW e;
-    e.w = (double)(h2f(r.h.x) * (float)(ls - 32));
+    e.w = iq4xs_scale(r.h.x, r.h.y, j);
     e.mn = 0.0;
     return e;
   }
@@ -142,7 +114,7 @@ template <> struct Sk<Q4_0> {
   }
   template <int J> __device__ static long codes(const Raw& r, int s) {
     const int sh = (s >> 1) ? 4 : 0;
-    return sk_pack(sk_q40((r.q[J].x >> sh) & 0x0F0F0F0Fu), sk_q40((r.q[J].y >> sh) & 0x0F0F0F0Fu));
+    return sk_pack(q40_signed((r.q[J].x >> sh) & 0x0F0F0F0Fu), q40_signed((r.q[J].y >> sh) & 0x0F0F0F0Fu));
   }
   __device__ static SkW entry(const Raw& r, int j) {
     SkW e;
@@ -195,10 +167,8 @@ template <> struct Sk<Q6_K> {
     constexpr int h = J >> 2, g = J & 3;
     const u32x2 l = r.l[2 * h + (g & 1)];
     const u32x2 q = r.q[h];
-    constexpr int sh = g >= 2 ? 4 : 0;
-    const uint32_t c0 = ((l.x >> sh) & 0x0F0F0F0Fu) | (((q.x >> (2 * g)) & 0x03030303u) << 4);
-    const uint32_t c1 = ((l.y >> sh) & 0x0F0F0F0Fu) | (((q.y >> (2 * g)) & 0x03030303u) << 4);
-    return sk_pack(sk_q6(c0), sk_q6(c1));
+    return sk_pack(q6k_signed(q6k_code<(g >= 2)>(l.x, q.x, g & 1)),
+                   q6k_signed(q6k_code<(g >= 2)>(l.y, q.y, g & 1)));
   }
   __device__ static SkW entry(const Raw& r, int j) {
     const uint32_t sc = r.sc >> (16 * (j & 1));

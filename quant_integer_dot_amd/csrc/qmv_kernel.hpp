@@ -26,7 +26,7 @@
 
 #pragma once
 
-#include "qdot_common.hpp"
+#include "formats.hpp"
 
 namespace qdot {
 
@@ -129,27 +129,6 @@ template <> struct Fmt<Q8_0> {
   __device__ static int blk(int q, int half) { return 2 * q + half; }
 };
 
-// IQ4_NL-style codebook as four little-endian dwords (entries 0-3, 4-7, 8-11,
-// 12-15).  Placeholder values (the pages name kvalues_iq4nl without printing
-// it): round_half_away(-127 + 240*(i/15)^1.4).
-//   -127 -122 -113 -102 | -89 -75 -60 -44 | -27 -10 9 28 | 49 69 91 113
-constexpr uint32_t CB0 = 0x9A8F8681u;  // 0x81=-127 0x86=-122 0x8F=-113 0x9A=-102
-constexpr uint32_t CB1 = 0xD4C4B5A7u;  // 0xA7=-89 0xB5=-75 0xC4=-60 0xD4=-44
-constexpr uint32_t CB2 = 0x1C09F6E5u;  // 0xE5=-27 0xF6=-10 0x09=9 0x1C=28
-constexpr uint32_t CB3 = 0x715B4531u;  // 0x31=49 0x45=69 0x5B=91 0x71=113
-
-// Four 4-bit indices (one per byte, values 0..15) -> four int8 codebook
-// values: two v_perm lookups on entries 0-7 and 8-15, then a v_perm that
-// picks, per byte, the first or the second result by bit 3 of the index.
-__device__ __forceinline__ uint32_t cb_lookup(uint32_t idx, uint32_t t0, uint32_t t1,
-                                              uint32_t t2, uint32_t t3) {
-  const uint32_t sel = idx & 0x07070707u;
-  const uint32_t lo = perm(t1, t0, sel);
-  const uint32_t hi = perm(t3, t2, sel);
-  const uint32_t pick = ((idx >> 1) & 0x04040404u) | 0x03020100u;
-  return perm(hi, lo, pick);
-}
-
 // ---------------------------------------------------------------- kernels
 //
 // One lane handles quarter q of superblock b for one weight row (slot s, row
@@ -171,31 +150,18 @@ template <int T>
 __device__ __forceinline__ void decode_sub(const typename Fmt<T>::Regs& g, int q, int half,
                                            Sub<T>& o) {
   if constexpr (T == Q4_K) {
-    // sub-block j = 2q + half: 6-bit scale and min (plain GGUF packing); q < 2
-    // reads scales[j], scales[j+4]; q >= 2 splices the nibbles of scales[j+4]
-    // with the top two bits of scales[j-4] (scale) and scales[j] (min).
-    const int sh = 8 * (((2 * q) & 3) + half);
-    const bool lo = q < 2;
-    const uint32_t Ys = g.h.y >> sh, Zs = g.h.z >> sh, Ws = g.h.w >> sh;
-    const uint32_t sc = lo ? (Ys & 63u) : ((Ws & 15u) | ((Ys >> 2) & 0x30u));
-    const uint32_t mn = lo ? (Zs & 63u) : (((Ws >> 4) & 15u) | ((Zs >> 2) & 0x30u));
-    o.wsc = (double)(h2f(g.h.x) * (float)sc);          // d*sc, exact in fp32
-    o.wmn = -(double)(h2f(g.h.x >> 16) * (float)mn);   // -dmin*m, exact in fp32
+    q4k_scales(g.h, 2 * q + half, o.wsc, o.wmn);       // sub-block 2q + half
     const uint32_t pk[8] = {g.a.x, g.a.y, g.a.z, g.a.w, g.b.x, g.b.y, g.b.z, g.b.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) o.cw[i] = (half ? (pk[i] >> 4) : pk[i]) & 0x0F0F0F0Fu;
   } else if constexpr (T == IQ4_XS) {
-    const int j = 2 * q + half;
-    const uint32_t sl = (g.h.y >> (4 * j)) & 15u;
-    const uint32_t shb = ((g.h.x >> 16) >> (2 * j)) & 3u;
-    const int ls = (int)(sl | (shb << 4));
-    o.wsc = (double)(h2f(g.h.x) * (float)(ls - 32));  // d*(ls-32), exact in fp32
+    o.wsc = iq4xs_scale(g.h.x, g.h.y, 2 * q + half);
     const u32x4 pq = half ? g.b : g.a;
     const uint32_t pk[4] = {pq.x, pq.y, pq.z, pq.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      o.cw[i] = cb_lookup(pk[i], CB0, CB1, CB2, CB3);           // elements 4i..4i+3
-      o.cw[i + 4] = cb_lookup(pk[i] >> 4, CB0, CB1, CB2, CB3);  // elements 16+4i..
+      o.cw[i] = iq4nl_lookup(pk[i]);           // elements 4i..4i+3
+      o.cw[i + 4] = iq4nl_lookup(pk[i] >> 4);  // elements 16+4i..
     }
   } else if constexpr (T == Q4_0) {
     // block 2q (bytes 0-17) or 2q+1 (bytes 18-35); raw nibbles 0..15, the -8
@@ -236,12 +202,7 @@ __device__ __forceinline__ void decode_sub(const typename Fmt<T>::Regs& g, int q
     const uint32_t pl[8] = {g.a.x, g.a.y, g.a.z, g.a.w, g.b.x, g.b.y, g.b.z, g.b.w};
     const uint32_t ph[8] = {g.c.x, g.c.y, g.c.z, g.c.w, g.e.x, g.e.y, g.e.z, g.e.w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (half == 0)
-        o.cw[i] = (pl[i] & 0x0F0F0F0Fu) | ((ph[i] << (4 - 2 * gp)) & 0x30303030u);
-      else
-        o.cw[i] = ((pl[i] >> 4) & 0x0F0F0F0Fu) | ((ph[i] >> (2 * gp)) & 0x30303030u);
-    }
+    for (int i = 0; i < 8; ++i) o.cw[i] = half ? q6k_code<1>(pl[i], ph[i], gp) : q6k_code<0>(pl[i], ph[i], gp);
     // int8 sub-scales of sub-blocks t0 = 8h + 2gp + 4*half and t0 + 1
     const uint32_t scw = h ? (half ? g.sc.w : g.sc.z) : (half ? g.sc.y : g.sc.x);
     o.s0 = (int)(int8_t)(scw >> (16 * gp));
@@ -602,8 +563,8 @@ __device__ __forceinline__ void qmf_tile(const uint8_t* __restrict__ W, int N, i
           // nibbles of its 16 bytes, looked up in the codebook
           const u32x4 v = st.q[4 * g + jj];
           const int sh = 4 * s;
-          bq = qmf_v4i{(int)cb_lookup(v.x >> sh, CB0, CB1, CB2, CB3), (int)cb_lookup(v.y >> sh, CB0, CB1, CB2, CB3),
-                       (int)cb_lookup(v.z >> sh, CB0, CB1, CB2, CB3), (int)cb_lookup(v.w >> sh, CB0, CB1, CB2, CB3)};
+          bq = qmf_v4i{(int)iq4nl_lookup(v.x >> sh), (int)iq4nl_lookup(v.y >> sh),
+                       (int)iq4nl_lookup(v.z >> sh), (int)iq4nl_lookup(v.w >> sh)};
         }
         C = __builtin_amdgcn_mfma_i32_32x32x32_i8(slot == jj ? a : z4, bq, C, 0, 0, 0);
       }
@@ -612,19 +573,8 @@ __device__ __forceinline__ void qmf_tile(const uint8_t* __restrict__ W, int N, i
         const int j = 4 * g + jj;
         // scale (and Q4_K min) of sub-block j, as qmv_tile's decode_sub computes them
         double wsc, wmn = 0.0;
-        if constexpr (T == Q4_K) {
-          const int sh = 8 * jj;
-          const uint32_t Ys = st.h.y >> sh, Zs = st.h.z >> sh, Ws = st.h.w >> sh;
-          const uint32_t sc = g == 0 ? (Ys & 63u) : ((Ws & 15u) | ((Ys >> 2) & 0x30u));
-          const uint32_t mn = g == 0 ? (Zs & 63u) : (((Ws >> 4) & 15u) | ((Zs >> 2) & 0x30u));
-          wsc = (double)(h2f(st.h.x) * (float)sc);
-          wmn = -(double)(h2f(st.h.x >> 16) * (float)mn);
-        } else {
-          const uint32_t sl = (st.h.y >> (4 * j)) & 15u;
-          const uint32_t shb = ((st.h.x >> 16) >> (2 * j)) & 3u;
-          const int ls = (int)(sl | (shb << 4));
-          wsc = (double)(h2f(st.h.x) * (float)(ls - 32));  // d*(ls-32), exact in fp32
-        }
+        if constexpr (T == Q4_K) q4k_scales(st.h, j, wsc, wmn);
+        else wsc = iq4xs_scale(st.h.x, st.h.y, j);
         // rows m >= M (upper-half lanes at M = 7) drain zero dots against
         // row 0's scales and are never stored
 #pragma unroll
@@ -783,8 +733,8 @@ __device__ __forceinline__ void qmf16_tile(const uint8_t* __restrict__ W, int N,
           // nibbles of its 16 bytes, looked up in the codebook
           const u32x4 v = st.q[j];
           const int sh = 4 * s;
-          bq = qmf_v4i{(int)cb_lookup(v.x >> sh, CB0, CB1, CB2, CB3), (int)cb_lookup(v.y >> sh, CB0, CB1, CB2, CB3),
-                       (int)cb_lookup(v.z >> sh, CB0, CB1, CB2, CB3), (int)cb_lookup(v.w >> sh, CB0, CB1, CB2, CB3)};
+          bq = qmf_v4i{(int)iq4nl_lookup(v.x >> sh), (int)iq4nl_lookup(v.y >> sh),
+                       (int)iq4nl_lookup(v.z >> sh), (int)iq4nl_lookup(v.w >> sh)};
         }
         C = __builtin_amdgcn_mfma_i32_32x32x32_i8(slot == jj ? a : z4, bq, C, 0, 0, 0);
       }
@@ -793,19 +743,8 @@ __device__ __forceinline__ void qmf16_tile(const uint8_t* __restrict__ W, int N,
         const int j = S * g + jj;
         // scale (and Q4_K min) of sub-block j, as qmv_tile's decode_sub computes them
         double wsc, wmn = 0.0;
-        if constexpr (T == Q4_K) {
-          const int sh = 8 * (j & 3);
-          const uint32_t Ys = st.h.y >> sh, Zs = st.h.z >> sh, Ws = st.h.w >> sh;
-          const uint32_t sc = j < 4 ? (Ys & 63u) : ((Ws & 15u) | ((Ys >> 2) & 0x30u));
-          const uint32_t mn = j < 4 ? (Zs & 63u) : (((Ws >> 4) & 15u) | ((Zs >> 2) & 0x30u));
-          wsc = (double)(h2f(st.h.x) * (float)sc);
-          wmn = -(double)(h2f(st.h.x >> 16) * (float)mn);
-        } else {
-          const uint32_t sl = (st.h.y >> (4 * j)) & 15u;
-          const uint32_t shb = ((st.h.x >> 16) >> (2 * j)) & 3u;
-          const int ls = (int)(sl | (shb << 4));
-          wsc = (double)(h2f(st.h.x) * (float)(ls - 32));  // d*(ls-32), exact in fp32
-        }
+        if constexpr (T == Q4_K) q4k_scales(st.h, j, wsc, wmn);
+        else wsc = iq4xs_scale(st.h.x, st.h.y, j);
         // Result register r of lane l holds A row 8(r/4) + 4s + r%4, i.e.
         // slot (8(r/4))/R -- the registers of slot jj carry sub-block j --
         // and activation row m = (8(r/4)) % R + 4s + r%4.
