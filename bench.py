@@ -6,7 +6,10 @@ K/V 1024x4096, O 4096x4096, gate/up 12288x4096, down 4096x12288; V and down in
 Q6_K, the rest Q4_K), seeded synthetic weights resident in HBM.  One step is one
 pass of the whole path for M = 1, 2, 4 and 8 token rows: per layer, four
 activation quantizations (qkv input, o input, gate/up input, down input) and the
-seven qmatmuls.  Every matrix is cold in the 256 MB Infinity Cache because a
+seven qmatmuls.  At M = 1 (--fused-max-m) the quantizations run inside the
+matmul launches (qdot_quantize_qmatmul[_multi], bitwise the same results),
+which measured faster there than a separate quantize launch; above it, one
+quantize launch per input.  Every matrix is cold in the 256 MB Infinity Cache because a
 36-layer sweep streams 4.4 GB.
 
 Timing: each M's 36-layer sweep is captured once in a HIP graph; the timed
@@ -59,6 +62,9 @@ def parse():
     p.add_argument("--no-check", action="store_true", help="skip the sampled oracle check")
     p.add_argument("--kernel-reps", type=int, default=None,
                    help="replays of each per-projection graph (default: steps)")
+    p.add_argument("--fused-max-m", type=int, default=1,
+                   help="largest M whose launches quantize the activations in the matmul kernel "
+                        "(qdot_quantize_qmatmul[_multi]) instead of a separate quantize launch; 0 = never")
     p.add_argument("--separate", action="store_true",
                    help="one launch per projection (default: projections sharing an input in one "
                         "qdot_qmatmul_multi launch for M <= 8)")
@@ -95,6 +101,7 @@ def workload_def(name):
 # The HIP kernel function behind each kernel label of qdot_kernel_name (and
 # of the grouped decode launch).
 KERNEL_FUNCTION = {"qmv_dot4": "qmv_kernel", "qmv_mfma": "qmv_kernel", "qmv_multi": "qmv_multi_kernel",
+                   "qmv_dot4q": "qmv_kernel",
                    "qmm_skinny": "qmm_skinny_kernel", "qmm_mfma": "qmm_mfma_kernel",
                    "quantize_q8_1": "quantize_q8_1_kernel"}
 
@@ -630,7 +637,14 @@ def main():
                 out.extend((shapes[pi][0], [pi]) for pi in pis)
         return out
 
+    def fused(M):
+        """Whether M's launches quantize their activations themselves."""
+        return M <= args.fused_max_m and not prefill
+
     def unit_kernel(M, pis):
+        if fused(M):
+            names = [f"qmv_dot4q<{synth.TYPE_NAMES[shapes[pi][3]]},{M}>" for pi in pis]
+            return names[0] if len(pis) == 1 else "qmv_multi<" + "+".join(names) + ">"
         if len(pis) == 1:
             _, N, K, t = shapes[pis[0]]
             return qd.qdot_kernel_name_shape(t, N, K, M)
@@ -648,19 +662,22 @@ def main():
         b = bufs[M]
         s = torch.cuda.current_stream(dev).cuda_stream
         us = units(M)
+        fz = fused(M)
         for layer in range(layers):
             for inp, pis in groups:
                 K = shapes[pis[0]][2]
-                if only is None or only == "quantize":
+                if not fz and (only is None or only == "quantize"):
                     rc = lib.qdot_quantize_q8_1(b["x"][inp].data_ptr(), M, K, b["xq"][inp].data_ptr(), s)
                     assert rc == 0, rc
+                src = b["x"][inp] if fz else b["xq"][inp]
                 for label, upis in us:
                     if upis[0] not in pis or (only is not None and only != label):
                         continue
                     if len(upis) == 1:
                         name, N, K, t = shapes[upis[0]]
-                        rc = lib.qdot_qmatmul(Wdev[layer][upis[0]].data_ptr(), t, N, K, b["xq"][inp].data_ptr(),
-                                              M, b["y"][name].data_ptr(), s)
+                        fn = lib.qdot_quantize_qmatmul if fz else lib.qdot_qmatmul
+                        rc = fn(Wdev[layer][upis[0]].data_ptr(), t, N, K, src.data_ptr(), M,
+                                b["y"][name].data_ptr(), s)
                     else:
                         key = (M, layer, label)
                         if key not in multi_args:
@@ -671,7 +688,8 @@ def main():
                                 (I64_ * n)(*[shapes[pi][1] for pi in upis]),
                                 (P_ * n)(*[b["y"][shapes[pi][0]].data_ptr() for pi in upis]))
                         wa, ta, na, ya = multi_args[key]
-                        rc = lib.qdot_qmatmul_multi(len(upis), wa, ta, na, K, b["xq"][inp].data_ptr(), M, ya, s)
+                        fn = lib.qdot_quantize_qmatmul_multi if fz else lib.qdot_qmatmul_multi
+                        rc = fn(len(upis), wa, ta, na, K, src.data_ptr(), M, ya, s)
                     assert rc == 0, rc
 
     # eager run once (also fills every xq buffer)
@@ -747,7 +765,8 @@ def main():
             K = shapes[upis[0]][2]
             Ns = [shapes[pi][1] for pi in upis]
             wb = sum(qd.qdot_weight_bytes(shapes[pi][3], shapes[pi][1], K) for pi in upis)
-            alg = wb + qd.qdot_q8_1_bytes(M, K) + 4 * M * sum(Ns)
+            # activations read once (fp32 when quantized in the kernel, Q8_1 otherwise), y written once
+            alg = wb + (4 * M * K if fused(M) else qd.qdot_q8_1_bytes(M, K)) + 4 * M * sum(Ns)
             rows[label] = {"N": Ns[0] if len(Ns) == 1 else Ns, "K": K,
                            "type": "+".join(synth.TYPE_NAMES[shapes[pi][3]] for pi in upis),
                            "us": round(us, 3), "weight_GBps": round(wb / us / 1e3, 1),
@@ -759,29 +778,32 @@ def main():
             e[1] += us * layers * 1e-3
             e[2] += layers
             e[3] += 2 * M * sum(Ns) * K * layers
-        # quantizer
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            sweep(M, only="quantize")
-        g.replay()
-        torch.cuda.synchronize()
-        a, bb = ev(), ev()
-        a.record()
-        for _ in range(reps):
+        # quantizer (none where the matmul kernels quantize their activations)
+        qus = None
+        if not fused(M):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                sweep(M, only="quantize")
             g.replay()
-        bb.record()
-        torch.cuda.synchronize()
-        nq = layers * len(inputs)
-        qus = a.elapsed_time(bb) * 1e3 / (reps * nq)
-        qbytes = sum(M * in_K[i] * 4 + qd.qdot_q8_1_bytes(M, in_K[i]) for i in inputs) * layers
-        e = kern.setdefault("quantize_q8_1", [0, 0.0, 0, 0])
-        e[0] += qbytes
-        e[1] += qus * nq * 1e-3
-        e[2] += nq
+            torch.cuda.synchronize()
+            a, bb = ev(), ev()
+            a.record()
+            for _ in range(reps):
+                g.replay()
+            bb.record()
+            torch.cuda.synchronize()
+            nq = layers * len(inputs)
+            qus = a.elapsed_time(bb) * 1e3 / (reps * nq)
+            qbytes = sum(M * in_K[i] * 4 + qd.qdot_q8_1_bytes(M, in_K[i]) for i in inputs) * layers
+            e = kern.setdefault("quantize_q8_1", [0, 0.0, 0, 0])
+            e[0] += qbytes
+            e[1] += qus * nq * 1e-3
+            e[2] += nq
         wb_m = wbytes_sweep
         per_m[str(M)] = {"sweep_ms": round(float(np.median(per_m_ms[M])), 4),
                          "sweep_weight_GBps": round(wb_m / (np.median(per_m_ms[M]) * 1e-3) / 1e9, 1),
-                         "quantize_us": round(qus, 3), "qmatmul": rows}
+                         "quantize_us": round(qus, 3) if qus is not None else "in the matmul kernels",
+                         "qmatmul": rows}
 
     # The dominant kernel is the HIP kernel function with the largest share of
     # the step, summed over its template instances (weight types, M tile,
@@ -834,7 +856,7 @@ def main():
             layer = 0 if args.same_weights else layers - 1   # whose weights the last launches read
             for pi, (name, N, K, t) in enumerate(shapes):
                 W = synth.weights(t, N, K, synth.weight_seed(cfg_idx, layer, pi))
-                xq = b["xq"][INPUT_OF[name]].cpu().numpy()
+                xq = oracle.quantize_q8_1(b["x"][INPUT_OF[name]].cpu().numpy())
                 rows = np.random.default_rng(M * 100 + pi).integers(0, N, 8)
                 y64, _ = oracle.qmatmul_rows(W, t, N, K, xq, M, rows)
                 yg = b["y"][name].cpu().numpy()[:, rows].astype(np.float64)
@@ -871,8 +893,10 @@ def main():
         "config": {"workload": args.workload, "layers": layers, "M": Ms,
                    "projections": [f"{n} {N}x{K} {synth.TYPE_NAMES[t]}" for n, N, K, t in shapes],
                    "weight_bytes_per_sweep": wbytes_sweep,
-                   "launches_per_step": sum(len(units(M)) for M in Ms) * layers + len(Ms) * layers * len(inputs),
+                   "launches_per_step": sum(len(units(M)) for M in Ms) * layers +
+                                        sum(0 if fused(M) else 1 for M in Ms) * layers * len(inputs),
                    "grouped_launches": not args.separate,
+                   "quantized_in_matmul_at_M": [M for M in Ms if fused(M)],
                    **({"same_weights_every_layer": True} if args.same_weights else {})},
         **({"pct_mfma_i8_peak": round(100 * value / MFMA_I8_PEAK_TOPS, 2)} if prefill else
            {"pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1)}),

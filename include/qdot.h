@@ -163,6 +163,30 @@ int qdot_qmatmul_multi(int n, const void *const *W, const int *types,
                        const int64_t *N, int64_t K, const void *x_q8,
                        int64_t M, float *const *y, void *stream);
 
+/* The activation quantizer fused into the decode matmul: y = W x for fp32
+ * activations x [M][K] (device, 4-byte aligned), computed as
+ * qdot_qmatmul(W, type, N, K, quantize_q8_1(x), M) computes it -- bitwise
+ * the same y -- in one launch instead of two.  Each wave of the decode
+ * kernel quantizes the Q8_1 blocks of its own superblocks into LDS with the
+ * standalone quantizer's code (readings as qdot_quantize_q8_1), so no Q8_1
+ * buffer is written.  The pages launch quantize_q8_1 once ahead of the
+ * matmul (V100TPS log, 2026-08-12, ggml_mul_mat_a8); on MI355X a launch costs
+ * about as much as a small quantization, which is what the fusion saves.
+ * Every workgroup quantizes the activations it reads, so the fused call pays
+ * that work once per workgroup: it is meant for small M.  Runs the dot4
+ * decode tile.  1 <= M <= QDOT_QUANTIZE_QMATMUL_MAX_M, else E_ARG; other
+ * errors as qdot_qmatmul. */
+#define QDOT_QUANTIZE_QMATMUL_MAX_M 8
+int qdot_quantize_qmatmul(const void *W, int type, int64_t N, int64_t K,
+                          const float *x, int64_t M, float *y, void *stream);
+
+/* The same for up to QDOT_MULTI_MAX matrices that read the same activations
+ * (qdot_qmatmul_multi's grouping, dot4 tiles): y[i] bitwise equal to
+ * qdot_qmatmul(W[i], ..., quantize_q8_1(x), ...). */
+int qdot_quantize_qmatmul_multi(int n, const void *const *W, const int *types,
+                                const int64_t *N, int64_t K, const float *x,
+                                int64_t M, float *const *y, void *stream);
+
 /* RMSNorm fused with the Q8_1 quantizer: x_q8 = quantize_q8_1(RMSNorm(x) * w)
  * in one launch, for the producer of the Q/K/V and gate/up activations (the
  * xLLM v0.7 log, section C.1, quantizes the normalized input into one shared

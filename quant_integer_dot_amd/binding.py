@@ -57,6 +57,11 @@ def load():
     L.qdot_qmatmul_multi.argtypes = [i32, ctypes.POINTER(P), ctypes.POINTER(i32), ctypes.POINTER(i64),
                                      i64, P, i64, ctypes.POINTER(P), P]
     L.qdot_qmatmul_multi.restype = i32
+    L.qdot_quantize_qmatmul.argtypes = [P, i32, i64, i64, P, i64, P, P]
+    L.qdot_quantize_qmatmul.restype = i32
+    L.qdot_quantize_qmatmul_multi.argtypes = [i32, ctypes.POINTER(P), ctypes.POINTER(i32), ctypes.POINTER(i64),
+                                              i64, P, i64, ctypes.POINTER(P), P]
+    L.qdot_quantize_qmatmul_multi.restype = i32
     L.qdot_rmsnorm_quantize_q8_1.argtypes = [P, P, ctypes.c_float, i64, i64, P, P]
     L.qdot_rmsnorm_quantize_q8_1.restype = i32
     L.qdot_attn_decode_kv4.argtypes = [P, i64, P, P, i64, i64, i64, ctypes.c_float, P, P, ctypes.c_size_t, P]
@@ -155,6 +160,28 @@ def qdot_qmatmul_multi(Ws, wtypes, Ns, K, x_q8, M, ys, stream=None):
     y_arr = (P * max(n, 1))(*[_addr(y) for y in ys])
     _check(load().qdot_qmatmul_multi(n, w_arr, t_arr, n_arr, K, _addr(x_q8), M, y_arr, s),
            "qdot_qmatmul_multi")
+
+
+def qdot_quantize_qmatmul(W, wtype, N, K, x, M, y, stream=None):
+    """y = W x for fp32 x, the Q8_1 quantization done inside the decode kernel."""
+    s = _stream(stream, W, x, y)
+    _check(load().qdot_quantize_qmatmul(_addr(W), wtype, N, K, _addr(x), M, _addr(y), s),
+           "qdot_quantize_qmatmul")
+
+
+def qdot_quantize_qmatmul_multi(Ws, wtypes, Ns, K, x, M, ys, stream=None):
+    """Grouped qdot_quantize_qmatmul over matrices sharing the fp32 activations x."""
+    n = len(Ws)
+    if not (len(wtypes) == n and len(Ns) == n and len(ys) == n):
+        raise ValueError("Ws, wtypes, Ns and ys must have the same length")
+    s = _stream(stream, x, *Ws, *ys)
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    w_arr = (P * max(n, 1))(*[_addr(w) for w in Ws])
+    t_arr = (i32 * max(n, 1))(*wtypes)
+    n_arr = (i64 * max(n, 1))(*Ns)
+    y_arr = (P * max(n, 1))(*[_addr(y) for y in ys])
+    _check(load().qdot_quantize_qmatmul_multi(n, w_arr, t_arr, n_arr, K, _addr(x), M, y_arr, s),
+           "qdot_quantize_qmatmul_multi")
 
 
 def qdot_qmatmul_dump_isums(W, wtype, N, K, x_q8, M, y, isums, stream=None):

@@ -20,7 +20,8 @@ int launch_qmm(const void* W, int type, int N, int K, const void* xq, int M, flo
 int launch_qmm_skinny(const void* W, int type, int N, int K, const void* xq, int M, float* y,
                       int32_t* isums, hipStream_t s);
 int launch_qmv_multi(int n, const void* const* W, const int* types, const int* N, int K, const void* xq,
-                     int M, float* const* y, hipStream_t s);
+                     int M, float* const* y, bool xf, hipStream_t s);
+int launch_qmv_x(const void* W, int type, int N, int K, const float* x, int M, float* y, hipStream_t s);
 bool qmv_multi_uses_mfma(int n, const int* types, const int* N, int K, int M, int i);
 int launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);
 }  // namespace qdot
@@ -174,7 +175,37 @@ int qdot_qmatmul_multi(int n, const void* const* W, const int* types, const int6
   }
   int n32[QDOT_MULTI_MAX];
   for (int i = 0; i < n; ++i) n32[i] = (int)N[i];
-  const int rc = qdot::launch_qmv_multi(n, W, types, n32, (int)K, x_q8, (int)M, y,
+  const int rc = qdot::launch_qmv_multi(n, W, types, n32, (int)K, x_q8, (int)M, y, false,
+                                        static_cast<hipStream_t>(stream));
+  return rc == 0 ? QDOT_OK : QDOT_E_HIP;
+}
+
+int qdot_quantize_qmatmul(const void* W, int type, int64_t N, int64_t K, const float* x, int64_t M,
+                          float* y, void* stream) {
+  const int st = check_dims(type, N, K, M);
+  if (st) return st;
+  if (!W || !x || !y || M > QDOT_QUANTIZE_QMATMUL_MAX_M) return QDOT_E_ARG;
+  if ((double)M * (double)K > 4.0e18) return QDOT_E_ARG;
+  if (!aligned4(x) || !aligned4(y)) return QDOT_E_ALIGN;
+  const int rc = qdot::launch_qmv_x(W, type, (int)N, (int)K, x, (int)M, y, static_cast<hipStream_t>(stream));
+  return rc == 0 ? QDOT_OK : QDOT_E_HIP;
+}
+
+int qdot_quantize_qmatmul_multi(int n, const void* const* W, const int* types, const int64_t* N, int64_t K,
+                                const float* x, int64_t M, float* const* y, void* stream) {
+  if (n < 1 || n > QDOT_MULTI_MAX || !W || !types || !N || !y || !x) return QDOT_E_ARG;
+  if (M > QDOT_QUANTIZE_QMATMUL_MAX_M) return QDOT_E_ARG;
+  for (int i = 0; i < n; ++i) {
+    const int st = check_dims(types[i], N[i], K, M);
+    if (st) return st;
+    if (!W[i] || !y[i]) return QDOT_E_ARG;
+  }
+  if (!aligned4(x)) return QDOT_E_ALIGN;
+  for (int i = 0; i < n; ++i)
+    if (!aligned4(y[i])) return QDOT_E_ALIGN;
+  int n32[QDOT_MULTI_MAX];
+  for (int i = 0; i < n; ++i) n32[i] = (int)N[i];
+  const int rc = qdot::launch_qmv_multi(n, W, types, n32, (int)K, x, (int)M, y, true,
                                         static_cast<hipStream_t>(stream));
   return rc == 0 ? QDOT_OK : QDOT_E_HIP;
 }

@@ -66,6 +66,72 @@ __device__ __forceinline__ uint32_t q8_1_s_bits(__half dh, int sumq) {
   return __half_as_ushort(__float2half_rn(p));
 }
 
+// One Q8_1 block quantized by an aligned group of 8 lanes, 4 values a lane
+// (lane part p = lane % 8 holds elements 4p .. 4p+3): amax over the group,
+// d32 = amax / 127 (correctly rounded fp32 division; this code must never be
+// built with fast-math), q = roundf(v / d32) (fp32 division, ties away from
+// zero) clamped to [-127, 127], all zero when amax == 0; d and s stored as
+// binary16, s = d * sum q.  Returns this lane's four codes packed little
+// endian, the sum of its own four codes, and (in every lane of the group)
+// the block's code sum and its d | s << 16 bits.  Every lane of the wave must
+// call it (the group reductions are cross-lane shuffles).  The standalone
+// quantizer and the decode kernel's in-kernel quantization both use it, so
+// their bytes are the same by construction.
+__device__ __forceinline__ void q8_1_block8(const float (&v)[4], uint32_t& packed, int& part_sum,
+                                            int& sumq, uint32_t& ds) {
+  float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  amax = fmaxf(amax, __shfl_xor(amax, 4));
+  packed = 0;
+  part_sum = 0;
+  float d32 = 0.0f;
+  if (amax != 0.0f) {
+    d32 = amax / 127.0f;  // IEEE-correct fp32 division
+    // q = roundf(v / d32) with the correctly rounded quotient, found without
+    // a division where that provably gives the same integer: with r the
+    // hardware reciprocal of d32 (within 1 ulp) and t = v * r rounded, t is
+    // within |v/d32| * 1.5 * 2^-23 <= 2.3e-5 of v/d32 (|v/d32| <= 127.00001),
+    // and the rounded quotient within 3.9e-6 of it.  If t is more than 2^-14
+    // from every half-integer, all three lie strictly between the same two
+    // half-integers, so they round to the same integer, the nearest to t.
+    // Otherwise (or for a reciprocal out of range: a NaN or infinite t fails
+    // the test) the whole wave takes the correctly rounded division.
+    const float rcp = __builtin_amdgcn_rcpf(d32);
+    float n[4];
+    bool fast = d32 >= 0x1p-100f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float t = v[i] * rcp;
+      n[i] = __builtin_rintf(t);
+      fast = fast && fabsf(t - n[i]) < 0.5f - 0x1p-14f;
+    }
+    if (__all(fast)) {  // every active lane of the wave can take the fast path
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int qi = (int)fminf(fmaxf(n[i], -127.0f), 127.0f);
+        part_sum += qi;
+        packed |= ((uint32_t)qi & 0xFFu) << (8 * i);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float r = roundf(v[i] / d32);  // ties away from zero
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        const int qi = (int)r;
+        part_sum += qi;
+        packed |= ((uint32_t)qi & 0xFFu) << (8 * i);
+      }
+    }
+  }
+  sumq = part_sum;
+  sumq += __shfl_xor(sumq, 1);
+  sumq += __shfl_xor(sumq, 2);
+  sumq += __shfl_xor(sumq, 4);
+  const __half dh = __float2half_rn(d32);
+  ds = (uint32_t)__half_as_ushort(dh) | (q8_1_s_bits(dh, sumq) << 16);
+}
+
 // Integer dot of four int8 pairs, accumulated (v_dot4_i32_i8).
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
   return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);

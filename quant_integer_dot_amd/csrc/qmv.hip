@@ -69,6 +69,56 @@ static int launch_qmv_m(const uint8_t* W, int N, int K, const uint8_t* xq, int M
   return -2;
 }
 
+// In-kernel quantization (fp32 activations x; dot4 tile, M = 1..8).
+template <int T, int M, int DEPTH>
+static int launch_qmv_xk(const uint8_t* W, int N, int K, const uint8_t* x, float* y, hipStream_t s) {
+  const int P = qmv_waves(K / QK);
+  const size_t lds = qmv_lds_bytes_tile<M>(false, P);
+  const int grid = (N + QMV_SLOTS - 1) / QMV_SLOTS;
+  hipLaunchKernelGGL((qmv_kernel<T, M, DEPTH, false, true>), dim3(grid), dim3(64 * P), lds, s, W, N, K, x,
+                     y, nullptr);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <int T, int M>
+static int launch_qmv_xr(const uint8_t* W, int N, int K, const uint8_t* x, float* y, hipStream_t s) {
+  switch (qmv_depth(T, M, N, K)) {
+    case 1: return launch_qmv_xk<T, M, 1>(W, N, K, x, y, s);
+    case 2: return launch_qmv_xk<T, M, 2>(W, N, K, x, y, s);
+    default:
+      if constexpr (T == Q6_K || T == Q8_0) return launch_qmv_xk<T, M, 2>(W, N, K, x, y, s);
+      else return launch_qmv_xk<T, M, 4>(W, N, K, x, y, s);
+  }
+}
+
+template <int T>
+static int launch_qmv_xm(const uint8_t* W, int N, int K, const uint8_t* x, int M, float* y, hipStream_t s) {
+  switch (M) {
+    case 1: return launch_qmv_xr<T, 1>(W, N, K, x, y, s);
+    case 2: return launch_qmv_xr<T, 2>(W, N, K, x, y, s);
+    case 3: return launch_qmv_xr<T, 3>(W, N, K, x, y, s);
+    case 4: return launch_qmv_xr<T, 4>(W, N, K, x, y, s);
+    case 5: return launch_qmv_xr<T, 5>(W, N, K, x, y, s);
+    case 6: return launch_qmv_xr<T, 6>(W, N, K, x, y, s);
+    case 7: return launch_qmv_xr<T, 7>(W, N, K, x, y, s);
+    case 8: return launch_qmv_xr<T, 8>(W, N, K, x, y, s);
+    default: return -2;
+  }
+}
+
+int launch_qmv_x(const void* W, int type, int N, int K, const float* x, int M, float* y, hipStream_t s) {
+  const uint8_t* w8 = static_cast<const uint8_t*>(W);
+  const uint8_t* x8 = reinterpret_cast<const uint8_t*>(x);
+  switch (type) {
+    case Q4_K: return launch_qmv_xm<Q4_K>(w8, N, K, x8, M, y, s);
+    case Q6_K: return launch_qmv_xm<Q6_K>(w8, N, K, x8, M, y, s);
+    case IQ4_XS: return launch_qmv_xm<IQ4_XS>(w8, N, K, x8, M, y, s);
+    case Q4_0: return launch_qmv_xm<Q4_0>(w8, N, K, x8, M, y, s);
+    case Q8_0: return launch_qmv_xm<Q8_0>(w8, N, K, x8, M, y, s);
+    default: return -2;
+  }
+}
+
 int launch_qmv(const void* W, int type, int N, int K, const void* xq, int M, float* y,
                int32_t* isums, hipStream_t s) {
   const uint8_t* w8 = static_cast<const uint8_t*>(W);

@@ -26,6 +26,8 @@
 
 #pragma once
 
+#include <type_traits>
+
 #include "formats.hpp"
 
 namespace qdot {
@@ -221,25 +223,28 @@ template <int T> __device__ __forceinline__ int sub_index(int q, int half) {
 // fp64 view of one Q8_1 block's scales: D and (Q4_K) S, or (Q6_K) 32 times
 // the integer sum of each 16-element half of q (for the -32 code offset), or
 // (Q4_0) 8 times the integer sum of q (for the -8 code offset).
-__device__ __forceinline__ DsEntry ds_entry(int T, uint32_t ds, const u32x4& q0, const u32x4& q1) {
+// The same from the block's d | s << 16 bits and the code sums of its two
+// 16-element halves.
+__device__ __forceinline__ DsEntry ds_entry_sums(int T, uint32_t ds, int lo, int hi) {
   DsEntry e;
   e.d = (double)h2f(ds & 0xFFFFu);
   if (T == Q4_0) {
-    const uint32_t ones = 0x01010101u;
-    const int lo = dot4(q0.w, ones, dot4(q0.z, ones, dot4(q0.y, ones, dot4(q0.x, ones, 0))));
-    const int sum = dot4(q1.w, ones, dot4(q1.z, ones, dot4(q1.y, ones, dot4(q1.x, ones, lo))));
-    e.xs32[0] = 8 * sum;
+    e.xs32[0] = 8 * (lo + hi);
     e.xs32[1] = 0;
   } else if (T == Q6_K) {
-    const uint32_t ones = 0x01010101u;
-    const int lo = dot4(q0.w, ones, dot4(q0.z, ones, dot4(q0.y, ones, dot4(q0.x, ones, 0))));
-    const int hi = dot4(q1.w, ones, dot4(q1.z, ones, dot4(q1.y, ones, dot4(q1.x, ones, 0))));
     e.xs32[0] = 32 * lo;
     e.xs32[1] = 32 * hi;
   } else {
     e.s = (double)h2f(ds >> 16);
   }
   return e;
+}
+__device__ __forceinline__ DsEntry ds_entry(int T, uint32_t ds, const u32x4& q0, const u32x4& q1) {
+  if (T != Q4_0 && T != Q6_K) return ds_entry_sums(T, ds, 0, 0);
+  const uint32_t ones = 0x01010101u;
+  const int lo = dot4(q0.w, ones, dot4(q0.z, ones, dot4(q0.y, ones, dot4(q0.x, ones, 0))));
+  const int hi = dot4(q1.w, ones, dot4(q1.z, ones, dot4(q1.y, ones, dot4(q1.x, ones, 0))));
+  return ds_entry_sums(T, ds, lo, hi);
 }
 
 // The integer dots of one (row, activation row, half quarter) and their
@@ -322,10 +327,17 @@ constexpr int QMV_MGROUP = 4;  // activation rows held in registers at once
 // up, so no wait covers weights fetched for later superblocks, and no
 // workgroup barrier sits in the main loop.
 // The work of one workgroup: weight rows 16*tile .. 16*tile+15 of one matrix.
-template <int T, int M, int DEPTH, bool DUMP>
+//
+// XF: the activations arrive as fp32 rows x [M][K] (xq points at them) and
+// each wave quantizes the 8*M Q8_1 blocks of its superblock itself, into the
+// same LDS slice, with the standalone quantizer's code (q8_1_block8), so the
+// slice holds the same bytes quantize_q8_1 would have written: one launch
+// instead of a quantize launch and a matmul launch, and bitwise the same y.
+template <int T, int M, int DEPTH, bool DUMP, bool XF = false>
 __device__ __forceinline__ void qmv_tile(const uint8_t* __restrict__ W, int N, int K,
                                          const uint8_t* __restrict__ xq, float* __restrict__ y,
                                          int32_t* __restrict__ isums, int tile, uint8_t* smem) {
+  static_assert(!(XF && DUMP), "the sub-block dump reads quantized activations");
   constexpr int BYTES = Geom<T>::BYTES;
   constexpr int ITEMS = 8 * M;  // Q8_1 blocks per superblock and activation rows
   static_assert(ITEMS <= 64, "one activation block per lane");
@@ -349,10 +361,15 @@ __device__ __forceinline__ void qmv_tile(const uint8_t* __restrict__ W, int N, i
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.0;
 
+  // XF: this lane's four fp32 values of block j = lane / 8 of the superblock
+  // (part lane % 8), for each activation row
+  const uint8_t* xfsrc = xq + (size_t)(32 * (lane >> 3) + 4 * (lane & 7)) * sizeof(float);
+
+  struct XStage { uint32_t ds; u32x4 c0, c1; };   // one Q8_1 block
+  struct FStage { u32x4 v[M]; };                   // fp32 values, one row each
   struct Stage {
     typename Fmt<T>::Regs w;
-    uint32_t ds;
-    u32x4 c0, c1;
+    typename std::conditional<XF, FStage, XStage>::type x;
   };
   Stage S[DEPTH];
   // Unconditional loads (superblock clamped to the row): the compiler then
@@ -360,10 +377,16 @@ __device__ __forceinline__ void qmv_tile(const uint8_t* __restrict__ W, int N, i
   auto fetch = [&](Stage& st, int bsb) {
     const int bc = bsb < nsb ? bsb : nsb - 1;
     st.w = Fmt<T>::load(wrow + (size_t)bc * BYTES, q);
-    const uint8_t* src = xsrc + (size_t)bc * 8 * Q8_BYTES;
-    st.ds = ld4(src);
-    st.c0 = ld16(src + 4);
-    st.c1 = ld16(src + 20);
+    if constexpr (XF) {
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        st.x.v[m] = ld16(xfsrc + ((size_t)m * K + (size_t)bc * QK) * sizeof(float));
+    } else {
+      const uint8_t* src = xsrc + (size_t)bc * 8 * Q8_BYTES;
+      st.x.ds = ld4(src);
+      st.x.c0 = ld16(src + 4);
+      st.x.c1 = ld16(src + 20);
+    }
   };
   auto wave_sync = [] {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -372,10 +395,29 @@ __device__ __forceinline__ void qmv_tile(const uint8_t* __restrict__ W, int N, i
   };
   auto compute = [&](const Stage& st, int b) {
     wave_sync();  // the previous superblock's LDS reads are done
-    if (lane < ITEMS) {
-      *reinterpret_cast<u32x4*>(lds_x + item * Q8_BLOCK) = st.c0;
-      *reinterpret_cast<u32x4*>(lds_x + item * Q8_BLOCK + 16) = st.c1;
-      lds_ds[item] = ds_entry(T, st.ds, st.c0, st.c1);
+    if constexpr (XF) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float v[4] = {__uint_as_float(st.x.v[m].x), __uint_as_float(st.x.v[m].y),
+                            __uint_as_float(st.x.v[m].z), __uint_as_float(st.x.v[m].w)};
+        uint32_t packed, ds;
+        int part_sum, sumq;
+        q8_1_block8(v, packed, part_sum, sumq, ds);
+        // code sums of the block's halves (parts 0-3, 4-7) for the -32 / -8 offsets
+        int h = part_sum;
+        h += __shfl_xor(h, 1);
+        h += __shfl_xor(h, 2);
+        const int hi = __shfl_xor(h, 4);
+        const int it = 8 * m + (lane >> 3);
+        *reinterpret_cast<uint32_t*>(lds_x + it * Q8_BLOCK + 4 * (lane & 7)) = packed;
+        if ((lane & 7) == 0) lds_ds[it] = ds_entry_sums(T, ds, h, hi);
+      }
+    } else {
+      if (lane < ITEMS) {
+        *reinterpret_cast<u32x4*>(lds_x + item * Q8_BLOCK) = st.x.c0;
+        *reinterpret_cast<u32x4*>(lds_x + item * Q8_BLOCK + 16) = st.x.c1;
+        lds_ds[item] = ds_entry(T, st.x.ds, st.x.c0, st.x.c1);
+      }
     }
     wave_sync();
 #pragma unroll
@@ -809,12 +851,14 @@ template <int T, int M> inline size_t qmv_lds_bytes(int waves) {
   return qmv_lds_bytes_tile<M>(qmf_ok<T, M>(), waves);
 }
 
-template <int T, int M, int DEPTH, bool DUMP>
+template <int T, int M, int DEPTH, bool DUMP, bool XF = false>
 __global__ __launch_bounds__(QMV_MAX_THREADS) void qmv_kernel(
     const uint8_t* __restrict__ W, int N, int K, const uint8_t* __restrict__ xq,
     float* __restrict__ y, int32_t* __restrict__ isums) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  if constexpr (M > 8)
+  if constexpr (XF)
+    qmv_tile<T, M, DEPTH, false, true>(W, N, K, xq, y, nullptr, blockIdx.x, smem);
+  else if constexpr (M > 8)
     qmf16_tile<T, M, DEPTH, DUMP>(W, N, K, xq, y, isums, blockIdx.x, smem);
   else if constexpr (qmf_ok<T, M>())
     qmf_tile<T, M, DEPTH, DUMP>(W, N, K, xq, y, isums, blockIdx.x, smem);
@@ -837,9 +881,12 @@ struct QmvMulti {
   int n;
 };
 
-template <int TA, int TB, int M, int DEPTH, bool MF>
+// XF: fp32 activations quantized in the kernel (qmv_tile's XF mode; dot4
+// tiles only).
+template <int TA, int TB, int M, int DEPTH, bool MF, bool XF = false>
 __global__ __launch_bounds__(QMV_MAX_THREADS) void qmv_multi_kernel(QmvMulti a, int K,
                                                                     const uint8_t* __restrict__ xq) {
+  static_assert(!(XF && MF), "in-kernel quantization runs on the dot4 tile");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int g = blockIdx.x;
   int i = 0;
@@ -851,12 +898,12 @@ __global__ __launch_bounds__(QMV_MAX_THREADS) void qmv_multi_kernel(QmvMulti a, 
     if constexpr (qmf_group_ok<TA, M, MF>())
       qmf_tile<TA, M, DEPTH, false>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
     else
-      qmv_tile<TA, M, DEPTH, false>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
+      qmv_tile<TA, M, DEPTH, false, XF>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
   } else {
     if constexpr (qmf_group_ok<TB, M, MF>())
       qmf_tile<TB, M, DEPTH, false>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
     else
-      qmv_tile<TB, M, DEPTH, false>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
+      qmv_tile<TB, M, DEPTH, false, XF>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
   }
 }
 

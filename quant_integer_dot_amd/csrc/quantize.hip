@@ -9,7 +9,8 @@
 // binary16 round-to-nearest-even, s = d*sum(q).
 //
 // Mapping: 8 lanes per 32-element block, 4 floats per lane (one 16-byte
-// load); amax and sum(q) are reduced over the 8 lanes with xor shuffles.  The
+// load); amax and sum(q) are reduced over the 8 lanes with xor shuffles
+// (q8_1_block8, shared with the decode kernel's in-kernel quantization).  The
 // kernel is HBM-bound (4 B read, 1.125 B written per element).
 #include "qdot_common.hpp"
 
@@ -29,37 +30,14 @@ __global__ __launch_bounds__(256) void quantize_q8_1_kernel(
     v[2] = __uint_as_float(raw.z);
     v[3] = __uint_as_float(raw.w);
   }
-  float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
-  amax = fmaxf(amax, __shfl_xor(amax, 2));
-  amax = fmaxf(amax, __shfl_xor(amax, 4));
-
-  uint32_t packed = 0;
-  int sumq = 0;
-  float d32 = 0.0f;
-  if (amax != 0.0f) {
-    d32 = amax / 127.0f;  // IEEE-correct fp32 division
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float r = roundf(v[i] / d32);  // ties away from zero
-      r = fminf(fmaxf(r, -127.0f), 127.0f);
-      int qi = (int)r;
-      sumq += qi;
-      packed |= ((uint32_t)qi & 0xFFu) << (8 * i);
-    }
-  }
-  sumq += __shfl_xor(sumq, 1);
-  sumq += __shfl_xor(sumq, 2);
-  sumq += __shfl_xor(sumq, 4);
+  uint32_t packed, ds;
+  int part_sum, sumq;
+  q8_1_block8(v, packed, part_sum, sumq, ds);
   if (!live) return;
 
   uint8_t* ob = out + blk * Q8_BYTES;
   *reinterpret_cast<uint32_t*>(ob + 4 + 4 * part) = packed;
-  if (part == 0) {
-    const __half dh = __float2half_rn(d32);
-    const uint32_t ds = (uint32_t)__half_as_ushort(dh) | (q8_1_s_bits(dh, sumq) << 16);
-    *reinterpret_cast<uint32_t*>(ob) = ds;
-  }
+  if (part == 0) *reinterpret_cast<uint32_t*>(ob) = ds;
 }
 
 int launch_quantize_q8_1(const float* x, int64_t M, int64_t K, void* xq, hipStream_t s) {

@@ -284,3 +284,25 @@ def test_attn_noalloc_validation(lib):
     assert f(FAKE, 4, FAKE, FAKE, 3, 100, D, ctypes.c_float(0.1), FAKE, None) == qd.QDOT_E_ARG
     assert f(FAKE, 4, FAKE + 4, FAKE, 1, 100, D, ctypes.c_float(0.1), FAKE, None) == qd.QDOT_E_ALIGN
     assert f(FAKE, 4, FAKE, FAKE, 1, 100, D, ctypes.c_float(float("nan")), FAKE, None) == qd.QDOT_E_ARG
+
+
+def test_quantize_qmatmul_validation(lib):
+    """The fused quantizer + matmul calls take M <= 8 and check everything
+    before any HIP call."""
+    f = lib.qdot_quantize_qmatmul
+    assert f(FAKE, 1, 16, 256, FAKE, 9, FAKE, None) == qd.QDOT_E_ARG          # M above the decode range
+    assert f(FAKE, 1, 16, 256, FAKE, 0, FAKE, None) == qd.QDOT_E_ARG
+    assert f(FAKE, 7, 16, 256, FAKE, 1, FAKE, None) == qd.QDOT_E_ARG          # type
+    assert f(FAKE, 1, 16, 300, FAKE, 1, FAKE, None) == qd.QDOT_E_ARG          # K % 256
+    assert f(0, 1, 16, 256, FAKE, 1, FAKE, None) == qd.QDOT_E_ARG
+    assert f(FAKE, 1, 16, 256, FAKE + 2, 1, FAKE, None) == qd.QDOT_E_ALIGN    # x misaligned
+    assert f(FAKE, 1, 16, 256, FAKE, 1, FAKE + 1, None) == qd.QDOT_E_ALIGN
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    w = (P * 2)(FAKE, FAKE)
+    t = (i32 * 2)(1, 2)
+    n = (i64 * 2)(16, 16)
+    y = (P * 2)(FAKE, FAKE)
+    g = lib.qdot_quantize_qmatmul_multi
+    assert g(2, w, t, n, 256, FAKE, 9, y, None) == qd.QDOT_E_ARG
+    assert g(5, w, t, n, 256, FAKE, 1, y, None) == qd.QDOT_E_ARG
+    assert g(2, w, t, n, 256, FAKE + 2, 1, y, None) == qd.QDOT_E_ALIGN

@@ -58,6 +58,40 @@ def test_quantizer_edge_values():
     assert np.array_equal(got, oracle.quantize_q8_1(x).reshape(-1))
 
 
+def near_half_integer_blocks(nblk, seed):
+    """Blocks whose values sit within a few ulps of (k + 1/2) * d32 (d32 the
+    block's scale): the quantizer's rounding decisions there depend on the
+    correctly rounded quotient, and the reciprocal shortcut must hand them to
+    the division.  Also the block of the oracle's division pin."""
+    rng = np.random.default_rng(seed)
+    x = np.zeros((nblk, 32), np.float32)
+    for b in range(nblk):
+        A = np.float32(rng.uniform(0.1, 50.0)) * np.float32(2.0 ** int(rng.integers(-20, 20)))
+        d32 = np.float32(A / np.float32(127.0))
+        x[b, 0] = A if rng.random() < 0.5 else -A
+        for i in range(1, 32):
+            k = int(rng.integers(-127, 127))
+            v = np.float32((k + 0.5) * np.float64(d32))
+            for _ in range(int(rng.integers(-3, 4))):
+                v = np.nextafter(v, np.float32(np.inf))
+            if abs(v) > A:
+                v = np.float32(0.0)
+            x[b, i] = v
+    pin = [1.6125396490097046, 0.08253155648708344, -0.33647480607032776, 0.5269322395324707,
+           -0.5396293997764587, 0.0698343887925148, 0.03174290433526039, -0.057137228548526764]
+    x[0] = 0.0
+    x[0, :len(pin)] = pin
+    return x
+
+
+def test_quantizer_near_half_integers():
+    """Byte-exact against the oracle on values at the quantizer's rounding
+    boundaries (both the reciprocal path and its division fallback run)."""
+    x = near_half_integer_blocks(4096, 5).reshape(8, -1)
+    _, got = quantize(x)
+    assert np.array_equal(got, oracle.quantize_q8_1(x).reshape(-1))
+
+
 # ---------------------------------------------------------------- matmul
 CASES = [
     # (N, K): several 32-row workgroup tiles plus ragged tails, one superblock
