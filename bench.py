@@ -51,7 +51,8 @@ def parse():
     p.add_argument("--workload", default="qwen3-8b-decode",
                    choices=["qwen3-8b-decode", "qwen3-8b-prefill-512", "iq4xs-h5120-decode",
                             "qwen2.5-1.5b-decode", "qwen3-8b-q4_0-q8_0-decode", "qwen3-8b-mid-batch",
-                            "qwen3-8b-rmsnorm-q8_1", "q4k-matvec-1536", "qwen3-8b-attn-kv4-32k"])
+                            "qwen3-8b-rmsnorm-q8_1", "q4k-matvec-1536", "qwen3-8b-attn-kv4-32k",
+                            "qwen3-8b-tp8-shard-decode"])
     p.add_argument("--ms", default=None, help="comma-separated M values (default per workload)")
     p.add_argument("--ctx", type=int, default=32768,
                    help="context length of the attention workload (tokens in the KV cache)")
@@ -65,6 +66,8 @@ def parse():
     p.add_argument("--fused-max-m", type=int, default=1,
                    help="largest M whose launches quantize the activations in the matmul kernel "
                         "(qdot_quantize_qmatmul[_multi]) instead of a separate quantize launch; 0 = never")
+    p.add_argument("--no-shard-rows", action="store_true",
+                   help="skip the tensor-parallel share rows of the decode workload")
     p.add_argument("--separate", action="store_true",
                    help="one launch per projection (default: projections sharing an input in one "
                         "qdot_qmatmul_multi launch for M <= 8)")
@@ -89,6 +92,8 @@ def workload_def(name):
         return 5, synth.QWEN3_8B_Q40_Q80, 36, [1, 2, 4, 8]
     if name == "qwen3-8b-mid-batch":
         return 6, synth.QWEN3_8B, 36, [16, 32, 64, 96]
+    if name == "qwen3-8b-tp8-shard-decode":
+        return 7, synth.QWEN3_8B_TP8, 36, list(range(1, 9))
     if name == "q4k-matvec-1536":
         # One 1536 x 1536 Q4_K matrix at M = 1, as 400 distinct seeded copies
         # (531 MB, over twice the 256 MB Infinity Cache) launched in turn, so
@@ -324,6 +329,114 @@ def stream_reference(dev, launch_bytes, reps=10):
     t = e0.elapsed_time(e1) * 1e-3 / 36
     out["read_at_launch_size"] = {"bytes_per_read": m, "us": round(t * 1e6, 3), "GBps": round(m / t / 1e9, 1)}
     return out
+
+
+def shard_rows_shapes():
+    """The FFN matrices of one GPU's 8-way tensor-parallel share: gate and up
+    column-parallel (1536 x 4096), down row-parallel (4096 x 1536)."""
+    from quant_integer_dot_amd import synth
+    return [s for s in synth.QWEN3_8B_TP8 if s[0] in ("gate", "up", "down")]
+
+
+def shard_rows(dev, fused_max_m, reps, per_m_full, check=True):
+    """Per-launch timing of the tensor-parallel FFN share at M = 1..8 on this
+    one GPU: gate+up (one grouped launch) and down, 36 distinct seeded layers
+    (440 MB, cold in the 256 MB Infinity Cache), each launch list captured in
+    a graph and replayed between HIP events, with the full-shape rows of the
+    same step beside them where that M is in the step."""
+    import numpy as np
+    import torch
+    from quant_integer_dot_amd import binding as qd
+    from quant_integer_dot_amd import synth
+
+    shapes = shard_rows_shapes()
+    cfg_idx, layers = 7, 36
+    pidx = {n: i for i, (n, *_) in enumerate(synth.QWEN3_8B_TP8)}
+    W = [[torch.from_numpy(synth.weights(t, N, K, synth.weight_seed(cfg_idx, layer, pidx[n]))).to(dev)
+          for n, N, K, t in shapes] for layer in range(layers)]
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    out = {}
+    bad = nchk = 0
+    for M in range(1, 9):
+        fz = M <= fused_max_m
+        xs, xqs, ys = {}, {}, {}
+        for K in (4096, 1536):
+            x = torch.from_numpy(synth.activations(M, K, synth.act_seed(cfg_idx, K, M))).to(dev)
+            xq = torch.empty(qd.qdot_q8_1_bytes(M, K), dtype=torch.uint8, device=dev)
+            qd.qdot_quantize_q8_1(x, M, K, xq)
+            xs[K], xqs[K] = x, xq
+        for n, N, K, t in shapes:
+            ys[n] = torch.empty((M, N), dtype=torch.float32, device=dev)
+        gate, up, down = shapes
+
+        def launch(label, layer):
+            if label == "gate+up":
+                Ws, ts, Ns = W[layer][:2], [gate[3], up[3]], [gate[1], up[1]]
+                if fz:
+                    qd.qdot_quantize_qmatmul_multi(Ws, ts, Ns, 4096, xs[4096], M, [ys["gate"], ys["up"]])
+                else:
+                    qd.qdot_qmatmul_multi(Ws, ts, Ns, 4096, xqs[4096], M, [ys["gate"], ys["up"]])
+            else:
+                _, N, K, t = down
+                if fz:
+                    qd.qdot_quantize_qmatmul(W[layer][2], t, N, K, xs[K], M, ys["down"])
+                else:
+                    qd.qdot_qmatmul(W[layer][2], t, N, K, xqs[K], M, ys["down"])
+
+        rows = {}
+        for label in ("gate+up", "down"):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for layer in range(layers):
+                    launch(label, layer)
+            g.replay()
+            torch.cuda.synchronize()
+            a, b = ev(), ev()
+            a.record()
+            for _ in range(reps):
+                g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / (reps * layers)
+            mats = shapes[:2] if label == "gate+up" else shapes[2:]
+            wb = sum(qd.qdot_weight_bytes(t, N, K) for _, N, K, t in mats)
+            K = mats[0][2]
+            if fz:
+                tiles = [f"qmv_dot4q<{synth.TYPE_NAMES[t]},{M}>" for *_, t in mats]
+            elif len(mats) == 2:
+                tiles = [qd.qdot_multi_kernel_name([t for *_, t in mats], [N for _, N, _, _ in mats], K, M, i)
+                         for i in range(2)]
+            else:
+                tiles = [qd.qdot_kernel_name_shape(mats[0][3], mats[0][1], K, M)]
+            row = {"shape": " + ".join(f"{N}x{K} {synth.TYPE_NAMES[t]}" for _, N, K, t in mats),
+                   "us": round(us, 3), "weight_GBps": round(wb / us / 1e3, 1),
+                   "pct_hbm_peak": round(100 * wb / us / 1e3 / HBM_PEAK_GBS, 1), "tiles": tiles}
+            full = (per_m_full or {}).get(str(M), {}).get("qmatmul", {}).get(label)
+            if full:
+                row["full_shape"] = {"us": full["us"], "pct_hbm_peak": full["pct_hbm_peak"]}
+            rows[label] = row
+        if check:
+            import oracle
+            for layer_label in ("gate+up", "down"):
+                launch(layer_label, layers - 1)
+            torch.cuda.synchronize()
+            for i, (n, N, K, t) in enumerate(shapes):
+                Wh = synth.weights(t, N, K, synth.weight_seed(cfg_idx, layers - 1, pidx[n]))
+                xq = oracle.quantize_q8_1(xs[K].cpu().numpy())
+                r = np.random.default_rng(700 + 10 * M + i).integers(0, N, 8)
+                y64, _ = oracle.qmatmul_rows(Wh, t, N, K, xq, M, r)
+                yg = ys[n].cpu().numpy()[:, r].astype(np.float64)
+                bad += int((np.abs(yg - y64) > 1e-5 * np.abs(y64)).sum())
+                nchk += y64.size
+        out[str(M)] = rows
+    res = {"what": "one GPU's share of 8-way tensor parallelism: gate/up split by rows (column-parallel), "
+                   "down by K (row-parallel); 36 distinct layers, cold; no collective runs",
+           "per_M": out}
+    if check:
+        res["sampled_check"] = {"outputs_checked": nchk, "outside_1e-5_rel": bad}
+        if bad:
+            log(f"[bench] SHARD ROWS CHECK FAILED: {bad} of {nchk} outputs")
+    return res
 
 
 def producer_bench(args):
@@ -866,6 +979,10 @@ def main():
         if bad:
             log(f"[bench] SAMPLED CHECK FAILED: {bad} of {nchk} outputs")
 
+    shard = None
+    if args.workload == "qwen3-8b-decode" and not args.no_shard_rows:
+        shard = shard_rows(dev, args.fused_max_m, reps, per_m, check=not args.no_check)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(shapes, cfg_idx, Ms, prefill=prefill, layers=layers)
@@ -903,6 +1020,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "per_M": per_m,
+        **({"shard_tp8_rows": shard} if shard else {}),
         "kernels": kernels,
         "sampled_check": check,
     }

@@ -45,6 +45,14 @@ IQ4XS_H5120 = [
     ("gate", 17408, 5120, IQ4_XS), ("up", 17408, 5120, IQ4_XS),
     ("down", 5120, 17408, IQ4_XS),
 ]
+# One GPU's share of the Qwen3-8B layer under 8-way tensor parallelism:
+# q, k, v, gate and up split by output rows (column-parallel), o and down by
+# K (row-parallel, whole superblocks: 4096 / 8 = 512 and 12288 / 8 = 1536).
+QWEN3_8B_TP8 = [
+    ("q", 512, 4096, Q4_K), ("k", 128, 4096, Q4_K), ("v", 128, 4096, Q6_K),
+    ("o", 4096, 512, Q4_K), ("gate", 1536, 4096, Q4_K), ("up", 1536, 4096, Q4_K),
+    ("down", 4096, 1536, Q6_K),
+]
 
 # Workloads: index -> description.  Index 4 reuses the Qwen3-8B shapes at M=512.
 WORKLOADS = {
@@ -55,6 +63,7 @@ WORKLOADS = {
     4: dict(name="qwen3-8b-prefill-512", shapes=QWEN3_8B, layers=36, Ms=[512]),
     5: dict(name="qwen3-8b-q4_0-q8_0-decode", shapes=QWEN3_8B_Q40_Q80, layers=36, Ms=[1, 2, 4, 8]),
     6: dict(name="qwen3-8b-mid-batch", shapes=QWEN3_8B, layers=36, Ms=[16, 32, 64, 96]),
+    7: dict(name="qwen3-8b-tp8-shard-decode", shapes=QWEN3_8B_TP8, layers=36, Ms=list(range(1, 9))),
 }
 
 

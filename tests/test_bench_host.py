@@ -22,7 +22,8 @@ def test_more_than_one_gpu_is_refused():
 
 
 @pytest.mark.parametrize("name", ["qwen3-8b-decode", "qwen3-8b-prefill-512", "iq4xs-h5120-decode",
-                                  "qwen2.5-1.5b-decode", "qwen3-8b-q4_0-q8_0-decode", "qwen3-8b-mid-batch"])
+                                  "qwen2.5-1.5b-decode", "qwen3-8b-q4_0-q8_0-decode", "qwen3-8b-mid-batch",
+                                  "qwen3-8b-tp8-shard-decode"])
 def test_workloads_match_the_synthetic_configs(name):
     """Each bench workload has the shapes and layer count of the synthetic
     config it names, and M values inside that config's list."""
@@ -31,6 +32,23 @@ def test_workloads_match_the_synthetic_configs(name):
     assert w["name"] == name
     assert shapes == w["shapes"] and layers == w["layers"]
     assert set(Ms) <= set(w["Ms"])
+
+
+def test_tp8_shard_shapes():
+    """The tensor-parallel share: q, k, v, gate, up split by rows, o and down
+    by K, 8 ways, on superblock boundaries; together an eighth of the
+    layer's weights."""
+    full = {n: (N, K, t) for n, N, K, t in synth.QWEN3_8B}
+    for n, N, K, t in synth.QWEN3_8B_TP8:
+        fN, fK, ft = full[n]
+        assert t == ft
+        if n in ("o", "down"):
+            assert (N, K * 8) == (fN, fK) and K % 256 == 0
+        else:
+            assert (N * 8, K) == (fN, fK)
+    wb = lambda shapes: sum(synth.weight_bytes(t, N, K) for _, N, K, t in shapes)
+    assert wb(synth.QWEN3_8B_TP8) * 8 == wb(synth.QWEN3_8B)
+    assert [s for s in synth.QWEN3_8B_TP8 if s[0] in ("gate", "up", "down")] == bench.shard_rows_shapes()
 
 
 def test_c0_workload_is_cold():
