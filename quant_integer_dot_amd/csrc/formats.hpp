@@ -82,12 +82,20 @@ __device__ __forceinline__ uint32_t q6k_code(uint32_t ql, uint32_t qh, int gp) {
   else return (ql & 0x0F0F0F0Fu) | ((qh << (4 - 2 * gp)) & 0x30303030u);
 }
 
-// Q6_K: four six-bit codes (0..63, one per byte) -> int8 code - 32 (bit 5
-// flipped is the six-bit two's complement, then sign-extended to eight bits).
+// Q6_K: four six-bit codes (0..63, one per byte) -> int8 code - 32.  With
+// bit 7 of each byte set first, the subtraction cannot borrow across bytes
+// (128 + c - 32 >= 96), and flipping bit 7 back leaves c - 32 modulo 256.
 __device__ __forceinline__ uint32_t q6k_signed(uint32_t u) {
-  const uint32_t v = u ^ 0x20202020u;
-  const uint32_t t = v & 0x20202020u;
-  return v | (t << 1) | (t << 2);
+  return ((u | 0x80808080u) - 0x20202020u) ^ 0x80808080u;
+}
+
+// Q6_K: the exact integer s0*I0 + s1*I1 of two 16-element sub-blocks (int8
+// sub-scales s, sub-block sums I of 16 codes |c - 32| <= 32 against |q| <=
+// 127, so |I| <= 65024 and |s*I| < 2^23) on the full-rate 24-bit multipliers
+// (v_mul_i32_i24, v_mad_i32_i24).  Written as a plain int expression it
+// compiles to v_mul_lo_u32 and v_mad_u64_u32, four times slower.
+__device__ __forceinline__ int q6k_pair(int s0, int I0, int s1, int I1) {
+  return __mul24(s0, I0) + __mul24(s1, I1);
 }
 
 // Q4_0: four nibble codes (0..15, one per byte) -> int8 code - 8, without

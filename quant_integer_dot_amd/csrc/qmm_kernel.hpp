@@ -395,7 +395,7 @@ __global__ __launch_bounds__(64 * QMM_WAVES, (qmm_min_waves<T, KP, DUMP>())) voi
             const double D = stage[J][i].d;
 #pragma unroll
             for (int t = 0; t < QMM_NT; ++t) {
-              const int P = s0[t] * I0[t][r] + s1[t] * I1[t][r];   // exact int
+              const int P = q6k_pair(s0[t], I0[t][r], s1[t], I1[t][r]);  // exact int
               acc[t][r] = fma(d[t] * D, (double)P, acc[t][r]);     // exact product
               if (DUMP) {
                 const int m = m0 + i, n = n0 + 32 * t + c32;

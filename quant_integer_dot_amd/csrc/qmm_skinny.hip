@@ -288,7 +288,7 @@ __global__ __launch_bounds__(64 * SK_WAVES) void qmm_skinny_kernel(
           const v4i_s I1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(a1, bw, z, 0, 0, 0);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int P = we.s01[0] * I0[r] + we.s01[1] * I1[r];  // exact int
+            const int P = q6k_pair(we.s01[0], I0[r], we.s01[1], I1[r]);  // exact int
             acc[t][r] = fma(we.w * ae[r].d, (double)P, acc[t][r]);
             if (DUMP) {
               const int m = m0 + 4 * s + r, n = n0 + 16 * t + c16;

@@ -260,7 +260,7 @@ __device__ __forceinline__ void dot_drain(const Sub<T>& sw, const uint32_t (&xa)
     for (int i = 4; i < 8; ++i) I1 = dot4(sw.cw[i], xa[i], I1);
     I0 -= de.xs32[0];
     I1 -= de.xs32[1];
-    const int Pq = sw.s0 * I0 + sw.s1 * I1;               // exact int
+    const int Pq = q6k_pair(sw.s0, I0, sw.s1, I1);        // exact int
     acc = fma(sw.d * de.d, (double)Pq, acc);              // exact product, one rounding
     if (DUMP && isp) { isp[0] = I0; isp[1] = I1; }
   } else {
