@@ -8,8 +8,8 @@ pass of the whole path for M = 1, 2, 4 and 8 token rows: per layer, four
 activation quantizations (qkv input, o input, gate/up input, down input) and the
 seven qmatmuls.  At M = 1 (--fused-max-m) the quantizations run inside the
 matmul launches (qdot_quantize_qmatmul[_multi], bitwise the same results),
-which measured faster there than a separate quantize launch; above it, one
-quantize launch per input.  Every matrix is cold in the 256 MB Infinity Cache because a
+which measured faster there than a separate quantize launch (except with
+IQ4_XS weights); above it, one quantize launch per input.  Every matrix is cold in the 256 MB Infinity Cache because a
 36-layer sweep streams 4.4 GB.
 
 Timing: each M's 36-layer sweep is captured once in a HIP graph; the timed
@@ -750,9 +750,15 @@ def main():
                 out.extend((shapes[pi][0], [pi]) for pi in pis)
         return out
 
+    # IQ4_XS's dot4 tile already spends its VALU on the codebook lookups: its
+    # launches with the quantization inside measured slower than a separate
+    # quantize launch (hidden-5120 sweep at M = 1: 4.29 vs 4.09 ms), so
+    # workloads with IQ4_XS weights keep the separate launch.
+    fusable = not prefill and all(t != synth.IQ4_XS for *_, t in shapes)
+
     def fused(M):
         """Whether M's launches quantize their activations themselves."""
-        return M <= args.fused_max_m and not prefill
+        return M <= args.fused_max_m and fusable
 
     def unit_kernel(M, pis):
         if fused(M):
