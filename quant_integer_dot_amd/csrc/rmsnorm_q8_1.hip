@@ -17,8 +17,8 @@
 // Mapping: one workgroup per row, thread b owns Q8_1 block b (32 elements,
 // four groups of 8; K <= 32768).  The group sums are formed in parallel and
 // staged in LDS; one thread then adds all K/8 of them in order (the only
-// serial part: K/8 dependent fp32 adds), and every thread normalizes and
-// quantizes its own block.
+// serial part: K/8 dependent fp32 adds, its LDS reads issued well ahead),
+// and every thread normalizes and quantizes its own block.
 #include "qdot_common.hpp"
 
 #pragma clang fp contract(off)
@@ -26,6 +26,7 @@
 namespace qdot {
 
 constexpr int RN_MAX_THREADS = 1024;
+constexpr int RN_AHEAD = 12;  // LDS reads in flight ahead of the serial sum (lgkmcnt counts to 15)
 
 __global__ __launch_bounds__(RN_MAX_THREADS) void rmsnorm_q8_1_kernel(
     const float* __restrict__ x, const float* __restrict__ w, float eps, int K,
@@ -69,14 +70,35 @@ __global__ __launch_bounds__(RN_MAX_THREADS) void rmsnorm_q8_1_kernel(
   }
   __syncthreads();
   if (b == 0) {
-    float ss = 0.0f;  // the groups in order, one accumulator
-#pragma unroll 8
-    for (int i = 0; i < nb; ++i) {
-      const float4 g = group_sums[i];
-      ss = ss + g.x;
-      ss = ss + g.y;
-      ss = ss + g.z;
-      ss = ss + g.w;
+    // The groups in order, one accumulator.  The chain of K/8 dependent adds
+    // is the kernel's serial part; the LDS reads run RN_AHEAD blocks ahead of
+    // it (buf[j] holds block i + j) so that no add waits for a read.
+    float ss = 0.0f;
+    float4 buf[RN_AHEAD];
+#pragma unroll
+    for (int j = 0; j < RN_AHEAD; ++j) buf[j] = group_sums[j < nb ? j : nb - 1];
+    int i = 0;
+    for (; i + RN_AHEAD <= nb; i += RN_AHEAD) {
+#pragma unroll
+      for (int j = 0; j < RN_AHEAD; ++j) {
+        const float4 g = buf[j];
+        ss = ss + g.x;
+        ss = ss + g.y;
+        ss = ss + g.z;
+        ss = ss + g.w;
+        const int nx = i + j + RN_AHEAD;
+        buf[j] = group_sums[nx < nb ? nx : nb - 1];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < RN_AHEAD; ++j) {
+      if (j < nb - i) {  // the last nb - i blocks, already in buf
+        const float4 g = buf[j];
+        ss = ss + g.x;
+        ss = ss + g.y;
+        ss = ss + g.z;
+        ss = ss + g.w;
+      }
     }
     const float mean = ss / (float)K;
     r_shared = 1.0f / sqrtf(mean + eps);
