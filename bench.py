@@ -924,6 +924,39 @@ def main():
                          "quantize_us": round(qus, 3) if qus is not None else "in the matmul kernels",
                          "qmatmul": rows}
 
+    # µs per qmatmul for each projection on its own (one launch per matrix,
+    # as `--separate` runs them), beside the grouped launches the step uses.
+    per_proj = None
+    if not prefill and any(len(u) > 1 for M in Ms for _, u in units(M)):
+        per_proj = {}
+        for M in Ms:
+            b = bufs[M]
+            fz = fused(M)
+            row = {}
+            for pi, (name, N, K, t) in enumerate(shapes):
+                src = b["x"][INPUT_OF[name]] if fz else b["xq"][INPUT_OF[name]]
+                fn = lib.qdot_quantize_qmatmul if fz else lib.qdot_qmatmul
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    s_ = torch.cuda.current_stream(dev).cuda_stream
+                    for layer in range(layers):
+                        rc = fn(Wdev[layer][pi].data_ptr(), t, N, K, src.data_ptr(), M, b["y"][name].data_ptr(), s_)
+                        assert rc == 0, rc
+                g.replay()
+                torch.cuda.synchronize()
+                a, bb = ev(), ev()
+                a.record()
+                for _ in range(reps):
+                    g.replay()
+                bb.record()
+                torch.cuda.synchronize()
+                us = a.elapsed_time(bb) * 1e3 / (reps * layers)
+                wb = qd.qdot_weight_bytes(t, N, K)
+                row[name] = {"us": round(us, 3), "pct_hbm_peak": round(100 * wb / us / 1e3 / HBM_PEAK_GBS, 1),
+                             "kernel": (f"qmv_dot4q<{synth.TYPE_NAMES[t]},{M}>" if fz
+                                        else qd.qdot_kernel_name_shape(t, N, K, M))}
+            per_proj[str(M)] = row
+
     # The dominant kernel is the HIP kernel function with the largest share of
     # the step, summed over its template instances (weight types, M tile,
     # prefetch depth): its rate is its algorithmic bytes (or ops) over all its
@@ -1026,6 +1059,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "per_M": per_m,
+        **({"per_projection_single_launch": per_proj} if per_proj else {}),
         **({"shard_tp8_rows": shard} if shard else {}),
         "kernels": kernels,
         "sampled_check": check,

@@ -109,6 +109,24 @@ def test_headline_groups_signed_scales(M):
     check_group(GATE_UP_8B, 4096, M, seed=95 + M, n_oracle_rows=64, signed_scales=True)
 
 
+TP8_FFN = [(1536, synth.Q4_K), (1536, synth.Q4_K)]  # one GPU's gate and up under 8-way TP
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_tp8_shard_shapes_every_row(M):
+    """One GPU's share of the 8B FFN under 8-way tensor parallelism, as the
+    benchmark's shard rows run it: gate+up (2 x 1536 x 4096 Q4_K) grouped and
+    down (4096 x 1536 Q6_K, six superblocks a row) alone; every output
+    against the oracle."""
+    check_group(TP8_FFN, 4096, M, seed=200 + M, n_oracle_rows=None)
+    W = synth.weights(synth.Q6_K, 4096, 1536, (2026, 81, M))
+    x = synth.activations(M, 1536, (2026, 81, 1536, M))
+    xqd, xq = quantize(x)
+    y, _ = qmatmul(to_dev(W), synth.Q6_K, 4096, 1536, xqd, M)
+    y64, _, _ = oracle.qmatmul(W, synth.Q6_K, 4096, 1536, xq, M)
+    assert_close(y, y64, f"down shard 4096x1536 M={M}")
+
+
 @pytest.mark.parametrize("M", [1, 4, 8])
 def test_q4_0_with_q8_0(M):
     check_group([(130, synth.Q4_0), (64, synth.Q8_0), (17, synth.Q4_0)], 768, M, seed=30 + M)
