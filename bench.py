@@ -8,8 +8,9 @@ pass of the whole path for M = 1, 2, 4 and 8 token rows: per layer, four
 activation quantizations (qkv input, o input, gate/up input, down input) and the
 seven qmatmuls.  At M = 1 (--fused-max-m) the quantizations run inside the
 matmul launches (qdot_quantize_qmatmul[_multi], bitwise the same results),
-which measured faster there than a separate quantize launch (except with
-IQ4_XS weights); above it, one quantize launch per input.  Every matrix is cold in the 256 MB Infinity Cache because a
+which measured faster there than a separate quantize launch, except with
+IQ4_XS weights and for launches whose workgroups would repeat more than 4 M
+quantized values (gate+up); elsewhere, one quantize launch per input.  Every matrix is cold in the 256 MB Infinity Cache because a
 36-layer sweep streams 4.4 GB.
 
 Timing: each M's 36-layer sweep is captured once in a HIP graph; the timed
@@ -756,12 +757,23 @@ def main():
     # workloads with IQ4_XS weights keep the separate launch.
     fusable = not prefill and all(t != synth.IQ4_XS for *_, t in shapes)
 
-    def fused(M):
-        """Whether M's launches quantize their activations themselves."""
-        return M <= args.fused_max_m and fusable
+    # Quantizing inside the matmul repeats the work in every workgroup (16
+    # weight rows each): M*K values per workgroup.  Above about 4 M values per
+    # launch that costs more than the separate launch it saves (12288 x 4096
+    # gate+up at M = 1, 6.3 M: 16.1 us against 14.0 + 1.8; down 4096 x 12288,
+    # 3.1 M: 13.7 against 12.5 + 1.8).
+    REDUNDANT_MAX = 4_000_000
+
+    def fused(M, inp):
+        """Whether M's launches reading input `inp` quantize it themselves."""
+        if M > args.fused_max_m or not fusable:
+            return False
+        pis = [pi for pi, (name, *_r) in enumerate(shapes) if INPUT_OF[name] == inp]
+        work = sum((shapes[pi][1] + 15) // 16 * shapes[pi][2] * M for pi in pis)
+        return work <= REDUNDANT_MAX
 
     def unit_kernel(M, pis):
-        if fused(M):
+        if fused(M, INPUT_OF[shapes[pis[0]][0]]):
             names = [f"qmv_dot4q<{synth.TYPE_NAMES[shapes[pi][3]]},{M}>" for pi in pis]
             return names[0] if len(pis) == 1 else "qmv_multi<" + "+".join(names) + ">"
         if len(pis) == 1:
@@ -781,10 +793,10 @@ def main():
         b = bufs[M]
         s = torch.cuda.current_stream(dev).cuda_stream
         us = units(M)
-        fz = fused(M)
         for layer in range(layers):
             for inp, pis in groups:
                 K = shapes[pis[0]][2]
+                fz = fused(M, inp)
                 if not fz and (only is None or only == "quantize"):
                     rc = lib.qdot_quantize_q8_1(b["x"][inp].data_ptr(), M, K, b["xq"][inp].data_ptr(), s)
                     assert rc == 0, rc
@@ -885,7 +897,8 @@ def main():
             Ns = [shapes[pi][1] for pi in upis]
             wb = sum(qd.qdot_weight_bytes(shapes[pi][3], shapes[pi][1], K) for pi in upis)
             # activations read once (fp32 when quantized in the kernel, Q8_1 otherwise), y written once
-            alg = wb + (4 * M * K if fused(M) else qd.qdot_q8_1_bytes(M, K)) + 4 * M * sum(Ns)
+            fz_u = fused(M, INPUT_OF[shapes[upis[0]][0]])
+            alg = wb + (4 * M * K if fz_u else qd.qdot_q8_1_bytes(M, K)) + 4 * M * sum(Ns)
             rows[label] = {"N": Ns[0] if len(Ns) == 1 else Ns, "K": K,
                            "type": "+".join(synth.TYPE_NAMES[shapes[pi][3]] for pi in upis),
                            "us": round(us, 3), "weight_GBps": round(wb / us / 1e3, 1),
@@ -897,9 +910,10 @@ def main():
             e[1] += us * layers * 1e-3
             e[2] += layers
             e[3] += 2 * M * sum(Ns) * K * layers
-        # quantizer (none where the matmul kernels quantize their activations)
+        # quantizer (none for inputs the matmul kernels quantize themselves)
         qus = None
-        if not fused(M):
+        q_inputs = [i for i in inputs if not fused(M, i)]
+        if q_inputs:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 sweep(M, only="quantize")
@@ -911,9 +925,9 @@ def main():
                 g.replay()
             bb.record()
             torch.cuda.synchronize()
-            nq = layers * len(inputs)
+            nq = layers * len(q_inputs)
             qus = a.elapsed_time(bb) * 1e3 / (reps * nq)
-            qbytes = sum(M * in_K[i] * 4 + qd.qdot_q8_1_bytes(M, in_K[i]) for i in inputs) * layers
+            qbytes = sum(M * in_K[i] * 4 + qd.qdot_q8_1_bytes(M, in_K[i]) for i in q_inputs) * layers
             e = kern.setdefault("quantize_q8_1", [0, 0.0, 0, 0])
             e[0] += qbytes
             e[1] += qus * nq * 1e-3
@@ -922,6 +936,7 @@ def main():
         per_m[str(M)] = {"sweep_ms": round(float(np.median(per_m_ms[M])), 4),
                          "sweep_weight_GBps": round(wb_m / (np.median(per_m_ms[M]) * 1e-3) / 1e9, 1),
                          "quantize_us": round(qus, 3) if qus is not None else "in the matmul kernels",
+                         "quantized_in_matmul": [i for i in inputs if fused(M, i)],
                          "qmatmul": rows}
 
     # µs per qmatmul for each projection on its own (one launch per matrix,
@@ -931,9 +946,9 @@ def main():
         per_proj = {}
         for M in Ms:
             b = bufs[M]
-            fz = fused(M)
             row = {}
             for pi, (name, N, K, t) in enumerate(shapes):
+                fz = fused(M, INPUT_OF[name])
                 src = b["x"][INPUT_OF[name]] if fz else b["xq"][INPUT_OF[name]]
                 fn = lib.qdot_quantize_qmatmul if fz else lib.qdot_qmatmul
                 g = torch.cuda.CUDAGraph()
@@ -1050,9 +1065,10 @@ def main():
                    "projections": [f"{n} {N}x{K} {synth.TYPE_NAMES[t]}" for n, N, K, t in shapes],
                    "weight_bytes_per_sweep": wbytes_sweep,
                    "launches_per_step": sum(len(units(M)) for M in Ms) * layers +
-                                        sum(0 if fused(M) else 1 for M in Ms) * layers * len(inputs),
+                                        sum(0 if fused(M, i) else 1 for M in Ms for i in inputs) * layers,
                    "grouped_launches": not args.separate,
-                   "quantized_in_matmul_at_M": [M for M in Ms if fused(M)],
+                   "quantized_in_matmul": {str(M): [i for i in inputs if fused(M, i)] for M in Ms
+                                           if any(fused(M, i) for i in inputs)},
                    **({"same_weights_every_layer": True} if args.same_weights else {})},
         **({"pct_mfma_i8_peak": round(100 * value / MFMA_I8_PEAK_TOPS, 2)} if prefill else
            {"pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1)}),
