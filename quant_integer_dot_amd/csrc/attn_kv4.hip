@@ -176,58 +176,78 @@ __global__ __launch_bounds__(AT_THREADS) void attn_kv4_partial_kernel(
   }
   __syncthreads();
 
-  // P.V: wave w takes tokens 64w .. 64w+63 of the chunk; lane l owns
-  // elements 32b + j and 32b + j + 16 (b = l/16, j = l%16) of every head
+  // P.V: wave w takes tokens 64w .. 64w+63 of the chunk, half-wave hw = l/32
+  // the 32 tokens 64w + 32hw ..; lane l owns elements 32b + 2i, 32b + 2i + 1
+  // (low nibbles of code bytes 2i, 2i+1 of block b) and the same + 16 (high
+  // nibbles), b = (l%32)/8, i = l%8: one fp16 scale and one 16-bit code read
+  // per token for four values
   {
-    const int b = lane >> 4, j = lane & 15;
-    float acc0[G], acc1[G];
+    const int hw = lane >> 5, b = (lane & 31) >> 3, i2 = 2 * (lane & 7);
+    float acc[4][G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) acc0[g] = acc1[g] = 0.0f;
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int g = 0; g < G; ++g) acc[e][g] = 0.0f;
     const uint8_t* vb = reinterpret_cast<const uint8_t*>(v_s);
-    const int tend = min(ntok, 64 * wave + 64);
-    // value pair of token t for this lane (exact: fp16 d times a small integer)
-    auto vpair = [&](int t, float& v0, float& v1) {
+    const int tbeg = 64 * wave + 32 * hw;
+    const int tend = min(ntok, tbeg + 32);
+    // the four values of token t for this lane, exact: d * q - 8 * d = d * (q - 8)
+    // (fp16 d times a 4-bit code is exact in fp32, and so is the fma)
+    auto vquad = [&](int t, float (&v)[4]) {
       const uint8_t* blk = vb + t * AT_ROW + 18 * b;
       const float dv = h2f(*reinterpret_cast<const uint16_t*>(blk));
-      const uint32_t code = blk[2 + j];
-      v0 = dv * (float)((int)(code & 15u) - 8);
-      v1 = dv * (float)((int)(code >> 4) - 8);
+      const uint32_t code = *reinterpret_cast<const uint16_t*>(blk + 2 + i2);
+      const uint32_t lo = code & 0x0F0Fu, hi = (code >> 4) & 0x0F0Fu;
+      const float m8 = -8.0f * dv;
+      v[0] = fmaf(dv, (float)(lo & 0xFFu), m8);   // element 32b + i2
+      v[1] = fmaf(dv, (float)(lo >> 8), m8);      // 32b + i2 + 1
+      v[2] = fmaf(dv, (float)(hi & 0xFFu), m8);   // 32b + 16 + i2
+      v[3] = fmaf(dv, (float)(hi >> 8), m8);      // 32b + 16 + i2 + 1
     };
-    // four tokens a step (their LDS reads issued together; p of the four
-    // tokens in one 16-byte read), the sums still in token order
-    int t = 64 * wave;
+    // four tokens a step (p of the four tokens in one 16-byte read), the sums
+    // in token order
+    int t = tbeg;
     for (; t + 4 <= tend; t += 4) {
-      float v0[4], v1[4];
+      float v[4][4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) vpair(t + u, v0[u], v1[u]);
+      for (int u = 0; u < 4; ++u) vquad(t + u, v[u]);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float4 p4 = *reinterpret_cast<const float4*>(&p_s[g][t]);
-        acc0[g] = fmaf(p4.x, v0[0], acc0[g]);
-        acc1[g] = fmaf(p4.x, v1[0], acc1[g]);
-        acc0[g] = fmaf(p4.y, v0[1], acc0[g]);
-        acc1[g] = fmaf(p4.y, v1[1], acc1[g]);
-        acc0[g] = fmaf(p4.z, v0[2], acc0[g]);
-        acc1[g] = fmaf(p4.z, v1[2], acc1[g]);
-        acc0[g] = fmaf(p4.w, v0[3], acc0[g]);
-        acc1[g] = fmaf(p4.w, v1[3], acc1[g]);
+        const float pu[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e][g] = fmaf(pu[u], v[u][e], acc[e][g]);
       }
     }
     for (; t < tend; ++t) {
-      float v0, v1;
-      vpair(t, v0, v1);
+      float v[4];
+      vquad(t, v);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float p = p_s[g][t];
-        acc0[g] = fmaf(p, v0, acc0[g]);
-        acc1[g] = fmaf(p, v1, acc1[g]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e][g] = fmaf(p, v[e], acc[e][g]);
       }
     }
-    __syncthreads();  // every wave is done with p_s before o_red overwrites it
+    // the two half-waves' partials: first half + second half
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      o_red[wave][g][32 * b + j] = acc0[g];
-      o_red[wave][g][32 * b + j + 16] = acc1[g];
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float other = __shfl_xor(acc[e][g], 32, 64);
+        acc[e][g] = hw == 0 ? acc[e][g] + other : other + acc[e][g];
+      }
+    __syncthreads();  // every wave is done with p_s before o_red overwrites it
+    if (hw == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        o_red[wave][g][32 * b + i2] = acc[0][g];
+        o_red[wave][g][32 * b + i2 + 1] = acc[1][g];
+        o_red[wave][g][32 * b + 16 + i2] = acc[2][g];
+        o_red[wave][g][32 * b + 16 + i2 + 1] = acc[3][g];
+      }
     }
   }
   __syncthreads();

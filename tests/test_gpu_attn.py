@@ -12,8 +12,9 @@ carries the roundings of s_t and of the maxima, two subtractions and two
 expf calls (2 ulp each), at most (6 smax + 6) u relative with smax the
 largest |s_t| of the head, and a relative change e of every weight moves a
 convex combination by at most 2 e A_d; the numerator is summed in chains of
-n_num = 64 (tokens of a wave) + 3 (waves) + ceil(chunks / 16) (partials of a
-residue) + 15 (residues) additions and the denominator in n_den = 6 + 3 +
+n_num = 32 (tokens of a half-wave) + 1 (the two half-waves) + 3 (waves) +
+ceil(chunks / 16) (partials of a residue) + 15 (residues) additions and the
+denominator in n_den = 6 + 3 +
 ceil(chunks / 512) + 6 + 7, each addition adding at most u of the sum of the
 absolute terms; one more rounding for the division.  On top, the RMS over a
 call's outputs of |out - oracle| / A_d must stay under u (4 + sqrt(n_num +
@@ -87,7 +88,7 @@ def check(out, o64, V, scores, Hq, Hkv, where):
     assert not np.isnan(out).any(), f"{where}: output not fully written"
     T = scores.shape[1]
     chunks = -(-T // 256)
-    n_num = 64 + 3 + -(-chunks // 16) + 15
+    n_num = 32 + 1 + 3 + -(-chunks // 16) + 15
     n_den = 6 + 3 + -(-chunks // 512) + 6 + 7
     A, smax = term_scale(V, scores, Hq, Hkv)
     tol = A * U * (2 * (6 * smax[:, None] + 6) + n_num + n_den + 2)
