@@ -208,9 +208,9 @@ template <int T> constexpr int qmm_ring() { return T == Q6_K ? 2 : 4; }  // A-op
 template <int KP> constexpr int qmm_bm() { return 32 * QMM_WAVES / KP; }  // activation rows per workgroup
 
 template <int T, int KP, bool DUMP>
-__global__ __launch_bounds__(64 * QMM_WAVES, (qmm_min_waves<T, KP, DUMP>())) void qmm_mfma_kernel(
-    const uint8_t* __restrict__ W, int N, int K, const uint8_t* __restrict__ xq, int M,
-    float* __restrict__ y, int32_t* __restrict__ isums, int m_tiles, int n_tiles) {
+__device__ __forceinline__ void qmm_split_tile(const uint8_t* __restrict__ W, int N, int K,
+                                               const uint8_t* __restrict__ xq, int M, float* __restrict__ y,
+                                               int32_t* __restrict__ isums, int m_tiles, int n_tiles) {
   using F = QmmFmt<T>;
   constexpr int SUB = Geom<T>::SUB;
   constexpr int BYTES = Geom<T>::BYTES;
@@ -484,6 +484,288 @@ __global__ __launch_bounds__(64 * QMM_WAVES, (qmm_min_waves<T, KP, DUMP>())) voi
       if (m < M && n < N) y[(size_t)m * N + n] = (float)acc[t][r];
     }
   }
+}
+
+// ------------------------------------------------------ Q4_K, 16x16 tiles
+// The same workgroup, K split and weight staging as the tile above, but the
+// block dots come from v_mfma_i32_16x16x32_i8 on 16 x 16 tiles (a wave's 32
+// activation rows x 64 weight rows are 2 x 4 of them), whose result layout
+// lets the Q4_K min term -dmin*m_j*S run on the fp64 matrix cores instead of
+// the VALU: per superblock and tile, two v_mfma_f64_16x16x4_f64 add
+// sum over blocks j of S(m, j) * (-dmin*m_j)(n) straight into the fp64
+// accumulators (every product exact in fp64, as in the VALU form; only the
+// order of the fp64 additions differs).  The VALU keeps d*sc_j*D*I per block
+// and output: one product of the two exact scales, the conversion of I and
+// one fma.  The weight scales d*sc_j and -dmin*m_j of the wave's 64 rows are
+// unpacked once per superblock into a per-wave fp64 table.
+//
+// Lane layouts (measured on gfx950), g4 = lane / 16, c16 = lane % 16:
+//   v_mfma_i32_16x16x32_i8: A = row c16, bytes 8*g4 .. 8*g4+7 of K; B =
+//   column c16, same K bytes; result v of the lane = D[4*g4 + v][c16].
+//   v_mfma_f64_16x16x4_f64: A = row c16, k = g4; B = column c16, k = g4;
+//   result v of the lane = D[g4 + 4*v][c16].
+// So the f64 A operand of lane c16 carries activation row qf_row(c16) =
+// 4*(c16 % 4) + c16 / 4, which puts result v of the lane on row 4*g4 + v,
+// where the integer tile keeps it.
+typedef double v4d __attribute__((ext_vector_type(4)));
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ int qf_row(int c16) { return 4 * (c16 & 3) + (c16 >> 2); }
+
+struct QfW { double w, mn; };  // d*sc_j and -dmin*m_j of one weight row and block
+
+template <int KP> constexpr int qf_lds_bytes() {
+  // per-wave D, S tables [8][32] fp64, the weight stage, per-wave weight scale tables [8][64]
+  return QMM_SCALE_BYTES + qmm_stage_bytes<Q4_K, KP>() + QMM_WAVES * 8 * 64 * 16 > qmm_red_bytes<KP>()
+             ? QMM_SCALE_BYTES + qmm_stage_bytes<Q4_K, KP>() + QMM_WAVES * 8 * 64 * 16
+             : qmm_red_bytes<KP>();
+}
+
+template <int KP, bool DUMP>
+__device__ __forceinline__ void qmm_q4k16_tile(const uint8_t* __restrict__ W, int N, int K,
+                                               const uint8_t* __restrict__ xq, int M, float* __restrict__ y,
+                                               int32_t* __restrict__ isums, int m_tiles, int n_tiles) {
+  constexpr int T = Q4_K;
+  constexpr int BYTES = Geom<T>::BYTES;
+  constexpr int PITCH = qmm_pitch<T>();
+  constexpr int CPR = qmm_cpr<T>();
+  constexpr int CHUNKS = qmm_stage_chunks<T, KP>();
+  constexpr int NCH = qmm_stage_regs<T, KP>();
+  constexpr int RING = 4;
+  static_assert(PITCH == 16 * CPR, "unpadded Q4_K stage");
+  __shared__ __align__(16) double lds_raw[qf_lds_bytes<KP>() / 8];
+  uint8_t* const lds_w = reinterpret_cast<uint8_t*>(lds_raw) + QMM_SCALE_BYTES;
+
+  const int id = blockIdx.x;
+  const int xcd = id % QMM_XCDS, local = id / QMM_XCDS;
+  const int m_tile = local % m_tiles;
+  const int n_tile = (local / m_tiles) * QMM_XCDS + xcd;
+  if (n_tile >= n_tiles) return;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5, c32 = lane & 31, g4 = lane >> 4, c16 = lane & 15;
+  const int kp = wave % KP, wq = wave / KP;
+  const int nsb = K / QK, nq8 = K / Q8_BLOCK;
+  const size_t row_bytes = (size_t)nsb * BYTES;
+  const int m0 = m_tile * qmm_bm<KP>() + 32 * wq;
+  const int n0 = n_tile * QMM_BN;
+
+  // Per-wave tables: activation D and S of the wave's 32 rows, [block][row];
+  // weight scales of its 64 rows, [block][row].
+  double(*const Dt)[32] = reinterpret_cast<double(*)[32]>(lds_raw + wave * 512);
+  double(*const St)[32] = reinterpret_cast<double(*)[32]>(lds_raw + wave * 512 + 256);
+  QfW(*const Wt)[64] = reinterpret_cast<QfW(*)[64]>(
+      reinterpret_cast<uint8_t*>(lds_raw) + QMM_SCALE_BYTES + qmm_stage_bytes<T, KP>() + wave * 8 * 64 * 16);
+
+  // Activation rows of this lane: A operand rows 16*tm + c16 (clamped to the
+  // last row past M; never stored) and the scale staging row c32.
+  const uint8_t* xr[2];
+#pragma unroll
+  for (int tm = 0; tm < 2; ++tm) {
+    const int m = m0 + 16 * tm + c16 < M ? m0 + 16 * tm + c16 : M - 1;
+    xr[tm] = xq + (size_t)m * nq8 * Q8_BYTES;
+  }
+  const int ms = m0 + c32 < M ? m0 + c32 : M - 1;
+  const uint8_t* xs = xq + (size_t)ms * nq8 * Q8_BYTES;
+  // Weight rows of this lane in K slice kp: B operand rows 16*tn + c16, and
+  // row `lane` for the scale table.
+  const uint8_t* wl[4];
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn) wl[tn] = lds_w + (size_t)(kp * QMM_BN + 16 * tn + c16) * PITCH;
+  const uint8_t* wh = lds_w + (size_t)(kp * QMM_BN + lane) * PITCH;
+
+  auto stage_load = [&](int it, u32x4 (&breg)[NCH]) {
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int iu = tid + 64 * QMM_WAVES * u;
+      const int i = iu < CHUNKS ? iu : CHUNKS - 1;
+      const int sl = i / (QMM_BN * CPR), rem = i % (QMM_BN * CPR);
+      const int r = rem / CPR, c = rem % CPR;
+      const int n = n0 + r < N ? n0 + r : N - 1;
+      int bb = sl + KP * it;
+      bb = bb < nsb ? bb : nsb - 1;
+      breg[u] = ld16(W + (size_t)n * row_bytes + (size_t)bb * BYTES + 16 * c);
+    }
+  };
+  auto stage_store = [&](const u32x4 (&breg)[NCH]) {
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int i = tid + 64 * QMM_WAVES * u;
+      if (i < CHUNKS) *reinterpret_cast<u32x4*>(lds_w + 16 * i) = breg[u];
+    }
+  };
+  // A operand of block j of superblock b: 8 bytes of rows 16*tm + c16.
+  auto load_a = [&](int b, int j) {
+    const size_t o = (size_t)(b * 8 + j) * Q8_BYTES + 4 + 8 * g4;
+    const u32x2 a0 = ld8(xr[0] + o), a1 = ld8(xr[1] + o);
+    return u32x4{a0.x, a0.y, a1.x, a1.y};
+  };
+  auto load_ds = [&](int b, uint32_t* ds) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ds[u] = ld4(xs + (size_t)(b * 8 + 4 * g + u) * Q8_BYTES);
+  };
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  v4d acc[2][4];
+#pragma unroll
+  for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = v4d{0.0, 0.0, 0.0, 0.0};
+
+  const int nit = (nsb + KP - 1) / KP;
+  const int b0 = kp < nsb ? kp : nsb - 1;
+  u32x4 breg[NCH];
+  stage_load(0, breg);
+  uint32_t ds_next[4];
+  load_ds(b0, ds_next);
+  u32x4 ring[RING];
+#pragma unroll
+  for (int j = 0; j < RING - 1; ++j) ring[j] = load_a(b0, j);
+  stage_store(breg);
+  __syncthreads();
+
+#pragma unroll 1
+  for (int it = 0; it < nit; ++it) {
+    const int b = kp + KP * it;
+    const int bn = b + KP < nsb ? b + KP : nsb - 1;
+    const bool more = it + 1 < nit;
+    stage_load(it + 1, breg);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      Dt[4 * g + u][c32] = (double)h2f(ds_next[u] & 0xFFFFu);
+      St[4 * g + u][c32] = (double)h2f(ds_next[u] >> 16);
+    }
+    load_ds(bn, ds_next);
+    {  // weight scales of row `lane`, all eight blocks
+      const u32x4 h = ld16(wh);
+      const float dw = h2f(h.x), dm = h2f(h.x >> 16);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t sc, mm;
+        q4k_scale_min(h, j, sc, mm);
+        Wt[j][lane] = QfW{(double)(dw * (float)sc), -(double)(dm * (float)mm)};
+      }
+    }
+    wave_sync();
+
+    if (b < nsb) {
+      auto do_block = [&](auto JC) {
+        constexpr int J = decltype(JC)::value;
+        constexpr int JN = J + RING - 1;
+        __builtin_amdgcn_sched_barrier(0);
+        ring[JN % RING] = JN < 8 ? load_a(b, JN) : load_a(bn, JN - 8);
+        const u32x4 oa = ring[J % RING];
+        const long a0 = (long)((uint64_t)oa.x | ((uint64_t)oa.y << 32));
+        const long a1 = (long)((uint64_t)oa.z | ((uint64_t)oa.w << 32));
+        v4i_t I[2][4];
+        double w[4];
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) {
+          const u32x2 q = *reinterpret_cast<const u32x2*>(wl[tn] + 16 + 32 * (J >> 1) + 8 * g4);
+          constexpr int sh = (J & 1) ? 4 : 0;
+          const long bq = (long)((uint64_t)((q.x >> sh) & 0x0F0F0F0Fu) |
+                                 ((uint64_t)((q.y >> sh) & 0x0F0F0F0Fu) << 32));
+          const v4i_t z = {0, 0, 0, 0};
+          I[0][tn] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a0, bq, z, 0, 0, 0);
+          I[1][tn] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a1, bq, z, 0, 0, 0);
+          w[tn] = Wt[J][16 * tn + c16].w;
+        }
+        {  // two of the superblock's sixteen min-term MFMAs: blocks 4*kc + g4 of tile (tmm, tn)
+          constexpr int kc = J / 4, tmm = (J / 2) % 2;
+          const double sa = St[4 * kc + g4][16 * tmm + qf_row(c16)];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int tn = 2 * (J % 2) + e;
+            acc[tmm][tn] = __builtin_amdgcn_mfma_f64_16x16x4f64(sa, Wt[4 * kc + g4][16 * tn + c16].mn, acc[tmm][tn], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int tm = 0; tm < 2; ++tm) {
+          const double* dp = &Dt[J][16 * tm + 4 * g4];
+          const double dv[4] = {dp[0], dp[1], dp[2], dp[3]};
+#pragma unroll
+          for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              acc[tm][tn][v] = fma(w[tn] * dv[v], (double)I[tm][tn][v], acc[tm][tn][v]);  // exact product
+              if (DUMP) {
+                const int m = m0 + 16 * tm + 4 * g4 + v, n = n0 + 16 * tn + c16;
+                if (m < M && n < N) isums[((size_t)m * N + n) * (K / 32) + (size_t)b * 8 + J] = I[tm][tn][v];
+              }
+            }
+        }
+      };
+      do_block(std::integral_constant<int, 0>{});
+      do_block(std::integral_constant<int, 1>{});
+      do_block(std::integral_constant<int, 2>{});
+      do_block(std::integral_constant<int, 3>{});
+      do_block(std::integral_constant<int, 4>{});
+      do_block(std::integral_constant<int, 5>{});
+      do_block(std::integral_constant<int, 6>{});
+      do_block(std::integral_constant<int, 7>{});
+    }
+    if (more) {
+      __syncthreads();
+      stage_store(breg);
+      __syncthreads();
+    }
+  }
+
+  if constexpr (KP > 1) {
+    __syncthreads();
+    double* red = lds_raw;
+    auto slot = [&](int q, int k, int tm, int tn, int v) {
+      return (((((q * (KP - 1) + (k - 1)) * 2 + tm) * 4 + tn) * 4 + v) * 64) + lane;
+    };
+    if (kp > 0) {
+#pragma unroll
+      for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) red[slot(wq, kp, tm, tn, v)] = acc[tm][tn][v];
+    }
+    __syncthreads();
+    if (kp > 0) return;
+#pragma unroll 1
+    for (int k = 1; k < KP; ++k)
+#pragma unroll
+      for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[tm][tn][v] += red[slot(wq, k, tm, tn, v)];
+  }
+
+#pragma unroll
+  for (int tm = 0; tm < 2; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+      const int n = n0 + 16 * tn + c16;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + 16 * tm + 4 * g4 + v;
+        if (m < M && n < N) y[(size_t)m * N + n] = (float)acc[tm][tn][v];
+      }
+    }
+}
+
+constexpr bool QMM_Q4K16 = true;  // Q4_K on the 16x16 tile
+
+template <int T, int KP, bool DUMP> constexpr int qmm_occupancy() {
+  if constexpr (T == Q4_K && QMM_Q4K16) return !DUMP && qf_lds_bytes<KP>() <= 80 * 1024 ? 2 : 1;
+  else return qmm_min_waves<T, KP, DUMP>();
+}
+
+template <int T, int KP, bool DUMP>
+__global__ __launch_bounds__(64 * QMM_WAVES, (qmm_occupancy<T, KP, DUMP>())) void qmm_mfma_kernel(
+    const uint8_t* __restrict__ W, int N, int K, const uint8_t* __restrict__ xq, int M,
+    float* __restrict__ y, int32_t* __restrict__ isums, int m_tiles, int n_tiles) {
+  if constexpr (T == Q4_K && QMM_Q4K16) qmm_q4k16_tile<KP, DUMP>(W, N, K, xq, M, y, isums, m_tiles, n_tiles);
+  else qmm_split_tile<T, KP, DUMP>(W, N, K, xq, M, y, isums, m_tiles, n_tiles);
 }
 
 // K split: 2 or 4 waves per output tile, from N and K only (never M), so
