@@ -69,6 +69,8 @@ def parse():
                         "(qdot_quantize_qmatmul[_multi]) instead of a separate quantize launch; 0 = never")
     p.add_argument("--no-shard-rows", action="store_true",
                    help="skip the tensor-parallel share rows of the decode workload")
+    p.add_argument("--no-prefill-row", action="store_true",
+                   help="skip the M = 512 prefill row of the decode workload")
     p.add_argument("--separate", action="store_true",
                    help="one launch per projection (default: projections sharing an input in one "
                         "qdot_qmatmul_multi launch for M <= 8)")
@@ -437,6 +439,69 @@ def shard_rows(dev, fused_max_m, reps, per_m_full, check=True):
         res["sampled_check"] = {"outputs_checked": nchk, "outside_1e-5_rel": bad}
         if bad:
             log(f"[bench] SHARD ROWS CHECK FAILED: {bad} of {nchk} outputs")
+    return res
+
+
+def prefill_row(dev, Wdev, shapes, cfg_idx, layers, reps, check=True):
+    """The M = 512 prefill sweep on the decode line's resident weights (the
+    same 36 Qwen3-8B layers): one quantize launch per input and layer, then
+    one qdot_qmatmul per projection, captured in a graph and replayed between
+    HIP events; int8 TOP/s against the MFMA int8 peak, with a sampled oracle
+    check of the last layer."""
+    import numpy as np
+    import torch
+    from quant_integer_dot_amd import binding as qd
+    from quant_integer_dot_amd import synth
+
+    M = 512
+    inputs = sorted({INPUT_OF[name] for name, *_ in shapes})
+    in_K = {INPUT_OF[name]: K for name, N, K, t in shapes}
+    xs = {i: torch.from_numpy(synth.activations(M, in_K[i], synth.act_seed(cfg_idx, in_K[i], M))).to(dev)
+          for i in inputs}
+    xqs = {i: torch.empty(qd.qdot_q8_1_bytes(M, in_K[i]), dtype=torch.uint8, device=dev) for i in inputs}
+    ys = {name: torch.empty((M, N), dtype=torch.float32, device=dev) for name, N, K, t in shapes}
+
+    def sweep():
+        for layer in range(layers):
+            for i in inputs:
+                qd.qdot_quantize_q8_1(xs[i], M, in_K[i], xqs[i])
+                for pi, (name, N, K, t) in enumerate(shapes):
+                    if INPUT_OF[name] == i:
+                        qd.qdot_qmatmul(Wdev[layer][pi], t, N, K, xqs[i], M, ys[name])
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sweep()
+    g.replay()
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    a, b = ev(), ev()
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    ops = sum(2 * M * N * K for _, N, K, _ in shapes) * layers
+    tops = ops / (ms * 1e-3) / 1e12
+    res = {"what": "M = 512 prefill sweep over the same resident weights (quantize launches included)",
+           "M": M, "ms_per_sweep": round(ms, 3), "int8_TOPs": round(tops, 1),
+           "pct_mfma_i8_peak": round(100 * tops / MFMA_I8_PEAK_TOPS, 2),
+           "kernels": sorted({qd.qdot_kernel_name_shape(t, N, K, M) for _, N, K, t in shapes})}
+    if check:
+        import oracle
+        bad = nchk = 0
+        for pi, (name, N, K, t) in enumerate(shapes):
+            Wh = synth.weights(t, N, K, synth.weight_seed(cfg_idx, layers - 1, pi))
+            xq = oracle.quantize_q8_1(xs[INPUT_OF[name]].cpu().numpy())
+            r = np.random.default_rng(900 + pi).integers(0, N, 4)
+            y64, _ = oracle.qmatmul_rows(Wh, t, N, K, xq, M, r)
+            yg = ys[name].cpu().numpy()[:, r].astype(np.float64)
+            bad += int((np.abs(yg - y64) > 1e-5 * np.abs(y64)).sum())
+            nchk += y64.size
+        res["sampled_check"] = {"outputs_checked": nchk, "outside_1e-5_rel": bad}
+        if bad:
+            log(f"[bench] PREFILL ROW CHECK FAILED: {bad} of {nchk} outputs")
     return res
 
 
@@ -1036,6 +1101,11 @@ def main():
     shard = None
     if args.workload == "qwen3-8b-decode" and not args.no_shard_rows:
         shard = shard_rows(dev, args.fused_max_m, reps, per_m, check=not args.no_check)
+    pre_row = None
+    if args.workload == "qwen3-8b-decode" and not args.no_prefill_row and not args.same_weights:
+        pre_row = prefill_row(dev, Wdev, shapes, cfg_idx, layers, reps, check=not args.no_check)
+        log(f"[bench] prefill row: {pre_row['ms_per_sweep']} ms per M = 512 sweep, "
+            f"{pre_row['int8_TOPs']} int8 TOP/s ({pre_row['pct_mfma_i8_peak']} % of peak)")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -1077,6 +1147,7 @@ def main():
         "per_M": per_m,
         **({"per_projection_single_launch": per_proj} if per_proj else {}),
         **({"shard_tp8_rows": shard} if shard else {}),
+        **({"prefill_512_row": pre_row} if pre_row else {}),
         "kernels": kernels,
         "sampled_check": check,
     }

@@ -21,6 +21,17 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU only" in r.stdout + r.stderr
 
 
+def test_extra_rows_of_the_default_line_can_be_skipped(monkeypatch):
+    """The default decode line carries the shard rows and the M = 512 prefill
+    row; profiling runs switch each off, and the defaults keep both on."""
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    a = bench.parse()
+    assert a.workload == "qwen3-8b-decode" and not a.no_shard_rows and not a.no_prefill_row
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--no-shard-rows", "--no-prefill-row"])
+    a = bench.parse()
+    assert a.no_shard_rows and a.no_prefill_row
+
+
 @pytest.mark.parametrize("name", ["qwen3-8b-decode", "qwen3-8b-prefill-512", "iq4xs-h5120-decode",
                                   "qwen2.5-1.5b-decode", "qwen3-8b-q4_0-q8_0-decode", "qwen3-8b-mid-batch",
                                   "qwen3-8b-tp8-shard-decode"])
