@@ -111,7 +111,8 @@ int qdot_quantize_q8_1(const float *x, int64_t M, int64_t K, void *x_q8,
  *   Q4_0, Q8_0  d*D*I  (d the block's own scale; Q4_0 codes are q-8)
  * where I is the exact integer dot of the sub-block's weight codes with the
  * int8 activations and D, S are the activation block's fp16 d and s.  Every
- * scale product is exact and accumulated in fp64; y is rounded once to fp32.
+ * scale product is exact and accumulated in fp64 (in the prefill kernel the
+ * Q4_K min terms on the fp64 matrix cores); y is rounded once to fp32.
  * M <= 8 runs the decode kernel (v_dot4_i32_i8, M-row tile; for Q4_K at
  * M = 7, 8 and IQ4_XS at M = 5..8 the integer dots run on
  * v_mfma_i32_32x32x32_i8 instead, summed in the same order, so the rows are
