@@ -115,7 +115,8 @@ int qdot_quantize_q8_1(const float *x, int64_t M, int64_t K, void *x_q8,
  * Q4_K min terms on the fp64 matrix cores); y is rounded once to fp32.
  * M <= 8 runs the decode kernel (v_dot4_i32_i8, M-row tile; for Q4_K at
  * M = 7, 8 and IQ4_XS at M = 5..8 the integer dots run on
- * v_mfma_i32_32x32x32_i8 instead, summed in the same order, so the rows are
+ * v_mfma_i32_32x32x32_i8 instead, and for Q6_K at M = 7, 8 on
+ * v_mfma_i32_16x16x32_i8, summed in the same order, so the rows are
  * bitwise those of the dot4 tile); Q4_K and IQ4_XS keep that MFMA decode
  * tile, with 16-row activation slots, up to M = 16.  Above the decode range
  * and up to M = 96 runs a mid-batch MFMA i8 kernel (16-row activation tiles,

@@ -225,7 +225,7 @@ const char* qdot_kernel_name(int type, int64_t M) {
       {"qmv_dot4<Q4_K,1>", "qmv_dot4<Q4_K,2>", "qmv_dot4<Q4_K,3>", "qmv_dot4<Q4_K,4>",
        "qmv_dot4<Q4_K,5>", "qmv_dot4<Q4_K,6>", "qmv_mfma<Q4_K,7>", "qmv_mfma<Q4_K,8>"},
       {"qmv_dot4<Q6_K,1>", "qmv_dot4<Q6_K,2>", "qmv_dot4<Q6_K,3>", "qmv_dot4<Q6_K,4>",
-       "qmv_dot4<Q6_K,5>", "qmv_dot4<Q6_K,6>", "qmv_dot4<Q6_K,7>", "qmv_dot4<Q6_K,8>"},
+       "qmv_dot4<Q6_K,5>", "qmv_dot4<Q6_K,6>", "qmv_mfma<Q6_K,7>", "qmv_mfma<Q6_K,8>"},
       {"qmv_dot4<IQ4_XS,1>", "qmv_dot4<IQ4_XS,2>", "qmv_dot4<IQ4_XS,3>", "qmv_dot4<IQ4_XS,4>",
        "qmv_mfma<IQ4_XS,5>", "qmv_mfma<IQ4_XS,6>", "qmv_mfma<IQ4_XS,7>", "qmv_mfma<IQ4_XS,8>"},
       {"qmv_dot4<Q4_0,1>", "qmv_dot4<Q4_0,2>", "qmv_dot4<Q4_0,3>", "qmv_dot4<Q4_0,4>",
@@ -263,7 +263,7 @@ const char* qdot_multi_kernel_name(int n, const int* types, const int64_t* N, in
       {"qmv_dot4<Q4_K,1>", "qmv_dot4<Q4_K,2>", "qmv_dot4<Q4_K,3>", "qmv_dot4<Q4_K,4>",
        "qmv_dot4<Q4_K,5>", "qmv_dot4<Q4_K,6>", "qmv_dot4<Q4_K,7>", "qmv_dot4<Q4_K,8>"},
       {"qmv_dot4<Q6_K,1>", "qmv_dot4<Q6_K,2>", "qmv_dot4<Q6_K,3>", "qmv_dot4<Q6_K,4>",
-       "qmv_dot4<Q6_K,5>", "qmv_dot4<Q6_K,6>", "qmv_dot4<Q6_K,7>", "qmv_dot4<Q6_K,8>"},
+       "qmv_dot4<Q6_K,5>", "qmv_dot4<Q6_K,6>", "qmv_mfma<Q6_K,7>", "qmv_mfma<Q6_K,8>"},
       {"qmv_dot4<IQ4_XS,1>", "qmv_dot4<IQ4_XS,2>", "qmv_dot4<IQ4_XS,3>", "qmv_dot4<IQ4_XS,4>",
        "qmv_dot4<IQ4_XS,5>", "qmv_dot4<IQ4_XS,6>", "qmv_dot4<IQ4_XS,7>", "qmv_dot4<IQ4_XS,8>"},
       {"qmv_dot4<Q4_0,1>", "qmv_dot4<Q4_0,2>", "qmv_dot4<Q4_0,3>", "qmv_dot4<Q4_0,4>",

@@ -474,6 +474,196 @@ __device__ __forceinline__ void qmv_tile(const uint8_t* __restrict__ W, int N, i
   reduce_store<M, 1>(acc2, reinterpret_cast<double*>(smem), P, wave, slot, q, tid, n0, N, y);
 }
 
+// ------------------------------------------ Q6_K on 16 x 16 MFMA tiles
+//
+// Q6_K at M >= Q6F_MIN_M: the same workgroup (16 weight rows), K split,
+// activation staging and summation order as qmv_tile, but the integer dots
+// come from one v_mfma_i32_16x16x32_i8 per Q8_1 block.  At M = 8 qmv_tile's
+// 16 row slots each read all 8*M staged activation blocks of a superblock
+// from LDS; here a lane reads 8 bytes per block.
+//
+// Lane l (c16 = l % 16, g4 = l / 16) supplies B = the signed codes of weight
+// row c16, elements 8*g4 .. 8*g4+7 of the block, and A row c16, which holds
+// activation row c16 / 2 in "slot" c16 % 2: slot 0 carries elements 0-15 of
+// the block (the first 16-element sub-block) and zeros for 16-31, slot 1 the
+// reverse, so one MFMA gives both sub-block sums.  Result v of lane l is
+// D[4*g4 + v][c16] (gfx950 layout): the sums I0 (v = 2k) and I1 (v = 2k+1)
+// of activation row 2*g4 + k.  The lane drains d*D*(s0*I0 + s1*I1) -- the
+// same exact integer and the same fp64 fma as qmv_tile (whose -32 code
+// offset goes through the activation sums instead) -- into per-quarter
+// accumulators in qmv_tile's block order, then adds the quarters as
+// qmv_tile's quad reduction does, and the waves are added in order: every
+// output is bitwise qmv_tile's.
+constexpr int Q6F_MIN_M = 7;
+template <int T, int M> constexpr bool q6f_ok() { return T == Q6_K && M >= Q6F_MIN_M && M <= 8; }
+
+template <int M, int DEPTH, bool DUMP>
+__device__ __forceinline__ void q6f_tile(const uint8_t* __restrict__ W, int N, int K,
+                                         const uint8_t* __restrict__ xq, float* __restrict__ y,
+                                         int32_t* __restrict__ isums, int tile, uint8_t* smem) {
+  typedef int v4i_q __attribute__((ext_vector_type(4)));
+  constexpr int BYTES = Geom<Q6_K>::BYTES;
+  constexpr int ITEMS = 8 * M;
+  const int P = blockDim.x >> 6;
+  const int nsb = K / QK;
+  const int nq8 = K / Q8_BLOCK;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int n0 = tile * QMV_SLOTS;
+
+  // the wave's LDS slice (qmv_tile's size): the codes of activation row m at
+  // m * Q6F_APITCH (the 32 distinct 8-byte A reads of a block on distinct
+  // banks; a 256-byte row pitch would put all eight rows on the same ones),
+  // then the fp64 D of each block
+  constexpr int Q6F_APITCH = 8 * Q8_BLOCK + 32;
+  static_assert(M * Q6F_APITCH + ITEMS * 8 <= ITEMS * (Q8_BLOCK + (int)sizeof(DsEntry)), "slice size");
+  uint8_t* lds_x = smem + (size_t)wave * ITEMS * (Q8_BLOCK + sizeof(DsEntry));
+  double* lds_d = reinterpret_cast<double*>(lds_x + M * Q6F_APITCH);
+
+  const int nrow = n0 + c16;
+  const uint8_t* wrow = W + (size_t)(nrow < N ? nrow : N - 1) * nsb * BYTES;
+  const int item = lane % ITEMS;
+  const uint8_t* xsrc = xq + ((size_t)(item >> 3) * nq8 + (item & 7)) * Q8_BYTES;
+  // A row of this lane: activation row am = c16 / 2 in slot c16 % 2; zero
+  // where the lane's K-slice is not in its slot's sub-block or am >= M
+  const int am = c16 >> 1;
+  const bool a_on = (g4 >> 1) == (c16 & 1) && am < M;
+  const uint8_t* a_src = lds_x + (size_t)(am < M ? am : 0) * Q6F_APITCH + 8 * g4;
+
+  // activation rows 2*g4 + k (k = 0, 1) of this lane's results (clamped into
+  // the staged rows; rows >= M are never stored)
+  int dm[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) dm[k] = 2 * g4 + k < M ? 2 * g4 + k : 0;
+
+  double acc[4][2];  // [quarter][k]
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) acc[q][k] = 0.0;
+
+  // weights: K-slice g4 of every block of the row -- ql bytes 8*g4 .. +7 of
+  // each 32-byte run of both halves, qh bytes 8*g4 .. +7 of each half --
+  // plus the sub-scales and d; activations: one Q8_1 block per lane, as qmv_tile
+  struct Stage { u32x2 l0[2], l1[2], qh[2]; u32x4 sc; uint32_t d; uint32_t ds; u32x4 c0, c1; };
+  Stage S[DEPTH];
+  auto fetch = [&](Stage& st, int bsb) {
+    const int bc = bsb < nsb ? bsb : nsb - 1;
+    const uint8_t* sb = wrow + (size_t)bc * BYTES;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      st.l0[h] = ld8(sb + 64 * h + 8 * g4);
+      st.l1[h] = ld8(sb + 64 * h + 32 + 8 * g4);
+      st.qh[h] = ld8(sb + 128 + 32 * h + 8 * g4);
+    }
+    st.sc = ld16(sb + 192);
+    unsigned short dh;
+    __builtin_memcpy(&dh, sb + 208, 2);
+    st.d = dh;
+    const uint8_t* src = xsrc + (size_t)bc * 8 * Q8_BYTES;
+    st.ds = ld4(src);
+    st.c0 = ld16(src + 4);
+    st.c1 = ld16(src + 20);
+  };
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  auto compute = [&](const Stage& st, int b) {
+    wave_sync();  // the previous superblock's LDS reads are done
+    if (lane < ITEMS) {
+      uint8_t* dst = lds_x + (item >> 3) * Q6F_APITCH + (item & 7) * Q8_BLOCK;
+      *reinterpret_cast<u32x4*>(dst) = st.c0;
+      *reinterpret_cast<u32x4*>(dst + 16) = st.c1;
+      lds_d[item] = (double)h2f(st.ds & 0xFFFFu);
+    }
+    wave_sync();
+    const double dw = (double)h2f(st.d);
+    // all eight blocks' MFMAs first, then the drains; no branch splits the
+    // superblock (rows >= M drain clamped copies that are never stored)
+    v4i_q I[8];
+    auto mfma_block = [&](auto JC) {
+      constexpr int J = decltype(JC)::value;
+      constexpr int h = J >> 2, g6 = J & 3;
+      const u32x2 src = (g6 & 1) ? st.l1[h] : st.l0[h];
+      const uint32_t bx = q6k_signed(q6k_code<(g6 >= 2)>(src.x, st.qh[h].x, g6 & 1));
+      const uint32_t by = q6k_signed(q6k_code<(g6 >= 2)>(src.y, st.qh[h].y, g6 & 1));
+      const long bq = (long)((uint64_t)bx | ((uint64_t)by << 32));
+      const u32x2 av = *reinterpret_cast<const u32x2*>(a_src + J * Q8_BLOCK);
+      const long aq = a_on ? (long)((uint64_t)av.x | ((uint64_t)av.y << 32)) : 0L;
+      const v4i_q z = {0, 0, 0, 0};
+      I[J] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aq, bq, z, 0, 0, 0);
+    };
+    auto drain_block = [&](auto JC) {
+      constexpr int J = decltype(JC)::value;
+      constexpr int q = 2 * (J >> 2) + (J & 1);  // qmv_tile's quarter of block J
+      const uint32_t scw = (J < 2 ? st.sc.x : (J < 4 ? st.sc.y : (J < 6 ? st.sc.z : st.sc.w))) >> (16 * (J & 1));
+      const int s0 = (int)(int8_t)scw, s1 = (int)(int8_t)(scw >> 8);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int I0 = I[J][2 * k], I1 = I[J][2 * k + 1];  // sub-blocks 2J, 2J+1 of row 2*g4 + k
+        const int Pq = q6k_pair(s0, I0, s1, I1);  // exact int
+        acc[q][k] = fma(dw * lds_d[dm[k] * 8 + J], (double)Pq, acc[q][k]);
+        if (DUMP && 2 * g4 + k < M && nrow < N) {
+          int32_t* p = isums + ((size_t)(2 * g4 + k) * N + nrow) * (K / 16) + (size_t)b * 16 + 2 * J;
+          p[0] = I0;
+          p[1] = I1;
+        }
+      }
+    };
+    mfma_block(std::integral_constant<int, 0>{});
+    mfma_block(std::integral_constant<int, 1>{});
+    mfma_block(std::integral_constant<int, 2>{});
+    mfma_block(std::integral_constant<int, 3>{});
+    mfma_block(std::integral_constant<int, 4>{});
+    mfma_block(std::integral_constant<int, 5>{});
+    mfma_block(std::integral_constant<int, 6>{});
+    mfma_block(std::integral_constant<int, 7>{});
+    drain_block(std::integral_constant<int, 0>{});
+    drain_block(std::integral_constant<int, 1>{});
+    drain_block(std::integral_constant<int, 2>{});
+    drain_block(std::integral_constant<int, 3>{});
+    drain_block(std::integral_constant<int, 4>{});
+    drain_block(std::integral_constant<int, 5>{});
+    drain_block(std::integral_constant<int, 6>{});
+    drain_block(std::integral_constant<int, 7>{});
+  };
+
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) fetch(S[d], wave + d * P);
+  const int niter = (((nsb + P - 1) / P) + DEPTH - 1) / DEPTH * DEPTH;
+  auto step = [&](Stage& st, int ii, bool refill) {
+    const int b = wave + ii * P;
+    if (b < nsb) compute(st, b);
+    if (refill) fetch(st, b + DEPTH * P);
+  };
+  int i = 0;
+  for (; i + DEPTH < niter; i += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) step(S[d], i + d, true);
+  }
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) step(S[d], i + d, false);
+
+  // quarters as qmv_tile's quad reduction adds them, then the waves in order
+  __syncthreads();  // the staging area is reused for the reduction
+  double* red = reinterpret_cast<double*>(smem);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int m = 2 * g4 + k;
+    if (m < M) red[(wave * QMV_SLOTS + c16) * M + m] = (acc[0][k] + acc[1][k]) + (acc[2][k] + acc[3][k]);
+  }
+  __syncthreads();
+  for (int o = tid; o < QMV_SLOTS * M; o += 64 * P) {
+    const int m = o % M, sl = o / M;
+    const int n = n0 + sl;
+    double v = red[sl * M + m];
+    for (int w = 1; w < P; ++w) v += red[(w * QMV_SLOTS + sl) * M + m];
+    if (n < N) y[(size_t)m * N + n] = (float)v;
+  }
+}
+
 // ------------------------------------------ the MFMA tile for M = 7, 8
 //
 // The same sums as qmv_tile, in the same fp64 order, with the integer dots
@@ -862,6 +1052,8 @@ __global__ __launch_bounds__(QMV_MAX_THREADS) void qmv_kernel(
     qmf16_tile<T, M, DEPTH, DUMP>(W, N, K, xq, y, isums, blockIdx.x, smem);
   else if constexpr (qmf_ok<T, M>())
     qmf_tile<T, M, DEPTH, DUMP>(W, N, K, xq, y, isums, blockIdx.x, smem);
+  else if constexpr (q6f_ok<T, M>())
+    q6f_tile<M, DEPTH, DUMP>(W, N, K, xq, y, isums, blockIdx.x, smem);
   else
     qmv_tile<T, M, DEPTH, DUMP>(W, N, K, xq, y, isums, blockIdx.x, smem);
 }
@@ -897,11 +1089,15 @@ __global__ __launch_bounds__(QMV_MAX_THREADS) void qmv_multi_kernel(QmvMulti a, 
   if (TA == TB || a.type[i] == TA) {
     if constexpr (qmf_group_ok<TA, M, MF>())
       qmf_tile<TA, M, DEPTH, false>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
+    else if constexpr (!XF && q6f_ok<TA, M>())
+      q6f_tile<M, DEPTH, false>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
     else
       qmv_tile<TA, M, DEPTH, false, XF>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
   } else {
     if constexpr (qmf_group_ok<TB, M, MF>())
       qmf_tile<TB, M, DEPTH, false>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
+    else if constexpr (!XF && q6f_ok<TB, M>())
+      q6f_tile<M, DEPTH, false>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
     else
       qmv_tile<TB, M, DEPTH, false, XF>(a.W[i], a.N[i], K, xq, a.y[i], nullptr, tile, smem);
   }

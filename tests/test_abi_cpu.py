@@ -52,7 +52,9 @@ def test_sizes(lib):
 def test_names_and_status(lib):
     assert qd.qdot_kernel_name(qd.QDOT_Q4_K, 8) == "qmv_mfma<Q4_K,8>"
     assert qd.qdot_kernel_name(qd.QDOT_Q4_K, 6) == "qmv_dot4<Q4_K,6>"
-    assert qd.qdot_kernel_name(qd.QDOT_Q6_K, 8) == "qmv_dot4<Q6_K,8>"
+    assert qd.qdot_kernel_name(qd.QDOT_Q6_K, 8) == "qmv_mfma<Q6_K,8>"
+    assert qd.qdot_kernel_name(qd.QDOT_Q6_K, 7) == "qmv_mfma<Q6_K,7>"
+    assert qd.qdot_kernel_name(qd.QDOT_Q6_K, 6) == "qmv_dot4<Q6_K,6>"
     assert qd.qdot_kernel_name(qd.QDOT_IQ4_XS, 5) == "qmv_mfma<IQ4_XS,5>"
     assert qd.qdot_kernel_name(qd.QDOT_IQ4_XS, 4) == "qmv_dot4<IQ4_XS,4>"
     assert qd.qdot_kernel_name(qd.QDOT_IQ4_XS, 1) == "qmv_dot4<IQ4_XS,1>"
