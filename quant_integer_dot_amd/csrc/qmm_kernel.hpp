@@ -5,8 +5,10 @@
 // weight codes with the Q8_1 activations, then exact-term fp64 scale drains
 // (Kestrel section 5: exact int32 inside the block, scales after) -- but the
 // block dots of a 32 x 32 output tile come from one MFMA per 32-element
-// block: v_mfma_i32_32x32x32_i8 for Q4_K and IQ4_XS (one MFMA = one
+// block: v_mfma_i32_32x32x32_i8 for IQ4_XS, Q4_0 and Q8_0 (one MFMA = one
 // sub-block), two v_mfma_i32_32x32x16_i8 for Q6_K (16-element sub-blocks).
+// Q4_K runs on 16 x 16 tiles with its min term on the fp64 matrix cores (its
+// own tile, further down).
 // The V100 pages found dequantize + dense GEMM faster than their dp4a kernel
 // above M ~ 32-64 and their fused WMMA attempts slower than dp4a because the
 // dequantized tile went through shared memory (V100TPS, "fp16 vs Q4
@@ -52,24 +54,6 @@ __device__ __forceinline__ int mfma_row(int r, int g) { return 8 * (r >> 2) + 4 
 // Per weight row and superblock: the scale fields.  Per weight row and
 // 32-element block: the B operand data of this lane's K-slice g.
 template <int T> struct QmmFmt;
-
-template <> struct QmmFmt<Q4_K> {
-  static constexpr int BYTES = 144;
-  struct Hdr { u32x4 h; };
-  struct Blk { u32x4 qs; };  // qs[32c + 16g .. +16], c = j/2: sub-blocks 2c (low), 2c+1 (high)
-  __device__ static Hdr hdr(const uint8_t* sb) { return Hdr{ld16(sb)}; }
-  __device__ static Blk blk(const uint8_t* sb, int j, int g) { return Blk{ld16(sb + 16 + 32 * (j >> 1) + 16 * g)}; }
-  // 6-bit scale and min of sub-block j (plain GGUF packing), as fp64 d*sc and -dmin*m.
-  template <int J> __device__ static void scales(const Hdr& x, double& w, double& mn) {
-    q4k_scales(x.h, J, w, mn);
-  }
-  template <int J> __device__ static v4i codes(const Blk& b, int /*g*/) {
-    const u32x4 v = b.qs;
-    const int s = (J & 1) ? 4 : 0;
-    return v4i{(int)((v.x >> s) & 0x0F0F0F0Fu), (int)((v.y >> s) & 0x0F0F0F0Fu),
-               (int)((v.z >> s) & 0x0F0F0F0Fu), (int)((v.w >> s) & 0x0F0F0F0Fu)};
-  }
-};
 
 template <> struct QmmFmt<IQ4_XS> {
   static constexpr int BYTES = 136;
@@ -211,6 +195,7 @@ template <int T, int KP, bool DUMP>
 __device__ __forceinline__ void qmm_split_tile(const uint8_t* __restrict__ W, int N, int K,
                                                const uint8_t* __restrict__ xq, int M, float* __restrict__ y,
                                                int32_t* __restrict__ isums, int m_tiles, int n_tiles) {
+  static_assert(T != Q4_K, "Q4_K runs the 16x16 tile (qmm_q4k16_tile)");
   using F = QmmFmt<T>;
   constexpr int SUB = Geom<T>::SUB;
   constexpr int BYTES = Geom<T>::BYTES;
@@ -410,13 +395,12 @@ __device__ __forceinline__ void qmm_split_tile(const uint8_t* __restrict__ W, in
         } else {
           const v4i a = v4i{(int)oa.x, (int)oa.y, (int)oa.z, (int)oa.w};
           v16i I[QMM_NT];
-          double w[QMM_NT], mn[QMM_NT];
+          double w[QMM_NT];
 #pragma unroll
           for (int t = 0; t < QMM_NT; ++t) {
             const v16i z = {0};
             I[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, F::template codes<J>(wb[t], g), z, 0, 0, 0);
-            if constexpr (T == Q4_K) F::template scales<J>(hd[t], w[t], mn[t]);
-            else { w[t] = F::template scale<J>(hd[t], wb[t]); mn[t] = 0.0; }
+            w[t] = F::template scale<J>(hd[t], wb[t]);
           }
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -425,7 +409,6 @@ __device__ __forceinline__ void qmm_split_tile(const uint8_t* __restrict__ W, in
 #pragma unroll
             for (int t = 0; t < QMM_NT; ++t) {
               acc[t][r] = fma(w[t] * e.d, (double)I[t][r], acc[t][r]);  // exact product
-              if constexpr (T == Q4_K) acc[t][r] = fma(mn[t], e.s, acc[t][r]);
               if (DUMP) {
                 const int m = m0 + i, n = n0 + 32 * t + c32;
                 if (m < M && n < N)
@@ -753,10 +736,8 @@ __device__ __forceinline__ void qmm_q4k16_tile(const uint8_t* __restrict__ W, in
     }
 }
 
-constexpr bool QMM_Q4K16 = true;  // Q4_K on the 16x16 tile
-
 template <int T, int KP, bool DUMP> constexpr int qmm_occupancy() {
-  if constexpr (T == Q4_K && QMM_Q4K16) return !DUMP && qf_lds_bytes<KP>() <= 80 * 1024 ? 2 : 1;
+  if constexpr (T == Q4_K) return !DUMP && qf_lds_bytes<KP>() <= 80 * 1024 ? 2 : 1;
   else return qmm_min_waves<T, KP, DUMP>();
 }
 
@@ -764,7 +745,7 @@ template <int T, int KP, bool DUMP>
 __global__ __launch_bounds__(64 * QMM_WAVES, (qmm_occupancy<T, KP, DUMP>())) void qmm_mfma_kernel(
     const uint8_t* __restrict__ W, int N, int K, const uint8_t* __restrict__ xq, int M,
     float* __restrict__ y, int32_t* __restrict__ isums, int m_tiles, int n_tiles) {
-  if constexpr (T == Q4_K && QMM_Q4K16) qmm_q4k16_tile<KP, DUMP>(W, N, K, xq, M, y, isums, m_tiles, n_tiles);
+  if constexpr (T == Q4_K) qmm_q4k16_tile<KP, DUMP>(W, N, K, xq, M, y, isums, m_tiles, n_tiles);
   else qmm_split_tile<T, KP, DUMP>(W, N, K, xq, M, y, isums, m_tiles, n_tiles);
 }
 
