@@ -635,6 +635,23 @@ __device__ __forceinline__ void qmm_q4k16_tile(const uint8_t* __restrict__ W, in
     wave_sync();
 
     if (b < nsb) {
+      // The drain scales of block J (weight scales d*sc_J of the lane's four
+      // weight rows, activation D of its eight activation rows) are read
+      // from the tables one block ahead, after block J-1's operand reads,
+      // so that their LDS latency overlaps block J-1's MFMAs and drains.
+      struct Sc { double w[4], dv[2][4]; };
+      auto load_sc = [&](int J, Sc& sc) {
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) sc.w[tn] = Wt[J][16 * tn + c16].w;
+#pragma unroll
+        for (int tm = 0; tm < 2; ++tm) {
+          const double* dp = &Dt[J][16 * tm + 4 * g4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) sc.dv[tm][v] = dp[v];
+        }
+      };
+      Sc scs[2];
+      load_sc(0, scs[0]);
       auto do_block = [&](auto JC) {
         constexpr int J = decltype(JC)::value;
         constexpr int JN = J + RING - 1;
@@ -643,37 +660,39 @@ __device__ __forceinline__ void qmm_q4k16_tile(const uint8_t* __restrict__ W, in
         const u32x4 oa = ring[J % RING];
         const long a0 = (long)((uint64_t)oa.x | ((uint64_t)oa.y << 32));
         const long a1 = (long)((uint64_t)oa.z | ((uint64_t)oa.w << 32));
+        u32x2 q[4];
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) q[tn] = *reinterpret_cast<const u32x2*>(wl[tn] + 16 + 32 * (J >> 1) + 8 * g4);
+        constexpr int kc = J / 4, tmm = (J / 2) % 2;
+        const double sa = St[4 * kc + g4][16 * tmm + qf_row(c16)];
+        double smn[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) smn[e] = Wt[4 * kc + g4][16 * (2 * (J % 2) + e) + c16].mn;
+        if constexpr (J < 7) load_sc(J + 1, scs[(J + 1) % 2]);
+        const Sc& sc = scs[J % 2];
         v4i_t I[2][4];
-        double w[4];
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn) {
-          const u32x2 q = *reinterpret_cast<const u32x2*>(wl[tn] + 16 + 32 * (J >> 1) + 8 * g4);
           constexpr int sh = (J & 1) ? 4 : 0;
-          const long bq = (long)((uint64_t)((q.x >> sh) & 0x0F0F0F0Fu) |
-                                 ((uint64_t)((q.y >> sh) & 0x0F0F0F0Fu) << 32));
+          const long bq = (long)((uint64_t)((q[tn].x >> sh) & 0x0F0F0F0Fu) |
+                                 ((uint64_t)((q[tn].y >> sh) & 0x0F0F0F0Fu) << 32));
           const v4i_t z = {0, 0, 0, 0};
           I[0][tn] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a0, bq, z, 0, 0, 0);
           I[1][tn] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a1, bq, z, 0, 0, 0);
-          w[tn] = Wt[J][16 * tn + c16].w;
         }
-        {  // two of the superblock's sixteen min-term MFMAs: blocks 4*kc + g4 of tile (tmm, tn)
-          constexpr int kc = J / 4, tmm = (J / 2) % 2;
-          const double sa = St[4 * kc + g4][16 * tmm + qf_row(c16)];
+        // two of the superblock's sixteen min-term MFMAs: blocks 4*kc + g4 of tile (tmm, tn)
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int tn = 2 * (J % 2) + e;
-            acc[tmm][tn] = __builtin_amdgcn_mfma_f64_16x16x4f64(sa, Wt[4 * kc + g4][16 * tn + c16].mn, acc[tmm][tn], 0, 0, 0);
-          }
+        for (int e = 0; e < 2; ++e) {
+          const int tn = 2 * (J % 2) + e;
+          acc[tmm][tn] = __builtin_amdgcn_mfma_f64_16x16x4f64(sa, smn[e], acc[tmm][tn], 0, 0, 0);
         }
 #pragma unroll
         for (int tm = 0; tm < 2; ++tm) {
-          const double* dp = &Dt[J][16 * tm + 4 * g4];
-          const double dv[4] = {dp[0], dp[1], dp[2], dp[3]};
 #pragma unroll
           for (int tn = 0; tn < 4; ++tn)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-              acc[tm][tn][v] = fma(w[tn] * dv[v], (double)I[tm][tn][v], acc[tm][tn][v]);  // exact product
+              acc[tm][tn][v] = fma(sc.w[tn] * sc.dv[tm][v], (double)I[tm][tn][v], acc[tm][tn][v]);  // exact product
               if (DUMP) {
                 const int m = m0 + 16 * tm + 4 * g4 + v, n = n0 + 16 * tn + c16;
                 if (m < M && n < N) isums[((size_t)m * N + n) * (K / 32) + (size_t)b * 8 + J] = I[tm][tn][v];
