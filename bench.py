@@ -63,7 +63,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true", help="skip the sampled oracle check")
     p.add_argument("--kernel-reps", type=int, default=None,
-                   help="replays of each per-projection graph (default: steps)")
+                   help="replays of each per-projection graph, the median of which is reported "
+                        "(default: 20 or --steps, whichever is larger)")
     p.add_argument("--fused-max-m", type=int, default=1,
                    help="largest M whose launches quantize the activations in the matmul kernel "
                         "(qdot_quantize_qmatmul[_multi]) instead of a separate quantize launch; 0 = never")
@@ -148,6 +149,20 @@ def recorded_traffic(kernel, workload):
             return None
         return int(kv["traffic_bytes_per_launch"])
     return None
+
+
+def graph_median_ms(g, reps):
+    """Median over `reps` replays of a captured graph, each replay between its
+    own pair of HIP events on the current stream (ms per replay)."""
+    import numpy as np
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
 
 
 def copy_calibration(mib):
@@ -357,7 +372,6 @@ def shard_rows(dev, fused_max_m, reps, per_m_full, check=True):
     pidx = {n: i for i, (n, *_) in enumerate(synth.QWEN3_8B_TP8)}
     W = [[torch.from_numpy(synth.weights(t, N, K, synth.weight_seed(cfg_idx, layer, pidx[n]))).to(dev)
           for n, N, K, t in shapes] for layer in range(layers)]
-    ev = lambda: torch.cuda.Event(enable_timing=True)
     out = {}
     bad = nchk = 0
     for M in range(1, 9):
@@ -394,13 +408,7 @@ def shard_rows(dev, fused_max_m, reps, per_m_full, check=True):
                     launch(label, layer)
             g.replay()
             torch.cuda.synchronize()
-            a, b = ev(), ev()
-            a.record()
-            for _ in range(reps):
-                g.replay()
-            b.record()
-            torch.cuda.synchronize()
-            us = a.elapsed_time(b) * 1e3 / (reps * layers)
+            us = graph_median_ms(g, reps) * 1e3 / layers
             mats = shapes[:2] if label == "gate+up" else shapes[2:]
             wb = sum(qd.qdot_weight_bytes(t, N, K) for _, N, K, t in mats)
             K = mats[0][2]
@@ -940,7 +948,7 @@ def main():
         f"{step_ops / (ms_per_step * 1e-3) / 1e12:.1f} int8 TOP/s")
 
     # ------------------------------------- per-projection kernel timing
-    reps = args.kernel_reps or args.steps
+    reps = args.kernel_reps or max(20, args.steps)
     kern = {}      # kernel name -> [bytes, ms, launches]
     per_m = {}
     for M in Ms:
@@ -951,13 +959,7 @@ def main():
                 sweep(M, only=label)
             g.replay()
             torch.cuda.synchronize()
-            a, bb = ev(), ev()
-            a.record()
-            for _ in range(reps):
-                g.replay()
-            bb.record()
-            torch.cuda.synchronize()
-            us = a.elapsed_time(bb) * 1e3 / (reps * layers)
+            us = graph_median_ms(g, reps) * 1e3 / layers
             K = shapes[upis[0]][2]
             Ns = [shapes[pi][1] for pi in upis]
             wb = sum(qd.qdot_weight_bytes(shapes[pi][3], shapes[pi][1], K) for pi in upis)
@@ -984,14 +986,8 @@ def main():
                 sweep(M, only="quantize")
             g.replay()
             torch.cuda.synchronize()
-            a, bb = ev(), ev()
-            a.record()
-            for _ in range(reps):
-                g.replay()
-            bb.record()
-            torch.cuda.synchronize()
             nq = layers * len(q_inputs)
-            qus = a.elapsed_time(bb) * 1e3 / (reps * nq)
+            qus = graph_median_ms(g, reps) * 1e3 / nq
             qbytes = sum(M * in_K[i] * 4 + qd.qdot_q8_1_bytes(M, in_K[i]) for i in q_inputs) * layers
             e = kern.setdefault("quantize_q8_1", [0, 0.0, 0, 0])
             e[0] += qbytes
@@ -1024,13 +1020,7 @@ def main():
                         assert rc == 0, rc
                 g.replay()
                 torch.cuda.synchronize()
-                a, bb = ev(), ev()
-                a.record()
-                for _ in range(reps):
-                    g.replay()
-                bb.record()
-                torch.cuda.synchronize()
-                us = a.elapsed_time(bb) * 1e3 / (reps * layers)
+                us = graph_median_ms(g, reps) * 1e3 / layers
                 wb = qd.qdot_weight_bytes(t, N, K)
                 row[name] = {"us": round(us, 3), "pct_hbm_peak": round(100 * wb / us / 1e3 / HBM_PEAK_GBS, 1),
                              "kernel": (f"qmv_dot4q<{synth.TYPE_NAMES[t]},{M}>" if fz
