@@ -1064,6 +1064,14 @@ def main():
                    "GBps": round(v[0] / (v[1] * 1e-3) / 1e9, 1),
                    **({"TOPs": round(v[3] / (v[1] * 1e-3) / 1e12, 2)} if v[3] else {})}
                for k, v in kern.items()}
+    # The sweep aggregate over kernel time alone (the sum of the per-launch
+    # figures above), beside the wall time of the step graphs.
+    ksum_ms = sum(v[1] for v in kern.values())
+    kernel_aggregate = {"sum_of_launch_ms_per_step": round(ksum_ms, 4), "step_wall_ms": round(ms_per_step, 4)}
+    if prefill:
+        kernel_aggregate["int8_TOPs_over_launch_time"] = round(step_ops / (ksum_ms * 1e-3) / 1e12, 2)
+    else:
+        kernel_aggregate["weight_GBps_over_launch_time"] = round(len(Ms) * wbytes_sweep / (ksum_ms * 1e-3) / 1e9, 1)
 
     # ------------------------------------------- sampled oracle check
     check = None
@@ -1139,6 +1147,7 @@ def main():
         **({"shard_tp8_rows": shard} if shard else {}),
         **({"prefill_512_row": pre_row} if pre_row else {}),
         "kernels": kernels,
+        "kernel_time_aggregate": kernel_aggregate,
         "sampled_check": check,
     }
     print(json.dumps(out), flush=True)
