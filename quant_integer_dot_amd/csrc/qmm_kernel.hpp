@@ -293,8 +293,7 @@ __device__ __forceinline__ void qmm_split_tile(const uint8_t* __restrict__ W, in
   auto load_a = [&](int b, int j) {
     const uint8_t* xb = xrow + (size_t)(b * 8 + j) * Q8_BYTES + 4;
     if constexpr (T == Q6_K) {
-      const u32x2 lo = ld8(xb + 8 * g), hi = ld8(xb + 16 + 8 * g);
-      return u32x4{lo.x, lo.y, hi.x, hi.y};
+      return ld16(xb + 16 * g);  // elements 16g .. 16g+15; see the exchange in the block loop
     } else {
       return ld16(xb + 16 * g);
     }
@@ -361,8 +360,16 @@ __device__ __forceinline__ void qmm_split_tile(const uint8_t* __restrict__ W, in
 #pragma unroll
         for (int t = 0; t < QMM_NT; ++t) wb[t] = F::blk(wl[t], J, g);
         if constexpr (T == Q6_K) {
-          const long a0 = (long)((uint64_t)oa.x | ((uint64_t)oa.y << 32));
-          const long a1 = (long)((uint64_t)oa.z | ((uint64_t)oa.w << 32));
+          // The MFMA of sub-block 2J+h takes elements 16h + 8g .. 16h + 8g+7
+          // from the lane of K-slice g.  This lane loaded elements 16g ..
+          // 16g+15 in one 16-byte load, so the two lanes of a row (l, l+32)
+          // trade halves: v_permlane32_swap exchanges the upper half-wave's
+          // first 8 bytes with the lower half-wave's last 8, which leaves
+          // sub-block 2J's slice in the first result and 2J+1's in the second.
+          const auto xl = __builtin_amdgcn_permlane32_swap(oa.x, oa.z, false, false);
+          const auto xh = __builtin_amdgcn_permlane32_swap(oa.y, oa.w, false, false);
+          const long a0 = (long)((uint64_t)xl[0] | ((uint64_t)xh[0] << 32));
+          const long a1 = (long)((uint64_t)xl[1] | ((uint64_t)xh[1] << 32));
           v16i I0[QMM_NT], I1[QMM_NT];
           int s0[QMM_NT], s1[QMM_NT];
           double d[QMM_NT];
