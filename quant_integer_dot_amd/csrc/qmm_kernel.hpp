@@ -239,6 +239,12 @@ __device__ __forceinline__ void qmm_split_tile(const uint8_t* __restrict__ W, in
 #pragma unroll
   for (int t = 0; t < QMM_NT; ++t) wl[t] = lds_w + (size_t)(kp * QMM_BN + 32 * t + c32) * PITCH;
   QmmDs(*const stage)[32] = lds_ds[wave];
+  // The Q6_K instance with four K slices (one wave per SIMD) keeps only D,
+  // as fp32 (an fp16 value, exact): half the LDS bytes of its sixteen D
+  // reads per block (v 1024 x 4096 at M = 512: 35.2 -> 32.3 us; with two
+  // K slices the conversions cost what the bytes save).
+  constexpr bool D32 = T == Q6_K && KP == 4;
+  float(*const dstage)[32] = reinterpret_cast<float(*)[32]>(lds_ds[wave]);
 
   // Stage copy: chunk i = (K slice s, row r, 16-byte piece c); rows past N
   // are clamped to the last row, superblocks past the row to the last one
@@ -339,7 +345,8 @@ __device__ __forceinline__ void qmm_split_tile(const uint8_t* __restrict__ W, in
     stage_load(it + 1, breg);                        // lands while this superblock is computed
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      stage[4 * g + u][c32] = QmmDs{(double)h2f(ds_next[u] & 0xFFFFu), (double)h2f(ds_next[u] >> 16)};
+      if constexpr (D32) dstage[4 * g + u][c32] = h2f(ds_next[u] & 0xFFFFu);
+      else stage[4 * g + u][c32] = QmmDs{(double)h2f(ds_next[u] & 0xFFFFu), (double)h2f(ds_next[u] >> 16)};
     load_ds(bn, ds_next);
     wave_sync();
 
@@ -384,7 +391,7 @@ __device__ __forceinline__ void qmm_split_tile(const uint8_t* __restrict__ W, in
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int i = mfma_row(r, g);
-            const double D = stage[J][i].d;
+            const double D = D32 ? (double)dstage[J][i] : stage[J][i].d;
 #pragma unroll
             for (int t = 0; t < QMM_NT; ++t) {
               const int P = q6k_pair(s0[t], I0[t][r], s1[t], I1[t][r]);  // exact int
